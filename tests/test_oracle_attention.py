@@ -1,0 +1,238 @@
+"""Pins of the oracle's decode attention, partition statistics and flash-combine (CPU).
+
+None of these re-types the oracle's formulas: the references are torch's
+scaled_dot_product_attention on a densely re-gathered cache, closed-form special cases
+(one token, equal scores, one-hot gathers), invariances the method must have
+(partition count, physical block placement, masked bytes) and a butterfly WHT."""
+
+import copy
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from quantized_paged_attention_amd import synth
+from tests.refdense import golden, sdpa_reference, sylvester_rotation
+
+
+def run(case, P=0):
+    return oracle.decode(case.q, case.cache, case.block_table, case.seq_lens,
+                         num_kv_heads=case.num_kv_heads, kv_format=case.kv_format,
+                         softmax_scale=case.softmax_scale, k_scale=case.k_scale,
+                         v_scale=case.v_scale, rot_signs=case.rot_signs, num_partitions=P)
+
+
+def small_fp8(seed=11, lens=(1, 15, 16, 17, 255, 256, 257, 700), hk=2, qg=4, bs=16, **kw):
+    return synth.make_fp8_case("small", seed, seq_lens=list(lens), num_kv_heads=hk, qg=qg,
+                               block_size=bs, spare_blocks=5, **kw)
+
+
+def small_fp4(seed=12, lens=(1, 63, 64, 65, 300), hk=2, qg=6, kind="e4m3", rotate=True):
+    return synth.make_fp4_case("small4", seed, seq_lens=list(lens), num_kv_heads=hk, qg=qg,
+                               head_dim=256, block_size=64, scale_kind=kind, rotate=rotate,
+                               spare_blocks=3)
+
+
+@pytest.mark.parametrize("values,ks,vs", [("normal", 1.0, 1.0), ("uniform_codes", 0.05, 0.02)])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_fp8_matches_torch_sdpa(values, ks, vs, bs):
+    case = small_fp8(values=values, k_scale=ks, v_scale=vs, bs=bs)
+    got = run(case)
+    want = sdpa_reference(case)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("kind", ["e4m3", "ue8m0"])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_fp4_matches_torch_sdpa(kind, rotate):
+    case = small_fp4(kind=kind, rotate=rotate)
+    got = run(case)
+    want = sdpa_reference(case)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12 * np.abs(want).max())
+
+
+def test_single_token_returns_v_exactly():
+    case = small_fp8(lens=(1, 1, 1), values="uniform_codes", v_scale=0.5)
+    got = run(case)
+    from tests.refdense import dense_kv
+    for b in range(case.B):
+        for h in range(case.num_kv_heads):
+            _, v = dense_kv(case, b, h)
+            for g in range(case.QG):
+                assert np.array_equal(got[b, h * case.QG + g], 0.5 * v[0])
+
+
+@pytest.mark.parametrize("mode", ["zero_q", "equal_k"])
+def test_equal_scores_give_mean_of_v(mode):
+    case = small_fp8(lens=(5, 40, 129), values="normal")
+    if mode == "zero_q":
+        case.q[:] = 0.0
+    else:
+        # every used slot gets the same K codes (token 0 of sequence 0)
+        D = case.D
+        ref = case.cache[case.block_table[0, 0], 0, 0, :D].copy()
+        case.cache[..., :D] = ref
+    got = run(case)
+    from tests.refdense import dense_kv
+    for b in range(case.B):
+        for h in range(case.num_kv_heads):
+            _, v = dense_kv(case, b, h)
+            for g in range(case.QG):
+                np.testing.assert_allclose(got[b, h * case.QG + g], v.mean(0), rtol=1e-12,
+                                           atol=1e-12)
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64])
+def test_one_hot_gather_is_exact(bs):
+    """Q = 100 e0 and a single token t* with K[0] = 448: every other weight underflows to
+    zero, so the output is exactly v[t*] for t* at every block edge."""
+    L = 5 * bs + 3
+    case = small_fp8(lens=(L,), hk=1, qg=2, bs=bs, values="normal")
+    D = case.D
+    case.q[:] = 0.0
+    case.q[:, :, 0] = 100.0
+    from tests.refdense import dense_kv
+    for tstar in sorted({0, bs - 1, bs, 2 * bs - 1, 2 * bs, L - 1}):
+        c = copy.deepcopy(case)
+        c.cache[..., :D] = 0
+        blk = c.block_table[0, tstar // bs]
+        c.cache[blk, tstar % bs, 0, 0] = 0x7E      # 448
+        got = run(c)
+        _, v = dense_kv(c, 0, 0)
+        assert np.array_equal(got[0, 0], v[tstar]), tstar
+        assert np.array_equal(got[0, 1], v[tstar]), tstar
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 7, 64])
+def test_partials_reduce_to_full_output(P):
+    case = small_fp8(lens=(0, 1, 255, 256, 257, 1000, 2049))
+    full, (pm, pl, po) = run(case, P)
+    assert np.array_equal(full, run(case))
+    red = oracle.reduce(po, pm, pl, case.seq_lens)
+    np.testing.assert_allclose(red, full, rtol=1e-12, atol=1e-12 * np.abs(full).max())
+    # empty partitions: p >= ceil(L/256) holds nothing
+    for b, L in enumerate(case.seq_lens):
+        ntg = -(-int(L) // 256)
+        for p in range(P):
+            if p >= ntg:
+                assert np.all(pm[b, :, p] == -np.inf) and np.all(pl[b, :, p] == 0)
+                assert np.all(po[b, :, p] == 0)
+            else:
+                assert np.all(np.isfinite(pm[b, :, p])) and np.all(pl[b, :, p] >= 1.0)
+
+
+def test_partition_owns_strided_tile_groups():
+    """With P=2, partition 0 owns tile-groups 0, 2, ... : its (m, l, o) must be the
+    softmax statistics of exactly those tokens, checked by zeroing the others out of an
+    SDPA over the dense cache."""
+    case = small_fp8(lens=(1100,), hk=1, qg=2, values="normal")
+    full, (pm, pl, po) = run(case, 2)
+    from tests.refdense import dense_kv
+    k, v = dense_kv(case, 0, 0)
+    t = np.arange(1100)
+    for p in range(2):
+        sel = (t // 256) % 2 == p
+        s = case.softmax_scale * (k[sel] @ case.q[0].astype(np.float64).T)   # [n, QG]
+        m = s.max(0)
+        np.testing.assert_allclose(pm[0, 0, p], m, rtol=1e-13)
+        np.testing.assert_allclose(pl[0, 0, p], np.exp(s - m).sum(0), rtol=1e-12)
+
+
+def test_block_permutation_invariance():
+    case = small_fp8(lens=(17, 300, 513), values="uniform_codes", k_scale=0.05, v_scale=0.02)
+    base = run(case)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(case.cache.shape[0])          # new id of old block i is perm[i]
+    c2 = copy.deepcopy(case)
+    c2.cache = np.empty_like(case.cache)
+    c2.cache[perm] = case.cache
+    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1)
+    assert np.array_equal(run(c2), base)
+
+
+def test_masked_bytes_never_matter():
+    """Bytes past each sequence's length, unreferenced blocks and table tails can hold
+    anything: the output is bit-identical."""
+    case = small_fp8(lens=(3, 20, 33), values="normal")
+    base = run(case)
+    c2 = copy.deepcopy(case)
+    used = np.zeros(c2.cache.shape[0], bool)
+    for b, L in enumerate(c2.seq_lens):
+        n = -(-int(L) // c2.block_size)
+        used[c2.block_table[b, :n]] = True
+        if L % c2.block_size:
+            c2.cache[c2.block_table[b, L // c2.block_size], L % c2.block_size:] = 0x7E
+        c2.block_table[b, n:] = 10 ** 6
+    c2.cache[~used] = 0x55
+    assert np.isfinite(base).all()
+    assert np.array_equal(run(c2), base)
+
+
+def test_out_of_range_block_id_is_rejected():
+    case = small_fp8(lens=(20,))
+    case.block_table[0, 1] = case.cache.shape[0]
+    with pytest.raises(ValueError):
+        run(case)
+
+
+def test_empty_sequence_gives_zero_row():
+    case = small_fp8(lens=(0, 5))
+    out = run(case)
+    assert np.all(out[0] == 0) and np.isfinite(out[1]).all()
+
+
+# ------------------------------------------------------------------ rotation
+
+
+def fwht_fp32(x):
+    """Iterative radix-2 fast Walsh-Hadamard transform in float32 (natural order)."""
+    x = np.array(x, np.float32)
+    n = x.shape[-1]
+    h = 1
+    while h < n:
+        x = x.reshape(*x.shape[:-1], n // (2 * h), 2, h)
+        a, b = x[..., 0, :].copy(), x[..., 1, :].copy()
+        x[..., 0, :], x[..., 1, :] = a + b, a - b
+        x = x.reshape(*x.shape[:-3], n)
+        h *= 2
+    return x
+
+
+def test_rotation_against_fp32_butterfly_bound():
+    """The direct O(D^2) rotation agrees with an fp32 butterfly within the page's 1.8e-6."""
+    g = golden("p1_wht_bound.txt")
+    D = g["head_dim"]
+    rng = np.random.default_rng(7)
+    signs = (rng.integers(0, 2, D) * 2 - 1).astype(np.int8)
+    worst = 0.0
+    for _ in range(16):
+        q = rng.standard_normal(D).astype(np.float32)
+        direct = oracle.rotate(q.astype(np.float64), signs)
+        bfly = fwht_fp32(q * signs) / np.float32(np.sqrt(D))
+        worst = max(worst, float(np.abs(direct - bfly).max()))
+    assert worst <= g["max_abs_diff_fp32"]
+
+
+def test_rotation_is_scipy_hadamard_and_orthonormal():
+    D = 256
+    rng = np.random.default_rng(8)
+    signs = (rng.integers(0, 2, D) * 2 - 1).astype(np.int8)
+    R = np.stack([oracle.rotate(np.eye(D)[i], signs) for i in range(D)])   # rows = e_i R
+    np.testing.assert_allclose(R, sylvester_rotation(signs), atol=1e-15)
+    np.testing.assert_allclose(R @ R.T, np.eye(D), atol=1e-13)
+
+
+def test_joint_rotation_preserves_scores():
+    """Rotating both q and the stored keys leaves attention unchanged: the oracle with
+    rotation over rotated-domain keys equals the oracle without rotation over keys
+    rotated back, up to fp4 re-encoding (so compare scores, not outputs)."""
+    D = 256
+    rng = np.random.default_rng(9)
+    signs = (rng.integers(0, 2, D) * 2 - 1).astype(np.int8)
+    q = rng.standard_normal(D)
+    k = rng.standard_normal(D)
+    qr = oracle.rotate(q, signs)
+    kr = oracle.rotate(k, signs)
+    assert abs(qr @ kr - q @ k) < 1e-12 * max(1.0, abs(q @ k))
