@@ -1,0 +1,245 @@
+// uq_abi.cpp -- the C ABI of libuq.so (declared in include/uq_paged.h): host-side
+// validation, derived launch parameters and kernel launches.  No allocation, no
+// synchronisation, no per-call state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/uq_paged.h"
+#include "uq_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return UQ_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(UQ_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_block_size(int bs) {
+  return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
+}
+
+int slot_content(int fmt, int D) {
+  if (fmt == UQ_KV_FP8_E4M3) return 2 * D;
+  if (fmt == UQ_KV_FP4_E2M1_E4M3S || fmt == UQ_KV_FP4_E2M1_UE8M0S)
+    return D % 32 ? -1 : 2 * (D / 2 + D / 32);
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uq_last_error(void) { return g_err; }
+
+size_t uq_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t qg,
+                                 int32_t head_dim, int32_t num_partitions) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || qg <= 0 || head_dim <= 0 || num_partitions <= 0)
+    return 0;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)num_seqs * num_kv_heads * num_partitions * qg;
+  return up(rows * head_dim * 2) + 2 * up(rows * 4);
+}
+
+int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_stride_head,
+                    const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t slot_bytes, int kv_format,
+                    const float* k_scale, const float* v_scale, const int8_t* rot_signs,
+                    const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_partitions,
+                    void* part_out, float* part_max, float* part_sum, void* stream) {
+  if (num_seqs < 0) return fail(UQ_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(UQ_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  const int QG = num_q_heads / num_kv_heads;
+  if (QG > 16) return fail(UQ_ERR_INVALID_ARG, "query group %d exceeds 16", QG);
+  if (q_dtype != UQ_F32 && q_dtype != UQ_BF16)
+    return fail(UQ_ERR_INVALID_ARG, "q_dtype must be UQ_F32 or UQ_BF16 (got %d)", q_dtype);
+  if (q_stride_seq <= 0 || q_stride_head <= 0)
+    return fail(UQ_ERR_INVALID_ARG, "query strides must be positive");
+  if (!valid_block_size(block_size))
+    return fail(UQ_ERR_INVALID_ARG, "block_size must be 16, 32, 64, 128 or 256 (got %d)", block_size);
+  if (num_blocks <= 0) return fail(UQ_ERR_INVALID_ARG, "num_blocks must be positive");
+  const int content = slot_content(kv_format, head_dim);
+  if (content < 0) return fail(UQ_ERR_INVALID_ARG, "unknown kv_format %d or head_dim %d", kv_format, head_dim);
+  if (slot_bytes < content || slot_bytes % 4 != 0)
+    return fail(UQ_ERR_INVALID_ARG, "slot_bytes %d must be >= %d and a multiple of 4", slot_bytes, content);
+  if (num_partitions < 1) return fail(UQ_ERR_INVALID_ARG, "num_partitions must be >= 1");
+  if (max_seq_len < 0) return fail(UQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  if (bt_stride <= 0 || (int64_t)bt_stride * block_size < max_seq_len)
+    return fail(UQ_ERR_INVALID_ARG, "bt_stride %d cannot hold max_seq_len %d at block size %d",
+                bt_stride, max_seq_len, block_size);
+  if (!std::isfinite(softmax_scale)) return fail(UQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (num_seqs > 0 && (!query || !kv_cache || !block_table || !seq_lens || !part_out || !part_max ||
+                       !part_sum))
+    return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((reinterpret_cast<uintptr_t>(query) | reinterpret_cast<uintptr_t>(part_out)) & 15)
+    return fail(UQ_ERR_INVALID_ARG, "query and part_out must be 16-byte aligned");
+  const int esz = q_dtype == UQ_F32 ? 4 : 2;
+  if (((q_stride_seq * esz) | (q_stride_head * esz)) % 16)
+    return fail(UQ_ERR_INVALID_ARG, "query strides must be multiples of 16 bytes");
+  if (reinterpret_cast<uintptr_t>(kv_cache) & 15)
+    return fail(UQ_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
+
+  uq::DecodeArgs a{};
+  a.q = query;
+  a.q_ss = q_stride_seq;
+  a.q_sh = q_stride_head;
+  a.cache = kv_cache;
+  a.slot_bytes = slot_bytes;
+  a.pos_stride = num_kv_heads * slot_bytes;
+  a.blk_stride = (int64_t)block_size * a.pos_stride;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.rot_signs = rot_signs;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens;
+  a.B = num_seqs;
+  a.Hk = num_kv_heads;
+  a.QG = QG;
+  a.P = num_partitions;
+  const int ntg = (max_seq_len + uq::kTileGroup - 1) / uq::kTileGroup;
+  a.TGPP = ntg == 0 ? 1 : (ntg + num_partitions - 1) / num_partitions;
+  a.max_seq_len = max_seq_len;
+  a.block_size = block_size;
+  a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+  a.part_o = static_cast<uint16_t*>(part_out);
+  a.part_m = part_max;
+  a.part_l = part_sum;
+  if ((int64_t)a.pos_stride * block_size > (int64_t)1 << 31)
+    return fail(UQ_ERR_UNSUPPORTED, "a physical block larger than 2 GiB is not supported");
+
+  if (kv_format == UQ_KV_FP8_E4M3) {
+    if (head_dim != 128) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports head_dim 128 only");
+    if (QG > 8) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports query groups up to 8");
+    if (rot_signs) return fail(UQ_ERR_UNSUPPORTED, "query rotation is supported with fp4 caches only");
+    if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache needs slot_bytes a multiple of 16");
+    if (num_seqs == 0) return ok();
+    return launch_status(uq::launch_decode_fp8(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
+                         "decode_fp8");
+  }
+  if (kv_format == UQ_KV_FP4_E2M1_E4M3S) {
+    if (head_dim != 256) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports head_dim 256 only");
+    if (QG != 6 && QG != 8 && QG != 16)
+      return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports query groups 6, 8 and 16 (got %d)", QG);
+    if (k_scale || v_scale) return fail(UQ_ERR_INVALID_ARG, "per-tensor scales apply to fp8 caches only");
+    if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache needs slot_bytes a multiple of 16");
+    if (num_seqs == 0) return ok();
+    return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
+                         "decode_fp4");
+  }
+  return fail(UQ_ERR_UNSUPPORTED, "kv_format %d is not implemented", kv_format);
+}
+
+int uq_paged_reduce(const void* part_out, const float* part_max, const float* part_sum,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads, int32_t qg,
+                    int32_t head_dim, int32_t num_partitions, int32_t max_seq_len, void* out,
+                    int out_dtype, int64_t o_stride_seq, int64_t o_stride_head, void* stream) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || qg < 1 || qg > 16)
+    return fail(UQ_ERR_INVALID_ARG, "bad sizes: num_seqs %d, num_kv_heads %d, qg %d", num_seqs,
+                num_kv_heads, qg);
+  if (head_dim != 128 && head_dim != 256)
+    return fail(UQ_ERR_UNSUPPORTED, "reduce supports head_dim 128 and 256 (got %d)", head_dim);
+  if (num_partitions < 1) return fail(UQ_ERR_INVALID_ARG, "num_partitions must be >= 1");
+  if (max_seq_len < 0) return fail(UQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  if (out_dtype != UQ_F32 && out_dtype != UQ_BF16)
+    return fail(UQ_ERR_INVALID_ARG, "out_dtype must be UQ_F32 or UQ_BF16 (got %d)", out_dtype);
+  if (o_stride_seq <= 0 || o_stride_head <= 0)
+    return fail(UQ_ERR_INVALID_ARG, "output strides must be positive");
+  if (num_seqs > 0 && (!part_out || !part_max || !part_sum || !seq_lens || !out))
+    return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  const int esz = out_dtype == UQ_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(part_out)) & 15 ||
+      ((o_stride_seq * esz) | (o_stride_head * esz)) % 16)
+    return fail(UQ_ERR_INVALID_ARG, "out, part_out and the output strides must be 16-byte aligned");
+  if (num_seqs == 0) return ok();
+  uq::ReduceArgs a{};
+  a.part_o = static_cast<const uint16_t*>(part_out);
+  a.part_m = part_max;
+  a.part_l = part_sum;
+  a.seq_lens = seq_lens;
+  a.B = num_seqs;
+  a.Hk = num_kv_heads;
+  a.QG = qg;
+  a.D = head_dim;
+  a.P = num_partitions;
+  a.max_seq_len = max_seq_len;
+  a.out = out;
+  a.o_ss = o_stride_seq;
+  a.o_sh = o_stride_head;
+  return launch_status(uq::launch_reduce(a, out_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
+                       "reduce");
+}
+
+int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head,
+                   const uint8_t* k_pages, int64_t page_stride, int64_t num_pages,
+                   const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                   int32_t num_reqs, int32_t query_len, int32_t heads, int32_t head_dim,
+                   int32_t init_blocks, int32_t local_blocks, float* scores,
+                   int64_t s_stride_head, int64_t s_stride_row, int32_t max_blocks,
+                   void* stream) {
+  if (num_reqs < 0) return fail(UQ_ERR_INVALID_ARG, "num_reqs must be >= 0");
+  if (heads != 1 && heads != 2 && heads != 4)
+    return fail(UQ_ERR_INVALID_ARG, "heads must be 1, 2 or 4 (got %d)", heads);
+  if (query_len < 1 || heads * query_len > 32)
+    return fail(UQ_ERR_INVALID_ARG, "heads * query_len must be in [1, 32] (got %d x %d)", heads,
+                query_len);
+  if (head_dim != 128) return fail(UQ_ERR_UNSUPPORTED, "index scorer supports head_dim 128 only");
+  if (init_blocks != 0 || local_blocks != 0)
+    return fail(UQ_ERR_UNSUPPORTED, "sentinel init/local blocks are not supported");
+  if (q_stride_tok <= 0 || q_stride_head <= 0 || q_stride_tok % 16 || q_stride_head % 16)
+    return fail(UQ_ERR_INVALID_ARG, "q strides must be positive multiples of 16 bytes");
+  const int64_t content = 128LL * (head_dim / 2 + head_dim / 16);
+  if (page_stride < content || page_stride % 16)
+    return fail(UQ_ERR_INVALID_ARG, "page_stride %lld must be >= %lld and a multiple of 16",
+                (long long)page_stride, (long long)content);
+  if (num_pages <= 0 || bt_stride <= 0 || max_blocks <= 0)
+    return fail(UQ_ERR_INVALID_ARG, "num_pages, bt_stride and max_blocks must be positive");
+  if (s_stride_head <= 0 || s_stride_row <= 0)
+    return fail(UQ_ERR_INVALID_ARG, "score strides must be positive");
+  if (num_reqs > 0 && (!q || !k_pages || !block_table || !seq_lens || !scores))
+    return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages)) & 15)
+    return fail(UQ_ERR_INVALID_ARG, "q and k_pages must be 16-byte aligned");
+  if (num_reqs == 0) return ok();
+  uq::IndexArgs a{};
+  a.q = q;
+  a.q_st = q_stride_tok;
+  a.q_sh = q_stride_head;
+  a.pages = k_pages;
+  a.page_stride = page_stride;
+  a.bt = block_table;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens;
+  a.num_reqs = num_reqs;
+  a.QL = query_len;
+  a.H = heads;
+  a.max_blocks = max_blocks < bt_stride ? max_blocks : bt_stride;
+  a.scores = scores;
+  a.s_sh = s_stride_head;
+  a.s_st = s_stride_row;
+  return launch_status(uq::launch_index_score(a, static_cast<hipStream_t>(stream)), "index_score");
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// uq_device.h -- small CDNA4 (gfx950) device helpers shared by the libuq kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "uq_kernels.h"
+
+namespace uq {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bits_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Lane exchange across 16-lane rows / 32-lane halves (ds_bpermute based).
+__device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Exchange with the lane n ^ 8 of the same 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ float row_ror8(float v) {
+  return bits_f((uint32_t)__builtin_amdgcn_mov_dpp((int)f_bits(v), 0x128, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = f_bits(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float bf16_to_f(uint32_t h) { return bits_f(h << 16); }
+
+// Two floats -> two OCP e4m3 bytes in the low (hi_word = false) or high half of `old`
+// (v_cvt_pk_fp8_f32, round to nearest even).
+template <bool hi_word>
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, hi_word);
+}
+// Byte `sel` of a word of e4m3 codes -> float (v_cvt_f32_fp8).
+template <int sel>
+__device__ __forceinline__ float e4m3_to_f(int word) {
+  return __builtin_amdgcn_cvt_f32_fp8(word, sel);
+}
+
+// 4x4 byte transpose: in[j] holds bytes (m = 0..3) of token j; out[m] holds byte m of
+// tokens 0..3 (byte j of out[m] = byte m of in[j]).
+__device__ __forceinline__ void transpose4x4_bytes(const uint32_t in[4], uint32_t out[4]) {
+  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x06020400u);  // a0b0 a1b0 a0b2 a1b2
+  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030501u);  // a0b1 a1b1 a0b3 a1b3
+  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x06020400u);  // a2b0 a3b0 a2b2 a3b2
+  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030501u);  // a2b1 a3b1 a2b3 a3b3
+  out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  out[2] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  out[1] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+template <typename T>
+__device__ __forceinline__ T nt_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+}  // namespace uq

@@ -1,0 +1,60 @@
+// uq_kernels.h -- internal launchers of the libuq kernels (host side, C++ linkage).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uq {
+
+constexpr int kTileGroup = 256;  // tokens per tile-group (partition granule)
+
+struct DecodeArgs {
+  const void* q;
+  int64_t q_ss, q_sh;          // element strides of the query (sequence, head)
+  const uint8_t* cache;
+  int64_t blk_stride;          // bytes per physical block = block_size * pos_stride
+  int32_t pos_stride;          // bytes per token position = num_kv_heads * slot_bytes
+  int32_t slot_bytes;
+  const float* k_scale;        // nullable device scalars
+  const float* v_scale;
+  const int8_t* rot_signs;     // nullable
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t B, Hk, QG, P, TGPP, max_seq_len, block_size;
+  float softmax_scale;
+  uint16_t* part_o;            // bf16 [B, Hk, P, QG, D]
+  float* part_m;               // [B, Hk, P, QG]
+  float* part_l;
+};
+
+struct ReduceArgs {
+  const uint16_t* part_o;
+  const float* part_m;
+  const float* part_l;
+  const int32_t* seq_lens;
+  int32_t B, Hk, QG, D, P, max_seq_len;
+  void* out;
+  int64_t o_ss, o_sh;
+};
+
+struct IndexArgs {
+  const uint8_t* q;
+  int64_t q_st, q_sh;          // byte strides
+  const uint8_t* pages;
+  int64_t page_stride;
+  const int32_t* bt;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  int32_t num_reqs, QL, H, max_blocks;
+  float* scores;
+  int64_t s_sh, s_st;
+};
+
+// Each returns the hipError_t of its launch.
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t stream);
+hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, bool out_is_f32, hipStream_t stream);
+hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream);
+
+}  // namespace uq

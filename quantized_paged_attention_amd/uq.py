@@ -1,0 +1,224 @@
+"""Thin ctypes binding of libuq.so (C ABI in include/uq_paged.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout, their
+pointers and strides are passed through, and every step runs in the HIP kernels.  There
+is no fallback: if the library is missing, or the tensors are not on a GPU, the calls
+raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libuq.so")
+
+UQ_OK, UQ_ERR_INVALID_ARG, UQ_ERR_UNSUPPORTED, UQ_ERR_LAUNCH = 0, 1, 2, 3
+UQ_F32, UQ_BF16 = 0, 1
+UQ_KV_FP8_E4M3, UQ_KV_FP4_E2M1_E4M3S, UQ_KV_FP4_E2M1_UE8M0S = 0, 1, 2
+
+EXPORTS = ("uq_paged_decode", "uq_paged_reduce", "uq_index_score",
+           "uq_decode_workspace_bytes", "uq_last_error")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class UqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[uq status {status}] {msg}")
+        self.status = status
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libuq.so (built by ``python -m quantized_paged_attention_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with "
+                               "`python -m quantized_paged_attention_amd.build`")
+        lib = ctypes.CDLL(p)
+        V, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        lib.uq_paged_decode.restype = ctypes.c_int
+        lib.uq_paged_decode.argtypes = [V, ctypes.c_int, i64, i64, V, i64, i32, i32, i32,
+                                        ctypes.c_int, V, V, V, V, i32, V, i32, i32, i32, i32,
+                                        f32, i32, V, V, V, V]
+        lib.uq_paged_reduce.restype = ctypes.c_int
+        lib.uq_paged_reduce.argtypes = [V, V, V, V, i32, i32, i32, i32, i32, i32, V,
+                                        ctypes.c_int, i64, i64, V]
+        lib.uq_index_score.restype = ctypes.c_int
+        lib.uq_index_score.argtypes = [V, i64, i64, V, i64, i64, V, i32, V, i32, i32, i32,
+                                       i32, i32, i32, V, i64, i64, i32, V]
+        lib.uq_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.uq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.uq_last_error.restype = ctypes.c_char_p
+        lib.uq_last_error.argtypes = []
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != UQ_OK:
+        raise UqError(status, load_library().uq_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("uq kernels take GPU tensors only")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return UQ_F32
+    if dt == torch.bfloat16:
+        return UQ_BF16
+    raise ValueError(f"query/output dtype must be float32 or bfloat16, got {dt}")
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def decode_workspace_bytes(num_seqs: int, num_kv_heads: int, qg: int, head_dim: int,
+                           num_partitions: int) -> int:
+    return int(load_library().uq_decode_workspace_bytes(num_seqs, num_kv_heads, qg, head_dim,
+                                                        num_partitions))
+
+
+def alloc_partials(num_seqs: int, num_kv_heads: int, qg: int, head_dim: int,
+                   num_partitions: int, device="cuda"):
+    """Caller-owned partial buffers for paged_decode (bf16 o, f32 m, f32 l)."""
+    shp = (num_seqs, num_kv_heads, num_partitions, qg)
+    return (torch.empty(*shp, head_dim, dtype=torch.bfloat16, device=device),
+            torch.empty(shp, dtype=torch.float32, device=device),
+            torch.empty(shp, dtype=torch.float32, device=device))
+
+
+def paged_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, *, kv_format: int, max_seq_len: int,
+                 num_partitions: int, part_out: torch.Tensor, part_max: torch.Tensor,
+                 part_sum: torch.Tensor, softmax_scale: float = 0.0,
+                 k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
+                 rot_signs: torch.Tensor | None = None, stream=None) -> None:
+    """uq_paged_decode on torch tensors: query [B, Hq, D] (strided over B and Hq, D
+    contiguous); kv_cache [num_blocks, block_size, Hk, slot] uint8."""
+    lib = load_library()
+    if query.dim() != 3 or query.stride(2) != 1:
+        raise ValueError("query must be [B, Hq, D] with a contiguous head dim")
+    if kv_cache.dim() != 4 or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_blocks, block_size, Hk, slot]")
+    _need(kv_cache, torch.uint8, "kv_cache")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, max_blocks] with contiguous rows")
+    _need(part_out, torch.bfloat16, "part_out")
+    _need(part_max, torch.float32, "part_max")
+    _need(part_sum, torch.float32, "part_sum")
+    B, Hq, D = query.shape
+    nb, bs, hk, slot = kv_cache.shape
+    qg = Hq // hk if hk else 0
+    if tuple(part_out.shape) != (B, hk, num_partitions, qg, D) or not part_out.is_contiguous():
+        raise ValueError("part_out must be a contiguous [B, Hk, P, QG, D] tensor")
+    for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
+        if tuple(t.shape) != (B, hk, num_partitions, qg) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous [B, Hk, P, QG] tensor")
+    for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t is not None:
+            _need(t, torch.float32, nm)
+    if rot_signs is not None:
+        _need(rot_signs, torch.int8, "rot_signs")
+    if seq_lens.shape != (B,) or block_table.shape[0] != B:
+        raise ValueError("seq_lens / block_table do not match the batch")
+    _check(lib.uq_paged_decode(
+        _ptr(query), _dtype_code(query.dtype), query.stride(0), query.stride(1), _ptr(kv_cache),
+        nb, bs, hk, slot, kv_format, _ptr(k_scale), _ptr(v_scale), _ptr(rot_signs),
+        _ptr(block_table), block_table.stride(0), _ptr(seq_lens), B, Hq, D, int(max_seq_len),
+        float(softmax_scale), int(num_partitions), _ptr(part_out), _ptr(part_max),
+        _ptr(part_sum), _stream(stream)))
+
+
+def paged_reduce(part_out: torch.Tensor, part_max: torch.Tensor, part_sum: torch.Tensor,
+                 seq_lens: torch.Tensor, out: torch.Tensor, *, max_seq_len: int,
+                 stream=None) -> None:
+    """uq_paged_reduce into out [B, Hk*QG, D] (float32 or bfloat16, D contiguous)."""
+    lib = load_library()
+    _need(part_out, torch.bfloat16, "part_out")
+    B, hk, P, qg, D = part_out.shape
+    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (B, hk * qg, D):
+        raise ValueError("out must be [B, Hk*QG, D] with a contiguous head dim")
+    _check(lib.uq_paged_reduce(
+        _ptr(part_out), _ptr(part_max), _ptr(part_sum), _ptr(seq_lens), B, hk, qg, D, P,
+        int(max_seq_len), _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
+        _stream(stream)))
+
+
+def paged_attention(query, kv_cache, block_table, seq_lens, *, kv_format, max_seq_len,
+                    num_partitions, out=None, partials=None, softmax_scale=0.0,
+                    k_scale=None, v_scale=None, rot_signs=None, stream=None):
+    """One decode step: uq_paged_decode then uq_paged_reduce; returns out [B, Hq, D] in
+    the query dtype."""
+    B, Hq, D = query.shape
+    hk = kv_cache.shape[2]
+    if partials is None:
+        partials = alloc_partials(B, hk, Hq // hk, D, num_partitions, query.device)
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=query.dtype, device=query.device)
+    po, pm, pl = partials
+    paged_decode(query, kv_cache, block_table, seq_lens, kv_format=kv_format,
+                 max_seq_len=max_seq_len, num_partitions=num_partitions, part_out=po,
+                 part_max=pm, part_sum=pl, softmax_scale=softmax_scale, k_scale=k_scale,
+                 v_scale=v_scale, rot_signs=rot_signs, stream=stream)
+    paged_reduce(po, pm, pl, seq_lens, out, max_seq_len=max_seq_len, stream=stream)
+    return out
+
+
+def index_score(q: torch.Tensor, k_pages: torch.Tensor, block_table: torch.Tensor,
+                seq_lens: torch.Tensor, scores: torch.Tensor, *, query_len: int,
+                init_blocks: int = 0, local_blocks: int = 0, stream=None) -> None:
+    """uq_index_score: q e4m3 codes [R*QL, H, D] uint8; k_pages [num_pages, page_stride]
+    uint8; scores float32 [H, R*QL, S] (page index contiguous)."""
+    lib = load_library()
+    _need(q, torch.uint8, "q")
+    _need(k_pages, torch.uint8, "k_pages")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(scores, torch.float32, "scores")
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [R*QL, H, D] with contiguous dims")
+    if k_pages.dim() != 2 or k_pages.stride(1) != 1:
+        raise ValueError("k_pages must be [num_pages, page_stride] with contiguous rows")
+    if scores.dim() != 3 or scores.stride(2) != 1:
+        raise ValueError("scores must be [H, R*QL, S] with a contiguous page index")
+    rows, H, D = q.shape
+    R = seq_lens.shape[0]
+    if rows != R * query_len or scores.shape[0] != H or scores.shape[1] != rows:
+        raise ValueError("q / scores shapes do not match seq_lens and query_len")
+    _check(lib.uq_index_score(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_pages), k_pages.stride(0), k_pages.shape[0],
+        _ptr(block_table), block_table.stride(0), _ptr(seq_lens), R, int(query_len), H, D,
+        int(init_blocks), int(local_blocks), _ptr(scores), scores.stride(0), scores.stride(1),
+        scores.shape[2], _stream(stream)))
+
+
+def default_softmax_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

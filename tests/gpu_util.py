@@ -1,0 +1,98 @@
+"""Helpers for the GPU parity tests: move a synthetic case to the device, run the HIP
+path through the C ABI binding, and compare against the oracle."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_paged_attention_amd import synth
+
+try:
+    from quantized_paged_attention_amd import uq
+except Exception:  # pragma: no cover
+    uq = None
+
+DEV = "cuda"
+TOL_DECODE = 1e-2      # max|gpu - ref| <= 1e-2 max|ref|  (fp8 tolerance of the pa_decode_tile PR)
+TOL_INDEX = 1e-4       # relative to max|ref| over finite cells
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def q_tensor(case, strided: bool = False) -> torch.Tensor:
+    dt = torch.float32 if case.q_dtype == "f32" else torch.bfloat16
+    q = torch.from_numpy(case.q).to(dt)
+    if strided:
+        # Q as a slice of a fused [B, Hq + 2 Hk, D] QKV projection
+        B, Hq, D = q.shape
+        big = torch.zeros(B, Hq + 2 * case.num_kv_heads, D, dtype=dt)
+        big[:, :Hq] = q
+        return big.to(DEV)[:, :Hq]
+    return q.to(DEV)
+
+
+def device_case(case):
+    return dict(
+        cache=torch.from_numpy(case.cache).to(DEV),
+        bt=torch.from_numpy(case.block_table).to(DEV),
+        sl=torch.from_numpy(case.seq_lens).to(DEV),
+        ks=(torch.tensor([case.k_scale], dtype=torch.float32, device=DEV)
+            if case.kv_format == synth.FMT_FP8_E4M3 else None),
+        vs=(torch.tensor([case.v_scale], dtype=torch.float32, device=DEV)
+            if case.kv_format == synth.FMT_FP8_E4M3 else None),
+        rot=(torch.from_numpy(case.rot_signs).to(DEV) if case.rot_signs is not None else None),
+    )
+
+
+def run_decode(case, P=None, strided=False, dev=None, q=None, partials=None, out=None):
+    """HIP decode + reduce; returns (out float64 numpy, (po, pm, pl) torch tensors)."""
+    dev = dev or device_case(case)
+    P = P or case.num_partitions
+    q = q if q is not None else q_tensor(case, strided)
+    B, Hq, D = q.shape
+    hk = case.num_kv_heads
+    partials = partials or uq.alloc_partials(B, hk, Hq // hk, D, P)
+    out = uq.paged_attention(q, dev["cache"], dev["bt"], dev["sl"], kv_format=case.kv_format,
+                             max_seq_len=case.max_seq_len, num_partitions=P, partials=partials,
+                             out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"],
+                             v_scale=dev["vs"], rot_signs=dev["rot"])
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), partials
+
+
+def oracle_decode(case, P=0):
+    from oracle import oracle
+    return oracle.decode(case.q, case.cache, case.block_table, case.seq_lens,
+                         num_kv_heads=case.num_kv_heads, kv_format=case.kv_format,
+                         softmax_scale=case.softmax_scale, k_scale=case.k_scale,
+                         v_scale=case.v_scale, rot_signs=case.rot_signs, num_partitions=P)
+
+
+def rel_err(got, ref):
+    scale = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / (scale if scale > 0 else 1.0))
+
+
+def assert_decode_close(got, ref, what=""):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    e = rel_err(got, ref)
+    log(f"  {what}: max|err|/max|ref| = {e:.3e}")
+    assert e <= TOL_DECODE, f"{what}: relative error {e:.3e} > {TOL_DECODE}"
+    return e

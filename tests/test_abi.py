@@ -1,0 +1,136 @@
+"""The C ABI: libuq.so loads, exports every function include/uq_paged.h declares, and its
+host-side validation rejects bad arguments before launching anything (CPU only: no call
+here reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_paged_attention_amd import uq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uq_paged.h")
+
+# fake, never-dereferenced device addresses (validation fails before any use)
+FAKE = 0x10000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uq_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(uq.LIB_PATH):
+        pytest.skip("libuq.so not built")
+    return uq.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(uq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def decode_args(**over):
+    a = dict(query=FAKE, q_dtype=uq.UQ_BF16, q_ss=64 * 128, q_sh=128, cache=FAKE, nb=16, bs=16,
+             hk=8, slot=256, fmt=uq.UQ_KV_FP8_E4M3, ks=None, vs=None, rot=None, bt=FAKE,
+             bt_stride=1024, sl=FAKE, B=4, Hq=64, D=128, max_len=16384, scale=0.0, P=64,
+             po=FAKE, pm=FAKE, pl=FAKE, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Hq=60), uq.UQ_ERR_INVALID_ARG),                 # Hq not a multiple of Hk
+    (dict(Hq=8 * 17), uq.UQ_ERR_INVALID_ARG),             # QG > 16
+    (dict(q_dtype=7), uq.UQ_ERR_INVALID_ARG),
+    (dict(bs=24), uq.UQ_ERR_INVALID_ARG),
+    (dict(bs=512), uq.UQ_ERR_INVALID_ARG),
+    (dict(slot=255), uq.UQ_ERR_INVALID_ARG),
+    (dict(slot=258), uq.UQ_ERR_INVALID_ARG),              # not 4-aligned
+    (dict(P=0), uq.UQ_ERR_INVALID_ARG),
+    (dict(max_len=-1), uq.UQ_ERR_INVALID_ARG),
+    (dict(bt_stride=10), uq.UQ_ERR_INVALID_ARG),          # table row too short for max_len
+    (dict(query=None), uq.UQ_ERR_INVALID_ARG),
+    (dict(po=None), uq.UQ_ERR_INVALID_ARG),
+    (dict(q_sh=0), uq.UQ_ERR_INVALID_ARG),
+    (dict(q_sh=129), uq.UQ_ERR_INVALID_ARG),              # stride not 16-byte aligned
+    (dict(fmt=9), uq.UQ_ERR_INVALID_ARG),
+    (dict(D=64, slot=128), uq.UQ_ERR_UNSUPPORTED),        # fp8 supports D=128 only
+    (dict(Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),             # fp8 QG up to 8
+    (dict(rot=FAKE), uq.UQ_ERR_UNSUPPORTED),              # rotation needs an fp4 cache
+    (dict(fmt=uq.UQ_KV_FP4_E2M1_UE8M0S, D=256, slot=272, Hq=8 * 8), uq.UQ_ERR_UNSUPPORTED),
+    (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 4), uq.UQ_ERR_UNSUPPORTED),
+    (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 8, ks=FAKE), uq.UQ_ERR_INVALID_ARG),
+    (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=268, Hq=8 * 8), uq.UQ_ERR_INVALID_ARG),
+])
+def test_decode_validation(lib, over, status):
+    st = lib.uq_paged_decode(*decode_args(**over))
+    assert st == status, lib.uq_last_error()
+    assert lib.uq_last_error().decode()
+
+
+def test_decode_zero_sequences_is_a_no_op(lib):
+    assert lib.uq_paged_decode(*decode_args(B=0)) == uq.UQ_OK
+    assert lib.uq_last_error() == b""
+
+
+def reduce_args(**over):
+    a = dict(po=FAKE, pm=FAKE, pl=FAKE, sl=FAKE, B=4, hk=8, qg=8, D=128, P=64, max_len=100,
+             out=FAKE, dt=uq.UQ_BF16, o_ss=64 * 128, o_sh=128, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(qg=0), uq.UQ_ERR_INVALID_ARG), (dict(qg=17), uq.UQ_ERR_INVALID_ARG),
+    (dict(D=64), uq.UQ_ERR_UNSUPPORTED), (dict(P=0), uq.UQ_ERR_INVALID_ARG),
+    (dict(dt=5), uq.UQ_ERR_INVALID_ARG), (dict(out=None), uq.UQ_ERR_INVALID_ARG),
+    (dict(o_sh=4), uq.UQ_ERR_INVALID_ARG), (dict(max_len=-5), uq.UQ_ERR_INVALID_ARG),
+])
+def test_reduce_validation(lib, over, status):
+    assert lib.uq_paged_reduce(*reduce_args(**over)) == status
+
+
+def index_args(**over):
+    a = dict(q=FAKE, q_st=512, q_sh=128, pages=FAKE, pstride=9216, npages=100, bt=FAKE,
+             bt_stride=256, sl=FAKE, R=32, QL=2, H=4, D=128, init=0, local=0, scores=FAKE,
+             s_sh=64 * 256, s_st=256, max_blocks=256, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(H=3), uq.UQ_ERR_INVALID_ARG), (dict(QL=16, H=4), uq.UQ_ERR_INVALID_ARG),
+    (dict(QL=0), uq.UQ_ERR_INVALID_ARG), (dict(D=64), uq.UQ_ERR_UNSUPPORTED),
+    (dict(init=1), uq.UQ_ERR_UNSUPPORTED), (dict(local=2), uq.UQ_ERR_UNSUPPORTED),
+    (dict(pstride=9200), uq.UQ_ERR_INVALID_ARG), (dict(pstride=9224), uq.UQ_ERR_INVALID_ARG),
+    (dict(q_st=100), uq.UQ_ERR_INVALID_ARG), (dict(scores=None), uq.UQ_ERR_INVALID_ARG),
+    (dict(npages=0), uq.UQ_ERR_INVALID_ARG),
+])
+def test_index_validation(lib, over, status):
+    assert lib.uq_index_score(*index_args(**over)) == status
+
+
+def test_workspace_bytes(lib):
+    n = uq.decode_workspace_bytes(128, 8, 8, 128, 64)
+    rows = 128 * 8 * 64 * 8
+    assert n == rows * 128 * 2 + 2 * rows * 4
+    assert uq.decode_workspace_bytes(1, 0, 8, 128, 64) == 0
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        uq.paged_decode(q, torch.zeros(1, 16, 1, 256, dtype=torch.uint8),
+                        torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                        kv_format=0, max_seq_len=1, num_partitions=1,
+                        part_out=torch.zeros(1, 1, 1, 8, 128, dtype=torch.bfloat16),
+                        part_max=torch.zeros(1, 1, 1, 8), part_sum=torch.zeros(1, 1, 1, 8))

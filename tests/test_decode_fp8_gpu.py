@@ -1,0 +1,193 @@
+"""GPU parity of the fp8 e4m3 decode + reduce path against the fp64 oracle."""
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_paged_attention_amd import synth
+from tests.gpu_util import (assert_decode_close, device_case, log, need_gpu, oracle_decode,
+                            q_tensor, rel_err, run_decode, uq)
+
+pytestmark = pytest.mark.gpu
+
+EDGE_LENS = (1, 15, 16, 17, 31, 255, 256, 257, 513, 1000)
+
+
+def small(seed=31, lens=EDGE_LENS, hk=2, qg=8, bs=16, **kw):
+    kw.setdefault("values", "uniform_codes")
+    kw.setdefault("k_scale", 0.05)
+    kw.setdefault("v_scale", 0.02)
+    return synth.make_fp8_case("fp8_small", seed, seq_lens=list(lens), num_kv_heads=hk, qg=qg,
+                               block_size=bs, spare_blocks=7, **kw)
+
+
+def test_tiny_config():
+    """B=2, Hk=1, QG=8, L={37, 200}, fp32 Q, one partition (the tiny workload)."""
+    need_gpu()
+    case = synth.tiny_fp8()
+    log(f"case tiny_fp8 seq_lens={case.seq_lens.tolist()}")
+    got, (po, pm, pl) = run_decode(case)
+    ref, (rm, rl, ro) = oracle_decode(case, case.num_partitions)
+    assert_decode_close(got, ref, "tiny_fp8 out")
+    # partition statistics themselves
+    np.testing.assert_allclose(pm.cpu().numpy(), rm, rtol=2e-3, atol=2e-3)
+    np.testing.assert_allclose(pl.cpu().numpy(), rl, rtol=2e-2)
+    assert rel_err(po.float().cpu().numpy(), ro) <= 1e-2
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 7])
+@pytest.mark.parametrize("q_dtype", ["bf16", "f32"])
+def test_edge_lengths_and_partitions(P, q_dtype):
+    need_gpu()
+    case = small(q_dtype=q_dtype)
+    log(f"case fp8 edge lens P={P} q={q_dtype}")
+    got, _ = run_decode(case, P=P)
+    assert_decode_close(got, oracle_decode(case), f"edge P={P} {q_dtype}")
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_block_sizes(bs):
+    need_gpu()
+    case = small(bs=bs, lens=(3, 300, 700, 1200), seed=32 + bs)
+    log(f"case fp8 block_size={bs}")
+    got, _ = run_decode(case, P=2)
+    assert_decode_close(got, oracle_decode(case), f"bs={bs}")
+
+
+@pytest.mark.parametrize("qg", [1, 2, 4, 6, 8])
+def test_query_groups(qg):
+    need_gpu()
+    case = small(qg=qg, hk=3, lens=(40, 600), seed=40 + qg)
+    log(f"case fp8 qg={qg}")
+    got, _ = run_decode(case, P=3)
+    assert_decode_close(got, oracle_decode(case), f"qg={qg}")
+
+
+def test_strided_query_from_fused_qkv():
+    need_gpu()
+    case = small(lens=(100, 777), seed=50)
+    got, _ = run_decode(case, P=2, strided=True)
+    assert_decode_close(got, oracle_decode(case), "strided q")
+
+
+def test_normal_values_unit_scales():
+    need_gpu()
+    case = small(values="normal", k_scale=1.0, v_scale=1.0, seed=51, lens=(2000, 5, 4096))
+    got, _ = run_decode(case, P=4)
+    assert_decode_close(got, oracle_decode(case), "normal values")
+
+
+def test_zero_length_sequences():
+    need_gpu()
+    case = small(lens=(0, 20, 0), seed=52)
+    got, _ = run_decode(case, P=2)
+    ref = oracle_decode(case)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert_decode_close(got, ref, "zero length")
+
+
+def test_one_hot_gather_bit_exact():
+    """Q = 100 e0, one key with K[0] = 448 and zeros elsewhere: every other weight is
+    exactly zero, so the output must equal v[t*] bit for bit (v_scale = 1)."""
+    need_gpu()
+    bs = 16
+    L = 10 * bs + 5
+    case = small(lens=(L,), hk=1, qg=8, bs=bs, values="normal", k_scale=1.0, v_scale=1.0,
+                 q_dtype="f32", seed=53)
+    D = case.D
+    case.q[:] = 0.0
+    case.q[:, :, 0] = 100.0
+    from tests.refdense import dense_kv
+    for tstar in (0, 15, 16, 17, 31, 32, 100, L - 1):
+        c = copy.deepcopy(case)
+        c.cache[..., :D] = 0
+        c.cache[c.block_table[0, tstar // bs], tstar % bs, 0, 0] = 0x7E
+        got, _ = run_decode(c, P=1)
+        _, v = dense_kv(c, 0, 0)
+        for g in range(8):
+            assert np.array_equal(got[0, g], v[tstar]), (tstar, g)
+
+
+def test_block_permutation_bit_identical():
+    need_gpu()
+    case = small(lens=(17, 300, 513, 2000), seed=54)
+    base, _ = run_decode(case, P=3)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(case.cache.shape[0])
+    c2 = copy.deepcopy(case)
+    c2.cache = np.empty_like(case.cache)
+    c2.cache[perm] = case.cache
+    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)],
+                              -1).astype(np.int32)
+    got, _ = run_decode(c2, P=3)
+    assert np.array_equal(got, base)
+
+
+def test_masked_bytes_bit_identical():
+    """Slots past L (NaN-poisoned by the generator), unreferenced blocks and table tails
+    changed to other garbage must not change a single output bit."""
+    need_gpu()
+    case = small(lens=(3, 20, 33, 250), seed=55)
+    base, _ = run_decode(case, P=2)
+    assert np.isfinite(base).all()
+    c2 = copy.deepcopy(case)
+    used = np.zeros(c2.cache.shape[0], bool)
+    for b, L in enumerate(c2.seq_lens):
+        n = -(-int(L) // c2.block_size)
+        used[c2.block_table[b, :n]] = True
+        if L % c2.block_size:
+            c2.cache[c2.block_table[b, L // c2.block_size], L % c2.block_size:] = 0x7E
+        c2.block_table[b, n:] = 1 << 30
+    c2.cache[~used] = 0xFE
+    got, _ = run_decode(c2, P=2)
+    assert np.array_equal(got, base)
+
+
+def test_reduce_against_oracle_partials():
+    """The reduce kernel alone, fed the oracle's partials (rounded to the workspace
+    types), including empty partitions (m = -inf, l = 0)."""
+    need_gpu()
+    from oracle import oracle
+    case = small(lens=(0, 1, 256, 257, 1500), seed=56)
+    P = 4
+    _, (rm, rl, ro) = oracle_decode(case, P)
+    po = torch.from_numpy(ro).to(torch.bfloat16)
+    pm = torch.from_numpy(rm).to(torch.float32)
+    pl = torch.from_numpy(rl).to(torch.float32)
+    want = oracle.reduce(po.double().numpy(), pm.double().numpy(), pl.double().numpy(),
+                         case.seq_lens)
+    out = torch.empty(case.B, case.Hq, case.D, dtype=torch.float32, device="cuda")
+    uq.paged_reduce(po.cuda(), pm.cuda(), pl.cuda(), torch.from_numpy(case.seq_lens).cuda(), out,
+                    max_seq_len=case.max_seq_len)
+    got = out.cpu().double().numpy()
+    assert np.all(got[0] == 0)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
+
+
+def test_mid_config_full():
+    """B=16, Hk=8, QG=8, L=16384, bf16 Q, 64 partitions, k/v scales 0.05/0.02."""
+    need_gpu()
+    case = synth.fp8_mid()
+    log("case fp8_mid (full)")
+    got, _ = run_decode(case)
+    assert_decode_close(got, oracle_decode(case), "fp8_mid")
+
+
+def test_high_config_sampled():
+    """B=128 with L ~ U[4096, 16384] at full size on the GPU; the oracle checks a sample
+    of 12 sequences (all their heads), including the shortest and longest."""
+    need_gpu()
+    case = synth.fp8_high()
+    log(f"case fp8_high (full GPU run, sampled oracle) kv_bytes={case.kv_bytes()}")
+    got, _ = run_decode(case)
+    order = np.argsort(case.seq_lens)
+    pick = sorted(set([int(order[0]), int(order[-1])] +
+                      list(np.random.default_rng(0).choice(case.B, 10, replace=False))))
+    sub = copy.copy(case)
+    sub.q = case.q[pick]
+    sub.block_table = case.block_table[pick]
+    sub.seq_lens = case.seq_lens[pick]
+    ref = oracle_decode(sub)
+    assert_decode_close(got[pick], ref, "fp8_high sample")

@@ -148,7 +148,8 @@ def test_block_permutation_invariance():
     c2 = copy.deepcopy(case)
     c2.cache = np.empty_like(case.cache)
     c2.cache[perm] = case.cache
-    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1)
+    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)],
+                              -1).astype(np.int32)
     assert np.array_equal(run(c2), base)
 
 

@@ -91,7 +91,8 @@ def test_permutation_invariance_and_untouched_cells():
     c2 = copy.deepcopy(case)
     c2.pages = np.empty_like(case.pages)
     c2.pages[perm] = case.pages
-    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)], -1)
+    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)],
+                              -1).astype(np.int32)
     got = run(c2)
     assert np.array_equal(np.isnan(got), np.isnan(base))
     assert np.array_equal(got[~np.isnan(got)], base[~np.isnan(base)])
