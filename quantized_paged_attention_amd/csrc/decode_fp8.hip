@@ -3,25 +3,29 @@
 //
 // What is computed (ROCm/FlyDSL PR #825 "pa_decode_tile": per-tensor fp8 K/V decode with
 // a cross-workgroup partition split; vLLM "ultraquant_decode_hd256" page: strided
-// partition -> 256-token tile-group map, online softmax of STEP F, epilogue of STEP G):
-// for a work unit (sequence b, kv head h, partition p) the softmax statistics
+// partition -> 256-token tile-group map, softmax statistics of STEP F, epilogue of
+// STEP G): for a work unit (sequence b, kv head h, partition p) the softmax statistics
 // (m, l, o = v_scale * sum exp(s - m) v / l) of the tokens of tile-groups p, p+P, ...
 //
-// Design (one 64-lane wave per work unit, no LDS):
-//   * QK: one 16x16x128 fp8 MFMA per 16-token tile.  A = K codes straight from HBM
-//     (lane = token, 32 head dims per lane), B = the query group as an e4m3 hi + lo pair:
-//     columns 0-7 carry hi(q * s_q), columns 8-15 carry lo = q * s_q - hi, so one MFMA
-//     gives both halves and a DPP row rotate adds them.  s_q is a per-row power of two,
-//     so the pair reproduces a bf16 query exactly.
-//   * Softmax is register resident in the MFMA output layout (lane = query column,
-//     4 tokens per lane); row max/sum cross lanes with xor 16 / xor 32 only.
-//   * PV: P (scaled by 256 so its small values stay normal in e4m3) is again split into
-//     hi/lo columns; V^T comes from registers: each lane loads 8 head dims of 4 tokens
-//     per tile and a v_perm byte transpose turns them into the 16x16x32 fp8 A operand.
-//     The output lane keeps one query column, so the online-softmax rescale needs no
-//     cross-lane traffic.
-//   * KV bytes are loaded once, non-temporal, with the next tile pairs in flight while
-//     the current pair computes.
+// Design (one 64-lane wave per work unit, no LDS, KV streamed once):
+//   * A tile-group (256 tokens = 16 tiles of 16) is processed in three phases, so the
+//     softmax needs one max and no running rescale inside the group:
+//       A. QK for all 16 tiles: per tile two 16x16x128 fp8 MFMAs with A = the K codes
+//          straight from HBM (lane = token, 32 head dims per lane) and B = the query
+//          group as an e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q) / lo(q s_q) in the
+//          first MFMA and the swapped order in the second, so every column ends with
+//          hi + lo of its row.  s_q is a per-row power of two: the pair reproduces a bf16
+//          query exactly.  Scores stay in registers (4 tokens x 16 tiles per lane).
+//       B. Softmax over the group: max across the 4 token lanes (xor 16 / xor 32),
+//          p = 2^(s - m + 8) (the 2^8 keeps small p normal in e4m3), P as hi/lo pair.
+//       C. PV: V^T comes from registers -- each lane loads 8 head dims of 4 tokens per
+//          tile and a v_perm byte transpose forms the 16x16x32 fp8 A operand; B = P with
+//          hi in columns 0-7 and lo in columns 8-15; accumulators stay in the MFMA
+//          output layout (lane = query column), added hi + lo once in the epilogue.
+//     Several tile-groups per unit (few partitions) merge with one rescale per group.
+//   * KV loads are buffer loads from a scalar per-tile base and constant per-lane
+//     offsets, non-temporal, issued several tiles ahead of their use; only the tail
+//     tile-group pays for masking.
 #include "uq_device.h"
 #include "uq_kernels.h"
 
@@ -29,51 +33,53 @@ namespace uq {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kPipe = 2;  // tile pairs in flight ahead of the one being computed
+constexpr int kTiles = 16;     // tiles of 16 tokens per tile-group
+constexpr int kAuxNT = 0;      // buffer cache policy bits (0: default)
 
-struct Tile {
-  i32x4 k0, k1;  // K bytes [16r, 16r+16) and [64+16r, 64+16r+16) of token n
-  i32x2 v[4];    // V bytes [8n, 8n+8) of tokens 4r + j
+struct KTile {
+  i32x4 a, b;  // K bytes [16r, 16r+16) and [64+16r, 64+16r+16) of token n
+};
+struct VTile {
+  i32x2 v[4];  // V bytes [8n, 8n+8) of tokens 4r + j
 };
 
-__device__ __forceinline__ void load_tile(Tile& t, const uint8_t* base, bool valid, int k_off,
-                                          int v_off, int pos_stride) {
-  if (valid) {
-    t.k0 = nt_load(reinterpret_cast<const i32x4*>(base + k_off));
-    t.k1 = nt_load(reinterpret_cast<const i32x4*>(base + k_off + 64));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      t.v[j] = nt_load(reinterpret_cast<const i32x2*>(base + v_off + j * pos_stride));
-  } else {
-    t.k0 = i32x4{0, 0, 0, 0};
-    t.k1 = i32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t.v[j] = i32x2{0, 0};
-  }
-}
-
 template <typename QT, int W>
-__global__ __launch_bounds__(64 * W) void decode_fp8_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t unit = (int64_t)blockIdx.x * W + (threadIdx.x >> 6);
-  if (unit >= (int64_t)a.P * a.B * a.Hk) return;
-  const int h = (int)(unit % a.Hk);
-  const int b = (int)((unit / a.Hk) % a.B);
-  const int p = (int)(unit / ((int64_t)a.Hk * a.B));
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t item = (int64_t)blockIdx.x * W + wave;
+  if (item >= (int64_t)a.runs * a.B * a.Hk) return;
+  const int h = (int)(item % a.Hk);
+  const int b = (int)((item / a.Hk) % a.B);
+  const int run = (int)(item / ((int64_t)a.Hk * a.B));
 
-  int L = a.seq_lens[b];
+  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);  // wave-uniform
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int ntg = (L + kTileGroup - 1) / kTileGroup;
-  if (p >= ntg) return;  // empty partition: nothing written, never read by the reduce
-  int trips = (ntg - p + a.P - 1) / a.P;
-  trips = trips < a.TGPP ? trips : a.TGPP;
+  // The wave's tile-groups: first_tg, first_tg + step, ...  With one tile-group per
+  // partition (run_len > 0) a run covers partitions [run * run_len, +run_len), each
+  // flushed on its own; otherwise the wave owns partition `run` and its strided
+  // tile-groups p, p+P, ... (the partition -> tile-group map of the FP4 decode page).
+  int first_tg, n_tg, step;
+  if (a.run_len > 0) {
+    first_tg = run * a.run_len;
+    const int lim = (a.P < ntg ? a.P : ntg) - first_tg;
+    n_tg = lim < a.run_len ? lim : a.run_len;
+    step = 1;
+  } else {
+    first_tg = run;
+    n_tg = run < ntg ? (ntg - run + a.P - 1) / a.P : 0;
+    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+    step = a.P;
+  }
+  if (n_tg <= 0) return;  // empty partitions: nothing written, never read by the reduce
 
   const int r = lane >> 4, n = lane & 15;
   const int g = n & 7;
   const bool lo_col = n >= 8;
 
-  // ---- query operand: hi/lo e4m3 pair of q * s_q, B layout of the 16x16x128 MFMA.
-  // Byte j of lane group r holds head dim d = j < 16 ? 16r + j : 64 + 16r + (j - 16).
+  // ---- query operands.  Byte j of lane group r holds head dim
+  //      d = j < 16 ? 16 r + j : 64 + 16 r + (j - 16)   (same map as the K loads)
   float x[32];
   const bool qvalid = g < a.QG;
   {
@@ -105,8 +111,7 @@ __global__ __launch_bounds__(64 * W) void decode_fp8_kernel(DecodeArgs a) {
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = fmaxf(amax, xor_lane(amax, 16));
-  amax = fmaxf(amax, xor_lane(amax, 32));
+  amax = max_across_rows(amax);
   // s_q = 2^(7 - E) with amax = f 2^E, f in [0.5, 1): amax * s_q in [64, 128)
   int E = 0;
   if (amax > 0.f) {
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(64 * W) void decode_fp8_kernel(DecodeArgs a) {
   const float v_scale = a.v_scale ? *a.v_scale : 1.f;
   const float qk_mul = a.softmax_scale * k_scale * kLog2e / s_q;
 
-  i32x8 qop;
+  i32x8 q_own;  // hi(q s_q) in columns 0-7, lo(q s_q) in columns 8-15
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     float y0 = x[4 * w] * s_q, y1 = x[4 * w + 1] * s_q, y2 = x[4 * w + 2] * s_q,
@@ -127,156 +132,214 @@ __global__ __launch_bounds__(64 * W) void decode_fp8_kernel(DecodeArgs a) {
     hw = cvt_pk_e4m3<true>(y2, y3, hw);
     int lw = cvt_pk_e4m3<false>(y0 - e4m3_to_f<0>(hw), y1 - e4m3_to_f<1>(hw), 0);
     lw = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hw), y3 - e4m3_to_f<3>(hw), lw);
-    qop[w] = qvalid ? (lo_col ? lw : hw) : 0;
+    hw = qvalid ? hw : 0;
+    lw = qvalid ? lw : 0;
+    q_own[w] = lo_col ? lw : hw;
   }
 
-  // ---- state
-  float m_run = -INFINITY, l_run = 0.f;
+  // ---- running state across tile-groups
+  // base-2 state: m_run is a reference max >= every score seen, m_true the max itself,
+  // l_run the sum of 2^(s - m_run + 8)
+  float m_run = -INFINITY, m_true = -INFINITY, l_run = 0.f;
   f32x4 acc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int pos_stride = a.pos_stride;
-  const int k_off = n * pos_stride + 16 * r;
-  const int v_off = 4 * r * pos_stride + kD + 8 * n;
+  const uint32_t pos = (uint32_t)a.pos_stride;
+  const uint32_t k_off = n * pos + 16 * r;
+  const uint32_t v_off = 4 * r * pos + kD + 8 * n;
   const uint8_t* head_base = a.cache + (int64_t)h * a.slot_bytes;
   const int32_t* bt_row = a.bt + (int64_t)b * a.bt_stride;
+  const int bs_shift = 31 - __builtin_clz(a.block_size);
 
-  for (int it = 0; it < trips; ++it) {
-    const int tg_start = (p + it * a.P) * kTileGroup;
-    // block id of tile t held by lane t (tiles past the context are not looked up)
-    int my_blk = 0;
-    if (lane < 16 && tg_start + 16 * lane < L) my_blk = bt_row[(tg_start + 16 * lane) / a.block_size];
-
-    auto tile_base = [&](int t) -> const uint8_t* {
-      const int blk = __builtin_amdgcn_readlane(my_blk, t);
-      const int tok = tg_start + 16 * t;
-      return head_base + (int64_t)blk * a.blk_stride + (int64_t)(tok % a.block_size) * pos_stride;
+  // Block ids come in windows of 8 work tile-groups: lane i holds the id of tile i % 16
+  // of tile-group w0 + i / 16 (lo) and of w0 + 4 + i / 16 (hi).  The window is loaded
+  // before the stream starts, so no vector-memory wait inside the stream waits for a
+  // table load (vector loads retire in order: such a wait would drain every KV load
+  // issued after it).  Only a wave with more than 8 tile-groups (a partition that owns
+  // several strided tile-groups) reloads it, once per 8.  Tiles past L, or past the
+  // wave's tile-groups, keep id 0 and are never dereferenced.
+  int win_lo, win_hi;
+  auto load_window = [&](int w0) {
+    auto one = [&](int k) {
+      int v = 0;
+      if (k < n_tg) {
+        const int tok = (first_tg + k * step) * kTileGroup + 16 * (lane & 15);
+        if (tok < L) v = bt_row[tok >> bs_shift];
+      }
+      return v;
     };
+    win_lo = one(w0 + (lane >> 4));
+    win_hi = one(w0 + 4 + (lane >> 4));
+  };
+  load_window(0);
 
-    Tile ring[kPipe + 1][2];
+  // Buffer resource of tile t (0..15) of work tile-group kk (in the current window):
+  // base = the tile's first slot of this head, record count = its visible tokens only
+  // (0 past L or past the wave's tile-groups), so every K/V byte of an invisible token
+  // reads as zero with no branch, no select and no memory access.
+  auto rsrc_of = [&](int kk, int t) {
+    const int idx = (kk & 3) * 16 + t;
+    const int b_lo = __builtin_amdgcn_readlane(win_lo, idx);
+    const int b_hi = __builtin_amdgcn_readlane(win_hi, idx);
+    const int blk = (kk & 7) >= 4 ? b_hi : b_lo;
+    const int tok = (first_tg + kk * step) * kTileGroup + 16 * t;
+    int nvis = L - tok;
+    nvis = kk >= n_tg ? 0 : (nvis < 0 ? 0 : (nvis > 16 ? 16 : nvis));
+    const uint64_t base = (uint64_t)(head_base + (int64_t)blk * a.blk_stride +
+                                     (int64_t)(tok & (a.block_size - 1)) * pos);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                             (short)0, __builtin_amdgcn_readfirstlane(nvis * (int)pos),
+                                             0x00020000);
+  };
+  auto load_k = [&](__amdgpu_buffer_rsrc_t rs, KTile& d) {
+    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kAuxNT);
+    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 64, 0, kAuxNT);
+  };
+  auto load_v = [&](__amdgpu_buffer_rsrc_t rs, VTile& d) {
 #pragma unroll
-    for (int s = 0; s < kPipe; ++s) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = 2 * s + tt;
-        const bool valid = tg_start + 16 * t < L;
-        load_tile(ring[s][tt], valid ? tile_base(t) : head_base, valid, k_off, v_off, pos_stride);
-      }
-    }
+    for (int j = 0; j < 4; ++j)  // token offset j * pos rides in the scalar offset
+      d.v[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, v_off, j * (int)pos, kAuxNT);
+  };
 
+  // The stream walks tile pairs (32 tokens).  The K loads of pair i + 1 are issued as
+  // soon as the QK MFMAs of pair i have read their registers and its V loads as soon as
+  // the V^T transpose of pair i has read them, so one pair of KV bytes is always in
+  // flight while the wave computes; the register footprint stays small enough for four
+  // waves per SIMD, which is what keeps the memory system busy.  No data-dependent
+  // branches except a rare wave-uniform softmax rescale.
+  KTile kp[2];
+  VTile vp[2];
+  {
+    const auto r0 = rsrc_of(0, 0), r1 = rsrc_of(0, 1);
+    load_k(r0, kp[0]);
+    load_k(r1, kp[1]);
+    load_v(r0, vp[0]);
+    load_v(r1, vp[1]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int k = 0; k < n_tg; ++k) {
+    const int tg = first_tg + k * step;
+    const int tg_start = tg * kTileGroup;
 #pragma unroll
-    for (int pr = 0; pr < 8; ++pr) {
-      // issue the loads kPipe pairs ahead
-      if (pr + kPipe < 8) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * (pr + kPipe) + tt;
-          const bool valid = tg_start + 16 * t < L;
-          load_tile(ring[(pr + kPipe) % (kPipe + 1)][tt], valid ? tile_base(t) : head_base,
-                    valid, k_off, v_off, pos_stride);
-        }
-      }
-      Tile* cur = ring[pr % (kPipe + 1)];
+    for (int pr = 0; pr < kTiles / 2; ++pr) {
       const int pair_start = tg_start + 32 * pr;
-
-      // ---- QK: S^T[token][column] for both tiles
+      const int pf_k = pr + 1 < kTiles / 2 ? k : k + 1;  // the next pair
+      const int pf_t0 = pr + 1 < kTiles / 2 ? 2 * (pr + 1) : 0;
+      if (pr == kTiles / 2 - 1 && (k & 7) == 7 && k + 1 < n_tg) load_window(k + 1);  // rare
+      // ---- QK: S^T[token][column] of both tiles, hi + lo columns added by DPP
       float s[2][4];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const i32x8 kop = {cur[tt].k0[0], cur[tt].k0[1], cur[tt].k0[2], cur[tt].k0[3],
-                           cur[tt].k1[0], cur[tt].k1[1], cur[tt].k1[2], cur[tt].k1[3]};
+        const i32x8 kop = {kp[tt].a[0], kp[tt].a[1], kp[tt].a[2], kp[tt].a[3],
+                           kp[tt].b[0], kp[tt].b[1], kp[tt].b[2], kp[tt].b[3]};
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qop, z, 0, 0, 0, 127, 0, 127);
+        z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own, z, 0, 0, 0, 127, 0, 127);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float v = z[j] + row_ror8(z[j]);  // hi column + lo column
-          v *= qk_mul;
-          const int tok = pair_start + 16 * tt + 4 * r + j;
-          s[tt][j] = tok < L ? v : -INFINITY;
+          const float v = (z[j] + row_ror8(z[j])) * qk_mul;
+          s[tt][j] = pair_start + 16 * tt + 4 * r + j < L ? v : -INFINITY;
         }
       }
-      // ---- online softmax (base 2)
-      float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      mloc = fmaxf(mloc, xor_lane(mloc, 16));
-      mloc = fmaxf(mloc, xor_lane(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float pv[2][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pv[tt][j] = fast_exp2(s[tt][j] - m_use);
-          psum += pv[tt][j];
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] *= alpha;
+      // Stage order is fixed: the scheduler must not hoist the prefetch loads above the
+      // instructions that free their registers, nor sink them below later waits (vector
+      // loads retire in order, so a misplaced load turns a partial wait into a drain).
+      __builtin_amdgcn_sched_barrier(0);
+      const auto rs0 = rsrc_of(pf_k, pf_t0), rs1 = rsrc_of(pf_k, pf_t0 + 1);
+      load_k(rs0, kp[0]);
+      load_k(rs1, kp[1]);
+      __builtin_amdgcn_sched_barrier(0);
 
-      // ---- P operand: e4m3 hi (columns 0-7) / lo (columns 8-15) of 256 p
+      // ---- softmax against a reference max m_run >= every score seen.  It is raised
+      // (with 4 units of base-2 headroom, so raises are rare) only when a score exceeds
+      // it; then the running sums are rescaled.  p * 256 = 2^(s - m_run + 8) <= 256.
+      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      mx = max_across_rows(mx);
+      m_true = fmaxf(m_true, mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m_run)) {  // wave-uniform
+        const float m_new = mx > m_run ? mx + 4.f : m_run;
+        const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] *= alpha;
+        m_run = m_new;
+      }
+      const float m8 = m_run - 8.f;
       int pw[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const float y0 = pv[tt][0] * 256.f, y1 = pv[tt][1] * 256.f, y2 = pv[tt][2] * 256.f,
-                    y3 = pv[tt][3] * 256.f;
-        int hw = cvt_pk_e4m3<false>(y0, y1, 0);
-        hw = cvt_pk_e4m3<true>(y2, y3, hw);
-        int lw = cvt_pk_e4m3<false>(y0 - e4m3_to_f<0>(hw), y1 - e4m3_to_f<1>(hw), 0);
-        lw = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hw), y3 - e4m3_to_f<3>(hw), lw);
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y[j] = fast_exp2(s[tt][j] - m8);
+          l_run += y[j];
+        }
+        int hw = cvt_pk_e4m3<false>(y[0], y[1], 0);
+        hw = cvt_pk_e4m3<true>(y[2], y[3], hw);
+        int lw = cvt_pk_e4m3<false>(y[0] - e4m3_to_f<0>(hw), y[1] - e4m3_to_f<1>(hw), 0);
+        lw = cvt_pk_e4m3<true>(y[2] - e4m3_to_f<2>(hw), y[3] - e4m3_to_f<3>(hw), lw);
         pw[tt] = lo_col ? lw : hw;
       }
       const long pop = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
 
-      // ---- V^T operand: byte transpose of 8 dims x 4 tokens per tile; masked tokens -> 0
-      uint32_t vt[2][8];
+      // ---- V^T: byte transpose of 8 dims x 4 tokens per tile
+      uint32_t vtr[2][8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         uint32_t lo4[4], hi4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool ok = pair_start + 16 * tt + 4 * r + j < L;
-          lo4[j] = ok ? (uint32_t)cur[tt].v[j][0] : 0u;
-          hi4[j] = ok ? (uint32_t)cur[tt].v[j][1] : 0u;
+          lo4[j] = (uint32_t)vp[tt].v[j][0];
+          hi4[j] = (uint32_t)vp[tt].v[j][1];
         }
-        transpose4x4_bytes(lo4, &vt[tt][0]);
-        transpose4x4_bytes(hi4, &vt[tt][4]);
+        transpose4x4_bytes(lo4, &vtr[tt][0]);
+        transpose4x4_bytes(hi4, &vtr[tt][4]);
       }
-      // ---- PV: acc[m][j'] accumulates O^T[d = 32 r' + 8 j' + m][column n']
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(rs0, vp[0]);
+      load_v(rs1, vp[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- PV: acc[m][j'] holds O^T[d = 32 r' + 8 j' + m][column n']
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const long vop = (long)vt[0][m] | ((long)vt[1][m] << 32);
+        const long vop = (long)vtr[0][m] | ((long)vtr[1][m] << 32);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop, acc[m], 0, 0, 0);
       }
     }
-  }
 
-  // ---- epilogue: add lo columns into hi columns, normalise, store bf16 partials
-  float l_tot = l_run + xor_lane(l_run, 16);
-  l_tot += xor_lane(l_tot, 32);
-  const float inv = v_scale / (256.f * (l_tot > 0.f ? l_tot : 1.f));
-  float o[8][4];
+    // ---- partition epilogue: add lo columns into hi columns, normalise, store
+    if (a.run_len > 0 || k + 1 == n_tg) {
+      const int part = a.run_len > 0 ? tg : first_tg;
+      const float l_tot = sum_across_rows(l_run);
+      const float inv = v_scale / (l_tot > 0.f ? l_tot : 1.f);
+      // every lane joins the DPP exchange (lanes of the lo columns feed the hi columns);
+      // accumulators are combined, packed and stored one output row segment at a time
+      const int64_t row = (((int64_t)b * a.Hk + h) * a.P + part) * a.QG + n;
+      uint16_t* dst = a.part_o + row * kD + 32 * r;
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
+      for (int j = 0; j < 4; ++j) {
+        i32x4 w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[m][j] = (acc[m][j] + row_ror8(acc[m][j])) * inv;
-  if (n < a.QG) {
-    const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + n;
-    uint16_t* dst = a.part_o + row * kD + 32 * r;
+        for (int e = 0; e < 4; ++e) {
+          const float o0 = (acc[2 * e][j] + row_ror8(acc[2 * e][j])) * inv;
+          const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
+          w[e] = (int)pack_bf16x2(o0, o1);
+        }
+        if (n < a.QG) *reinterpret_cast<i32x4*>(dst + 8 * j) = w;
+      }
+      if (n < a.QG && r == 0) {  // statistics relative to the true maximum
+        a.part_m[row] = m_true * kLn2;
+        a.part_l[row] = l_tot * fast_exp2(m_run - m_true - 8.f);
+      }
+      m_run = -INFINITY;
+      m_true = -INFINITY;
+      l_run = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      i32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (int)pack_bf16x2(o[2 * e][j], o[2 * e + 1][j]);
-      *reinterpret_cast<i32x4*>(dst + 8 * j) = w;
-    }
-    if (r == 0) {
-      a.part_m[row] = m_run * kLn2;
-      a.part_l[row] = l_tot;
+      for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -284,9 +347,9 @@ __global__ __launch_bounds__(64 * W) void decode_fp8_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t stream) {
-  constexpr int W = 4;
-  const int64_t units = (int64_t)a.P * a.B * a.Hk;
-  const dim3 grid((unsigned)((units + W - 1) / W));
+  constexpr int W = 2;
+  const int64_t items = (int64_t)a.runs * a.B * a.Hk;
+  const dim3 grid((unsigned)((items + W - 1) / W));
   if (q_is_f32)
     hipLaunchKernelGGL((decode_fp8_kernel<float, W>), grid, dim3(64 * W), 0, stream, a);
   else

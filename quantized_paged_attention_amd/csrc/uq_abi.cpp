@@ -123,6 +123,21 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
   a.TGPP = ntg == 0 ? 1 : (ntg + num_partitions - 1) / num_partitions;
   a.max_seq_len = max_seq_len;
   a.block_size = block_size;
+  // Work items: with one tile-group per partition a wave streams a run of consecutive
+  // partitions of one (sequence, kv head), so the per-item start-up chain (length ->
+  // block table -> first KV loads) is paid once per run; runs are sized to leave about
+  // three waves of work per SIMD slot of the chip.
+  if (a.TGPP == 1) {
+    const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
+    const int64_t work = (int64_t)num_seqs * num_kv_heads * pmax;
+    int64_t rl = work / (256 * 8 * 3);
+    rl = rl < 1 ? 1 : (rl > 8 ? 8 : rl);
+    a.run_len = (int)rl;
+    a.runs = (pmax + a.run_len - 1) / a.run_len;
+  } else {
+    a.run_len = 0;
+    a.runs = num_partitions;
+  }
   a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.part_o = static_cast<uint16_t*>(part_out);
   a.part_m = part_max;

@@ -23,6 +23,24 @@ __device__ __forceinline__ uint32_t f_bits(float f) { return __builtin_bit_cast(
 // Lane exchange across 16-lane rows / 32-lane halves (ds_bpermute based).
 __device__ __forceinline__ float xor_lane(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Reductions across the four 16-lane rows of a wave with the gfx950 lane-swap
+// instructions (VALU, no LDS round trip): permlane16_swap(x, x) returns the values of the
+// even and of the odd row of each row pair, permlane32_swap(x, x) those of the lower and
+// the upper half, so combining the two halves of each result reduces over lanes
+// l, l ^ 16, l ^ 32, l ^ 48.
+__device__ __forceinline__ float max_across_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  x = fmaxf(bits_f(a[0]), bits_f(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return fmaxf(bits_f(b[0]), bits_f(b[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  x = bits_f(a[0]) + bits_f(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return bits_f(b[0]) + bits_f(b[1]);
+}
+
 // Exchange with the lane n ^ 8 of the same 16-lane row (DPP row rotate by 8).
 __device__ __forceinline__ float row_ror8(float v) {
   return bits_f((uint32_t)__builtin_amdgcn_mov_dpp((int)f_bits(v), 0x128, 0xF, 0xF, false));

@@ -22,6 +22,8 @@ struct DecodeArgs {
   int32_t bt_stride;
   const int32_t* seq_lens;
   int32_t B, Hk, QG, P, TGPP, max_seq_len, block_size;
+  int32_t runs;     // work items per (sequence, kv head)
+  int32_t run_len;  // partitions per work item when each partition is one tile-group, else 0
   float softmax_scale;
   uint16_t* part_o;            // bf16 [B, Hk, P, QG, D]
   float* part_m;               // [B, Hk, P, QG]

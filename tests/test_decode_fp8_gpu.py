@@ -191,3 +191,15 @@ def test_high_config_sampled():
     sub.seq_lens = case.seq_lens[pick]
     ref = oracle_decode(sub)
     assert_decode_close(got[pick], ref, "fp8_high sample")
+
+
+def test_partition_runs_ragged_batch():
+    """A batch large enough that each wave streams a run of several partitions
+    (B=64, Hk=8, P=32): ragged lengths put the last token at every position of a run."""
+    need_gpu()
+    rng = np.random.default_rng(57)
+    lens = rng.integers(1, 8193, size=64)
+    lens[:6] = [1, 255, 256, 257, 8192, 4097]
+    case = small(lens=tuple(int(x) for x in lens), hk=8, qg=8, seed=57)
+    got, _ = run_decode(case, P=32)
+    assert_decode_close(got, oracle_decode(case), "runs ragged")
