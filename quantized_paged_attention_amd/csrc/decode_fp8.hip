@@ -40,11 +40,13 @@ struct KTile {
   i32x4 a, b;  // K bytes [16r, 16r+16) and [64+16r, 64+16r+16) of token n
 };
 struct VTile {
-  i32x2 v[4];  // V bytes [8n, 8n+8) of tokens 4r + j
+  i32x4 a, b;  // V bytes [16 (n/2), +16) of tokens 4r + 2 (n&1) and 4r + 2 (n&1) + 1
 };
 
 template <typename QT, int W>
 __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
+  // per-wave staging of one partition's bf16 output rows (QG <= 8 rows of 256 bytes)
+  __shared__ __attribute__((aligned(16))) uint16_t o_stage[W][8 * kD];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t item = (int64_t)blockIdx.x * W + wave;
@@ -147,7 +149,14 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 
   const uint32_t pos = (uint32_t)a.pos_stride;
   const uint32_t k_off = n * pos + 16 * r;
-  const uint32_t v_off = 4 * r * pos + kD + 8 * n;
+  // V: lane pair (2h, 2h+1) fetches dims [16h, 16h+16) of tokens 4r..4r+3 with two
+  // 16-byte loads per lane (the even lane tokens 4r, 4r+1, the odd lane 4r+2, 4r+3) and
+  // the pair swaps halves, so each lane ends with dims [8n, 8n+8) of all four tokens.
+  const int par = n & 1;
+  const uint32_t v_off = (4 * r + 2 * par) * pos + kD + 16 * (n >> 1);
+  // transpose selectors: the odd lane holds its four tokens in the order 2, 3, 0, 1
+  const uint32_t sel_a = par ? 0x01000504u : 0x05040100u;
+  const uint32_t sel_b = par ? 0x03020706u : 0x07060302u;
   const uint8_t* head_base = a.cache + (int64_t)h * a.slot_bytes;
   const int32_t* bt_row = a.bt + (int64_t)b * a.bt_stride;
   const int bs_shift = 31 - __builtin_clz(a.block_size);
@@ -199,9 +208,9 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
     d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 64, 0, kAuxNT);
   };
   auto load_v = [&](__amdgpu_buffer_rsrc_t rs, VTile& d) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)  // token offset j * pos rides in the scalar offset
-      d.v[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, v_off, j * (int)pos, kAuxNT);
+    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kAuxNT);
+    // the second token's offset rides in the scalar offset
+    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, (int)pos, kAuxNT);
   };
 
   // The stream walks tile pairs (32 tokens).  The K loads of pair i + 1 are issued as
@@ -230,6 +239,9 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       const int pf_k = pr + 1 < kTiles / 2 ? k : k + 1;  // the next pair
       const int pf_t0 = pr + 1 < kTiles / 2 ? 2 * (pr + 1) : 0;
       if (pr == kTiles / 2 - 1 && (k & 7) == 7 && k + 1 < n_tg) load_window(k + 1);  // rare
+      // the pair boundary is a scheduling fence: the next pair's QK (and its wait for
+      // K loads issued one pair earlier) must not be hoisted above this pair's PV work
+      __builtin_amdgcn_sched_barrier(0);
       // ---- QK: S^T[token][column] of both tiles, hi + lo columns added by DPP
       float s[2][4];
 #pragma unroll
@@ -286,18 +298,22 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       }
       const long pop = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
 
-      // ---- V^T: byte transpose of 8 dims x 4 tokens per tile
+      // ---- V^T: exchange halves with the neighbouring lane, then byte-transpose 8 dims
+      //      x 4 tokens per tile
       uint32_t vtr[2][8];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        uint32_t lo4[4], hi4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          lo4[j] = (uint32_t)vp[tt].v[j][0];
-          hi4[j] = (uint32_t)vp[tt].v[j][1];
-        }
-        transpose4x4_bytes(lo4, &vtr[tt][0]);
-        transpose4x4_bytes(hi4, &vtr[tt][4]);
+        const i32x4 va = vp[tt].a, vb = vp[tt].b;
+        // keep: this lane's 8 dims of its own two tokens; send: the neighbour's 8 dims
+        const uint32_t k0x = par ? va[2] : va[0], k0y = par ? va[3] : va[1];
+        const uint32_t k1x = par ? vb[2] : vb[0], k1y = par ? vb[3] : vb[1];
+        const uint32_t r0x = swap_adjacent(par ? va[0] : va[2]);
+        const uint32_t r0y = swap_adjacent(par ? va[1] : va[3]);
+        const uint32_t r1x = swap_adjacent(par ? vb[0] : vb[2]);
+        const uint32_t r1y = swap_adjacent(par ? vb[1] : vb[3]);
+        const uint32_t lo4[4] = {k0x, k1x, r0x, r1x}, hi4[4] = {k0y, k1y, r0y, r1y};
+        transpose4x4_bytes_sel(lo4, &vtr[tt][0], sel_a, sel_b);
+        transpose4x4_bytes_sel(hi4, &vtr[tt][4], sel_a, sel_b);
       }
       __builtin_amdgcn_sched_barrier(0);
       load_v(rs0, vp[0]);
@@ -316,10 +332,12 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       const int part = a.run_len > 0 ? tg : first_tg;
       const float l_tot = sum_across_rows(l_run);
       const float inv = v_scale / (l_tot > 0.f ? l_tot : 1.f);
-      // every lane joins the DPP exchange (lanes of the lo columns feed the hi columns);
-      // accumulators are combined, packed and stored one output row segment at a time
-      const int64_t row = (((int64_t)b * a.Hk + h) * a.P + part) * a.QG + n;
-      uint16_t* dst = a.part_o + row * kD + 32 * r;
+      // Every lane joins the DPP exchange (lanes of the lo columns feed the hi columns).
+      // The bf16 rows go through LDS so that the partial is written with whole-line
+      // stores: written from registers directly it would be 16-byte pieces at 64-byte
+      // stride, and such scattered partial-line writes slow the concurrent KV stream.
+      const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part) * a.QG;
+      uint16_t* stage = o_stage[threadIdx.x >> 6];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         i32x4 w;
@@ -329,8 +347,24 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
           const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
           w[e] = (int)pack_bf16x2(o0, o1);
         }
-        if (n < a.QG) *reinterpret_cast<i32x4*>(dst + 8 * j) = w;
+        if (n < a.QG) *reinterpret_cast<i32x4*>(stage + n * kD + 32 * r + 8 * j) = w;
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      {
+        const int nbytes = a.QG * kD * 2;  // contiguous partial rows of this unit
+        uint16_t* out = a.part_o + row0 * kD;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int byte = c * 1024 + 16 * lane;
+          if (byte < nbytes)
+            *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
+                *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) + byte);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the stage is reused
+      __builtin_amdgcn_wave_barrier();
+      const int64_t row = row0 + n;
       if (n < a.QG && r == 0) {  // statistics relative to the true maximum
         a.part_m[row] = m_true * kLn2;
         a.part_l[row] = l_tot * fast_exp2(m_run - m_true - 8.f);

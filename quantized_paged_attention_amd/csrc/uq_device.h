@@ -84,6 +84,25 @@ __device__ __forceinline__ void transpose4x4_bytes(const uint32_t in[4], uint32_
   out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
+// Same transpose with per-lane second-stage selectors: (0x05040100, 0x07060302) gives
+// tokens in input order 0,1,2,3; (0x01000504, 0x03020706) gives input order 2,3,0,1.
+__device__ __forceinline__ void transpose4x4_bytes_sel(const uint32_t in[4], uint32_t out[4],
+                                                       uint32_t sel_a, uint32_t sel_b) {
+  const uint32_t t0 = __builtin_amdgcn_perm(in[1], in[0], 0x06020400u);
+  const uint32_t t1 = __builtin_amdgcn_perm(in[1], in[0], 0x07030501u);
+  const uint32_t t2 = __builtin_amdgcn_perm(in[3], in[2], 0x06020400u);
+  const uint32_t t3 = __builtin_amdgcn_perm(in[3], in[2], 0x07030501u);
+  out[0] = __builtin_amdgcn_perm(t2, t0, sel_a);
+  out[2] = __builtin_amdgcn_perm(t2, t0, sel_b);
+  out[1] = __builtin_amdgcn_perm(t3, t1, sel_a);
+  out[3] = __builtin_amdgcn_perm(t3, t1, sel_b);
+}
+
+// Swap a value with the neighbouring lane (lane 2k <-> 2k+1; DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ int swap_adjacent(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+}
+
 template <typename T>
 __device__ __forceinline__ T nt_load(const T* p) {
   return __builtin_nontemporal_load(p);

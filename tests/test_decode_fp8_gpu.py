@@ -194,12 +194,13 @@ def test_high_config_sampled():
 
 
 def test_partition_runs_ragged_batch():
-    """A batch large enough that each wave streams a run of several partitions
-    (B=64, Hk=8, P=32): ragged lengths put the last token at every position of a run."""
+    """A batch large enough that each wave streams a run of two partitions (B=128, Hk=8,
+    P=32, i.e. 32768 (sequence, head, partition) items): ragged lengths end a sequence in
+    the first or the second partition of a run, on and off tile-group edges."""
     need_gpu()
     rng = np.random.default_rng(57)
-    lens = rng.integers(1, 8193, size=64)
-    lens[:6] = [1, 255, 256, 257, 8192, 4097]
+    lens = rng.integers(1, 8193, size=128)
+    lens[:8] = [1, 255, 256, 257, 511, 512, 8192, 4097]
     case = small(lens=tuple(int(x) for x in lens), hk=8, qg=8, seed=57)
     got, _ = run_decode(case, P=32)
     assert_decode_close(got, oracle_decode(case), "runs ragged")
