@@ -25,12 +25,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs/decode step + KV-stream GB/s (% of HBM peak) at B=128 ctx=16k"
-DECODE_SRC = os.path.join(ROOT, "quantized_paged_attention_amd", "csrc", "decode_fp8.hip")
+CSRC = os.path.join(ROOT, "quantized_paged_attention_amd", "csrc")
+# Sources that decide the decode kernel's code and launch shape.
+DECODE_SRCS = ("decode_fp8.hip", "uq_device.h", "uq_kernels.h", "uq_abi.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fp8_high_traffic.json")
 
 
-def source_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SRCS:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(units_per_launch: float):
@@ -39,28 +44,34 @@ def measured_traffic(units_per_launch: float):
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("kernel_source_sha256_16") != source_hash(DECODE_SRC):
+    if rec.get("kernel_source_sha256_16") != source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, n_seqs: int):
-    """fp64 oracle on the first n_seqs sequences (all kv heads) of the workload."""
+def cpu_baseline(case, n_seqs: int, min_seconds: float = 10.0):
+    """fp64 oracle on the first n_seqs sequences (all kv heads) of the workload, repeated
+    until at least min_seconds of wall time have been spent (at most 8 passes)."""
     from oracle import oracle
     sub = copy.copy(case)
     sub.q = case.q[:n_seqs]
     sub.block_table = case.block_table[:n_seqs]
     sub.seq_lens = case.seq_lens[:n_seqs]
-    t0 = time.perf_counter()
-    oracle.decode(sub.q, sub.cache, sub.block_table, sub.seq_lens,
-                  num_kv_heads=sub.num_kv_heads, kv_format=sub.kv_format,
-                  softmax_scale=sub.softmax_scale, k_scale=sub.k_scale, v_scale=sub.v_scale)
+    passes, t0 = 0, time.perf_counter()
+    while passes < 8 and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.decode(sub.q, sub.cache, sub.block_table, sub.seq_lens,
+                      num_kv_heads=sub.num_kv_heads, kv_format=sub.kv_format,
+                      softmax_scale=sub.softmax_scale, k_scale=sub.k_scale,
+                      v_scale=sub.v_scale)
+        passes += 1
+        print(f"cpu baseline: oracle pass {passes} done", file=sys.stderr, flush=True)
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count()
-    return {"value": round(sub.kv_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+    threads = oracle.num_threads()
+    return {"value": round(passes * sub.kv_bytes() / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
             "sample": f"first {n_seqs} of {case.B} sequences, all {case.num_kv_heads} kv heads "
-                      f"({sub.kv_bytes() / 1e6:.1f} MB of KV), fp64, {dt:.2f} s wall"}
+                      f"({sub.kv_bytes() / 1e6:.1f} MB of KV) x {passes} passes, fp64, "
+                      f"{dt:.2f} s wall"}
 
 
 def main():
@@ -68,9 +79,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-seqs", type=int, default=64,
+    ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of the workload the CPU oracle baseline runs")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 launches), "
+                         "the known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build measures one GPU only (the decode path needs no "
@@ -81,6 +95,18 @@ def main():
     import torch
 
     from quantized_paged_attention_amd import synth, uq
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}),
+              flush=True)
+        return
 
     uq.load_library()
     dev = "cuda"

@@ -54,6 +54,8 @@ def _load():
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.uqo_num_threads.restype = ctypes.c_int
+        lib.uqo_num_threads.argtypes = []
         lib.uqo_e4m3.restype = f64
         lib.uqo_e4m3.argtypes = [ctypes.c_uint32]
         lib.uqo_e2m1.restype = f64
@@ -85,6 +87,11 @@ def _c(a, dtype):
 
 
 # ------------------------------------------------------------------ codecs
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().uqo_num_threads())
 
 
 def e4m3(code: int) -> float:

@@ -33,6 +33,18 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops below run on (1 when built without OpenMP). */
+int uqo_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 #define UQO_FMT_FP8_E4M3 0       /* slot: K e4m3[D] | V e4m3[D]                          */
 #define UQO_FMT_FP4_E4M3S 1      /* slot: Kc[D/2] | Ks[D/32] | Vc[D/2] | Vs[D/32], e4m3 s */
