@@ -78,7 +78,7 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  *   k_scale,      device float[1] per-tensor scales (fp8 format only), or NULL for 1.0
  *   v_scale       ([P3] scales as 1-element device tensors).  Must be NULL for fp4.
  *   rot_signs     device int8[head_dim] of +-1 for the query rotation, or NULL.
- *                 fp4 formats only.
+ *                 fp4 formats only; 16-byte aligned.
  *   block_table   [num_seqs, bt_stride] int32 physical block ids.
  *   seq_lens      [num_seqs] int32 context lengths.
  *   max_seq_len   host-side upper bound of seq_lens (>= 0); fixes the tile-groups per
@@ -92,7 +92,7 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  * Only partitions that own at least one token (p < ceil(L_b / 256)) are written; the
  * others keep their contents and are never read by uq_paged_reduce.
  * Supported: (UQ_KV_FP8_E4M3, D = 128, QG <= 8) and (UQ_KV_FP4_E2M1_E4M3S, D = 256,
- * QG in {6, 8, 16}); anything else returns UQ_ERR_UNSUPPORTED.
+ * QG <= 16); anything else returns UQ_ERR_UNSUPPORTED.
  * Device preconditions: 0 <= seq_lens[b] <= max_seq_len (larger values are clamped to
  * max_seq_len); block_table[b][t / block_size] in [0, num_blocks) for every t < L_b;
  * entries past a sequence's last block are never read; slot bytes of tokens t >= L_b are

@@ -1,5 +1,409 @@
-// decode_fp4.hip -- placeholder until the FP4 D=256 kernel lands.
+// decode_fp4.hip -- paged decode over an fp4 e2m1 cache with e4m3 scales per 32 head
+// dims, D = 256, query groups of up to 16 heads, with the query rotated in-kernel into
+// the cache's randomized-Hadamard key domain.  gfx950.
+//
+// What is computed (vLLM "ultraquant_decode_hd256" page: AoS slot of K codes, K scales,
+// V codes, V scales; strided partition -> 256-token tile-group map; fused Walsh-Hadamard
+// query rotation of STEP B'; online softmax of STEP F; partition epilogue of STEP G):
+// for a unit (sequence b, kv head h, partition p) the softmax statistics of the tokens of
+// tile-groups p, p+P, ...:  m = max s, l = sum exp(s - m), o = sum exp(s - m) v / l, with
+// s = softmax_scale * (q R) . k, R = diag(signs) H / 16 (H the natural-order Sylvester
+// Hadamard matrix), k and v decoded as e2m1(code) * e4m3(scale of its 32-dim group).
+//
+// Design (one workgroup of four waves per unit):
+//   * Every product e2m1 * e4m3 is exact in f16 (at most 6 significant bits, magnitudes
+//     in [2^-10, 2688]), so K and V are dequantised exactly with one v_cvt_scalef32_pk_
+//     f16_fp4 (its scale operand applies only a power of two, so it is left at 1) and one
+//     packed f16 multiply per byte, and QK / PV run on v_mfma_f32_16x16x32_f16.
+//   * The rotated query is computed once per workgroup: wave w transforms heads 4w..4w+3
+//     (lane = 16 consecutive dims of a head: four butterfly stages in registers, four
+//     across lanes), scales each row by a power of two that puts its largest magnitude in
+//     [2^14, 2^15) (full f16 precision, no overflow), and leaves it in LDS in f16.
+//   * Wave w streams tokens [64w, 64w + 64) of each of the unit's tile-groups, 32 tokens
+//     per step.  QK: A = K (lane = token, 64 consecutive head dims per lane, dims permuted
+//     identically in the query operand), B = query (lane = head).  Softmax is online in
+//     exp2 units with a reference that is only moved when a score exceeds it (ballot).
+//     PV: A = P straight from the QK output layout, B = V with lane = 16 consecutive head
+//     dims of 8 tokens; a nibble transpose (v_bfi) pairs the two tokens of each f16x2 so
+//     that every B register is one convert and one multiply by the tokens' scale pair.
+//   * The four waves' (m, l, acc) are merged in LDS; the normalised rows are written as
+//     bf16 with whole-row stores.
+#include "uq_device.h"
 #include "uq_kernels.h"
+
 namespace uq {
-hipError_t launch_decode_fp4(const DecodeArgs&, bool, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 256;
+constexpr int kW = 4;          // waves per workgroup, 64 tokens of a tile-group each
+constexpr int kKScales = 128;  // slot offsets: K codes 0, K scales 128, V codes 136,
+constexpr int kVCodes = 136;   // V scales 264 (one e4m3 byte per 32 head dims)
+constexpr int kVScales = 264;
+
+template <int sel>
+__device__ __forceinline__ f16x2 fp4_pair(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, sel);
+}
+
+__device__ __forceinline__ f16x2 splat_h(float s) {
+  const _Float16 h = (_Float16)s;
+  return f16x2{h, h};
+}
+
+__device__ __forceinline__ f16x8 cat4(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// e4m3 byte `byte_idx` (0..3, runtime) of a word -> float
+__device__ __forceinline__ float e4m3_byte(uint32_t word, int byte_idx) {
+  return e4m3_to_f<0>((int)(word >> (8 * byte_idx)));
+}
+
+// Address of the slot of token t (0 <= t < L) of kv head h: the block id comes from
+// lane `(t / bs) - blk_lo` of `ids` (the wave's preloaded block ids).
+__device__ __forceinline__ const uint8_t* slot_ptr(const DecodeArgs& a, int ids, int blk_lo,
+                                                   int t, int h) {
+  const int blk = t / a.block_size;
+  const int phys = __shfl(ids, blk - blk_lo, 64);
+  return a.cache + (int64_t)phys * a.blk_stride + (int64_t)(t - blk * a.block_size) * a.pos_stride +
+         (int64_t)h * a.slot_bytes;
+}
+
+template <typename QT>
+__global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
+  // Rotated query (f16, row stride kD + 8 halves) during the stream; the four waves'
+  // scaled accumulators in the merge (reused after a barrier).
+  __shared__ __attribute__((aligned(16))) float lds_acc[kW][16][kD];
+  __shared__ float lds_fac[16];
+  __shared__ float lds_m[kW][16];
+  __shared__ float lds_l[kW][16];
+  _Float16* lds_q = reinterpret_cast<_Float16*>(&lds_acc[0][0][0]);
+  constexpr int kQStride = kD + 8;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int unit = blockIdx.x;
+  const int p = unit % a.P;
+  const int h = (unit / a.P) % a.Hk;
+  const int b = unit / (a.P * a.Hk);
+
+  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int ntg = (L + kTileGroup - 1) / kTileGroup;
+  if (p >= ntg) return;  // empty partition (uniform over the workgroup): nothing written
+  int n_tg = (ntg - p + a.P - 1) / a.P;
+  n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+
+  // ---- rotated query: wave w, lane (row 4w + lane/16, dims 16 c .. 16 c + 15)
+  {
+    const int row = 4 * wave + (lane >> 4);
+    const int c = lane & 15;
+    float x[16];
+    if (row < a.QG) {
+      const QT* src = reinterpret_cast<const QT*>(a.q) + (int64_t)b * a.q_ss +
+                      (int64_t)(h * a.QG + row) * a.q_sh + 16 * c;
+      if constexpr (sizeof(QT) == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * k);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * k + e] = v[e];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const i32x4 v = *reinterpret_cast<const i32x4*>(src + 8 * k);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[8 * k + 2 * e] = bf16_to_f((uint32_t)v[e] & 0xFFFFu);
+            x[8 * k + 2 * e + 1] = bf16_to_f((uint32_t)v[e] >> 16);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = 0.f;
+    }
+    if (a.rot_signs) {
+      const i32x4 sg = *reinterpret_cast<const i32x4*>(a.rot_signs + 16 * c);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int s8 = (int)(int8_t)((uint32_t)sg[e >> 2] >> (8 * (e & 3)));
+        x[e] = s8 < 0 ? -x[e] : x[e];
+      }
+      // butterflies of stride 1, 2, 4, 8: inside the lane
+#pragma unroll
+      for (int st = 1; st < 16; st <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          if ((e & st) == 0) {
+            const float u = x[e], v = x[e + st];
+            x[e] = u + v;
+            x[e + st] = u - v;
+          }
+        }
+      }
+      // strides 16, 32, 64, 128: partner lane c ^ 1, 2, 4, 8 of the same 16-lane row
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const bool upper = (c & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float o = __shfl_xor(x[e], m, 64);
+          x[e] = upper ? o - x[e] : x[e] + o;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] *= 0.0625f;  // 1 / sqrt(256)
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    // 2^sh puts amax in [2^14, 2^15)
+    int sh = 0;
+    if (amax > 0.f) {
+      const int E = (int)((f_bits(amax) >> 23) & 0xFF) - 127;  // amax in [2^E, 2^(E+1))
+      sh = 14 - (E < -126 ? -126 : E);
+      sh = sh > 126 ? 126 : sh;
+    }
+    const float up = __builtin_ldexpf(1.f, sh);
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f16x2 hv = f16x2{(_Float16)(x[2 * e] * up), (_Float16)(x[2 * e + 1] * up)};
+      w[e] = __builtin_bit_cast(uint32_t, hv);
+    }
+    uint8_t* dst = reinterpret_cast<uint8_t*>(lds_q + row * kQStride + 16 * c);
+    *reinterpret_cast<i32x4*>(dst) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    *reinterpret_cast<i32x4*>(dst + 16) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    if (c == 0) lds_fac[row] = a.softmax_scale * kLog2e * __builtin_ldexpf(1.f, -sh);
+  }
+  __syncthreads();
+
+  const int n = lane & 15;   // query head of the QK / softmax layout; PV column group
+  const int q = lane >> 4;   // lane row group
+  // B operand of QK: head n, dims 64 q + 8 kk .. + 8 for kk = 0..7
+  f16x8 qb[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    qb[kk] = *reinterpret_cast<const f16x8*>(lds_q + n * kQStride + 64 * q + 8 * kk);
+  const float fac = lds_fac[n];
+
+  float m_run = -INFINITY;  // reference of head n (exp2 units); acc/l are relative to it
+  float l_run = 0.f;        // this lane's share of sum p for head n
+  f32x4 acc[16];            // acc[mm][jj] = O[head 4q + jj][dim 16 n + mm]
+#pragma unroll
+  for (int mm = 0; mm < 16; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int blk_per_wave = 64 / a.block_size > 0 ? 64 / a.block_size : 1;
+  for (int k = 0; k < n_tg; ++k) {
+    const int start = (p + k * a.P) * kTileGroup + 64 * wave;
+    const int nvis = L - start;
+    if (nvis <= 0) continue;  // no tokens of this wave in this tile-group
+    // block ids of the wave's 64 tokens (lane i < blocks: block blk_lo + i), clamped to
+    // the last visible block so that no table entry past the sequence is dereferenced
+    const int blk_lo = start / a.block_size;
+    const int blk_last = (L - 1) / a.block_size;
+    int bi = blk_lo + (lane < blk_per_wave ? lane : 0);
+    bi = bi > blk_last ? blk_last : bi;
+    const int ids = a.bt[(int64_t)b * a.bt_stride + bi];
+    const int nchunk = nvis >= 64 ? 2 : (nvis + 31) / 32;
+
+    for (int ck = 0; ck < nchunk; ++ck) {
+      const int t0 = start + 32 * ck;
+      // ---- loads: K of two 16-token tiles (lane = token n, bytes 32 q .. 32 q + 31 and
+      //      the scale word holding groups 2q, 2q + 1), V of 8 tokens (lane = dims 16 n ..)
+      i32x4 kc[2][2];
+      uint32_t ksw[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        int t = t0 + 16 * T + n;
+        t = t < L ? t : L - 1;
+        const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
+        kc[T][0] = *reinterpret_cast<const i32x4*>(sp + 32 * q);
+        kc[T][1] = *reinterpret_cast<const i32x4*>(sp + 32 * q + 16);
+        ksw[T] = *reinterpret_cast<const uint32_t*>(sp + kKScales + 4 * (q >> 1));
+      }
+      i32x2 vc[8];
+      uint32_t vsw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int t = t0 + (e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4));
+        t = t < L ? t : L - 1;
+        const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
+        vc[e] = *reinterpret_cast<const i32x2*>(sp + kVCodes + 8 * n);
+        vsw[e] = *reinterpret_cast<const uint32_t*>(sp + kVScales + 4 * (n >> 3));
+      }
+
+      // ---- QK: s[T][jj] = score of token t0 + 16 T + 4 q + jj, head n
+      f32x4 s[2];
+#pragma unroll
+      for (int T = 0; T < 2; ++T) {
+        const f16x2 s0 = splat_h(e4m3_byte(ksw[T], 2 * (q & 1)));
+        const f16x2 s1 = splat_h(e4m3_byte(ksw[T], 2 * (q & 1) + 1));
+        f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const uint32_t wd = (uint32_t)kc[T][kk >> 2][kk & 3];
+          const f16x2 sc = kk < 4 ? s0 : s1;
+          const f16x8 A = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc,
+                               fp4_pair<2>(wd) * sc, fp4_pair<3>(wd) * sc);
+          c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[kk], c4, 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int t = t0 + 16 * T + 4 * q + jj;
+          c4[jj] = t < L ? c4[jj] * fac : -INFINITY;
+        }
+        s[T] = c4;
+      }
+
+      // ---- online softmax (reference moves only when a score exceeds it)
+      float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      if (__builtin_amdgcn_ballot_w64(mloc > m_run)) {
+        const float m_new = fmaxf(m_run, max_across_rows(mloc));
+        const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run = -inf
+        l_run *= alpha;
+        m_run = m_new;
+        // accumulator rows are heads 4q + jj: their factors live in lanes 4q + jj
+        float al[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) al[jj] = __shfl(alpha, 4 * q + jj, 64);
+#pragma unroll
+        for (int mm = 0; mm < 16; ++mm)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) acc[mm][jj] *= al[jj];
+      }
+      float pv[8];
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pv[4 * T + jj] = fast_exp2(s[T][jj] - m_run);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l_run += pv[e];
+      // A operand of PV: head n, k-slot 8q + e <-> token t0 + (e < 4 ? 4q + e : 16 + 4q + e - 4)
+      const f16x8 pa = f16x8{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3],
+                             (_Float16)pv[4], (_Float16)pv[5], (_Float16)pv[6], (_Float16)pv[7]};
+
+      // ---- PV.  Token pair u = (2u, 2u+1); X / Y hold per byte the even / odd dim of the
+      //      byte's position for both tokens (low nibble: token 2u).
+      f16x2 vs[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sb = (n >> 1) & 3;
+        vs[u] = f16x2{(_Float16)e4m3_byte(vsw[2 * u], sb), (_Float16)e4m3_byte(vsw[2 * u + 1], sb)};
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t X[4], Y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t wa = (uint32_t)vc[2 * u][hh], wb = (uint32_t)vc[2 * u + 1][hh];
+          X[u] = (wa & 0x0F0F0F0Fu) | ((wb << 4) & 0xF0F0F0F0u);
+          Y[u] = ((wa >> 4) & 0x0F0F0F0Fu) | (wb & 0xF0F0F0F0u);
+        }
+#define UQ_PV_BYTE(KB)                                                                         \
+  {                                                                                            \
+    const f16x8 bx = cat4(fp4_pair<KB>(X[0]) * vs[0], fp4_pair<KB>(X[1]) * vs[1],              \
+                          fp4_pair<KB>(X[2]) * vs[2], fp4_pair<KB>(X[3]) * vs[3]);             \
+    acc[8 * hh + 2 * KB] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bx, acc[8 * hh + 2 * KB], \
+                                                                  0, 0, 0);                    \
+    const f16x8 by = cat4(fp4_pair<KB>(Y[0]) * vs[0], fp4_pair<KB>(Y[1]) * vs[1],              \
+                          fp4_pair<KB>(Y[2]) * vs[2], fp4_pair<KB>(Y[3]) * vs[3]);             \
+    acc[8 * hh + 2 * KB + 1] =                                                                 \
+        __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, by, acc[8 * hh + 2 * KB + 1], 0, 0, 0);      \
+  }
+        UQ_PV_BYTE(0)
+        UQ_PV_BYTE(1)
+        UQ_PV_BYTE(2)
+        UQ_PV_BYTE(3)
+#undef UQ_PV_BYTE
+      }
+    }
+  }
+
+  // ---- merge the four waves: (m, l) per head, then the scaled accumulators
+  const float l_tot = sum_across_rows(l_run);
+  __syncthreads();  // every wave is done with the rotated query in lds_acc
+  if (q == 0) {
+    lds_m[wave][n] = m_run;
+    lds_l[wave][n] = l_tot;
+  }
+  __syncthreads();
+  {
+    float fself[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int hd = 4 * q + jj;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) M = fmaxf(M, lds_m[w][hd]);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const float mw = lds_m[w][hd];
+        lsum += mw == -INFINITY ? 0.f : lds_l[w][hd] * fast_exp2(mw - M);
+      }
+      const float ms = lds_m[wave][hd];
+      fself[jj] = (ms == -INFINITY || !(lsum > 0.f)) ? 0.f : fast_exp2(ms - M) / lsum;
+      if (wave == 0 && n == 0 && hd < a.QG) {
+        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + hd;
+        a.part_m[row] = M * kLn2;
+        a.part_l[row] = lsum;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float* dst = &lds_acc[wave][4 * q + jj][16 * n];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4)
+        *reinterpret_cast<f32x4*>(dst + 4 * k4) =
+            f32x4{acc[4 * k4][jj], acc[4 * k4 + 1][jj], acc[4 * k4 + 2][jj], acc[4 * k4 + 3][jj]} *
+            fself[jj];
+    }
+  }
+  __syncthreads();
+  {
+    const int row = 4 * wave + (lane >> 4);
+    const int c = lane & 15;
+    if (row < a.QG) {
+      f32x4 o[4];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        o[k4] = *reinterpret_cast<const f32x4*>(&lds_acc[0][row][16 * c + 4 * k4]);
+#pragma unroll
+        for (int w = 1; w < kW; ++w)
+          o[k4] += *reinterpret_cast<const f32x4*>(&lds_acc[w][row][16 * c + 4 * k4]);
+      }
+      const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + row;
+      uint16_t* dst = a.part_o + prow * kD + 16 * c;
+      *reinterpret_cast<i32x4*>(dst) =
+          i32x4{(int)pack_bf16x2(o[0][0], o[0][1]), (int)pack_bf16x2(o[0][2], o[0][3]),
+                (int)pack_bf16x2(o[1][0], o[1][1]), (int)pack_bf16x2(o[1][2], o[1][3])};
+      *reinterpret_cast<i32x4*>(dst + 8) =
+          i32x4{(int)pack_bf16x2(o[2][0], o[2][1]), (int)pack_bf16x2(o[2][2], o[2][3]),
+                (int)pack_bf16x2(o[3][0], o[3][1]), (int)pack_bf16x2(o[3][2], o[3][3])};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, hipStream_t stream) {
+  const int64_t units = (int64_t)a.B * a.Hk * a.P;
+  if (units <= 0) return hipSuccess;
+  if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)units), block(64 * kW);
+  if (q_is_f32)
+    hipLaunchKernelGGL(decode_fp4_kernel<float>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_fp4_kernel<uint16_t>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace uq

@@ -156,9 +156,9 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
   }
   if (kv_format == UQ_KV_FP4_E2M1_E4M3S) {
     if (head_dim != 256) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports head_dim 256 only");
-    if (QG != 6 && QG != 8 && QG != 16)
-      return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports query groups 6, 8 and 16 (got %d)", QG);
     if (k_scale || v_scale) return fail(UQ_ERR_INVALID_ARG, "per-tensor scales apply to fp8 caches only");
+    if (reinterpret_cast<uintptr_t>(rot_signs) & 15)
+      return fail(UQ_ERR_INVALID_ARG, "rot_signs must be 16-byte aligned");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache needs slot_bytes a multiple of 16");
     if (num_seqs == 0) return ok();
     return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
