@@ -1,0 +1,110 @@
+"""GPU parity of the nvfp4 index scorer against the fp64 oracle: finite cells within
+1e-4 of max|ref|, -inf cells exactly, cells past each request's pages bit-identical to
+the NaN-payload pre-fill."""
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+from quantized_paged_attention_amd import synth
+from tests.gpu_util import DEV, TOL_INDEX, log, need_gpu, uq
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(case, q=None, pages=None):
+    q = q if q is not None else torch.from_numpy(case.q).to(DEV)
+    pages = pages if pages is not None else torch.from_numpy(case.pages).to(DEV)
+    bt = torch.from_numpy(case.block_table).to(DEV)
+    sl = torch.from_numpy(case.seq_lens).to(DEV)
+    scores = torch.from_numpy(case.scores_init().copy()).to(DEV)
+    uq.index_score(q, pages, bt, sl, scores, query_len=case.query_len)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy()
+
+
+def run_oracle(case):
+    from oracle import oracle
+    return oracle.index_score(case.q, case.pages, case.block_table, case.seq_lens,
+                              query_len=case.query_len, scores_init=case.scores_init())
+
+
+def assert_index_match(got, ref, init, what):
+    ref_bits = init.view(np.uint32)
+    untouched = np.isnan(ref)
+    # untouched cells: the pre-fill bit pattern, exactly
+    assert np.array_equal(got.view(np.uint32)[untouched], ref_bits[untouched]), f"{what}: untouched"
+    neg = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(got), neg), f"{what}: -inf cells"
+    fin = np.isfinite(ref)
+    assert np.isfinite(got[fin]).all(), f"{what}: non-finite where the oracle is finite"
+    scale = np.abs(ref[fin]).max() if fin.any() else 1.0
+    err = float(np.abs(got[fin].astype(np.float64) - ref[fin]).max() / scale) if fin.any() else 0.0
+    log(f"  {what}: max|err|/max|ref| = {err:.3e} over {int(fin.sum())} cells")
+    assert err <= TOL_INDEX, f"{what}: {err:.3e} > {TOL_INDEX}"
+
+
+@pytest.mark.parametrize("ql,h", synth.INDEX_COMBOS)
+def test_index_config(ql, h):
+    """32 requests, L ~ U[1024, 32768], D=128, every (query_len, heads) combination."""
+    need_gpu()
+    case = synth.nvfp4_index(ql, h)
+    log(f"case nvfp4_index ql={ql} h={h} page_bytes={case.page_bytes()}")
+    got = run_gpu(case)
+    assert_index_match(got, run_oracle(case), case.scores_init(), f"ql={ql} h={h}")
+
+
+@pytest.mark.parametrize("ql,h", [(1, 1), (4, 2), (8, 4), (2, 4)])
+def test_edge_lengths(ql, h):
+    """Lengths on and around page edges, including L = QL (the first rows see nothing of
+    the only page beyond the first tokens)."""
+    need_gpu()
+    lens = [max(L, ql) for L in (1, 2, 8, 127, 128, 129, 255, 256, 257, 1000)]
+    case = synth.make_index_case("idx_edges", 100 + ql * h, seq_lens=lens, query_len=ql,
+                                 heads=h, max_pages=12)
+    got = run_gpu(case)
+    assert_index_match(got, run_oracle(case), case.scores_init(), f"edges ql={ql} h={h}")
+
+
+def test_strided_query_and_padded_pages():
+    """Query rows taken from a wider buffer (byte strides) and pages padded past 9216."""
+    need_gpu()
+    case = synth.make_index_case("idx_stride", 120, seq_lens=[300, 900, 129], query_len=2,
+                                 heads=2, page_stride=9216 + 256, max_pages=10)
+    R, H, D = case.q.shape
+    wide = torch.zeros(R, H + 1, D + 64, dtype=torch.uint8)
+    wide[:, :H, :D] = torch.from_numpy(case.q)
+    q = wide.to(DEV)[:, :H, :D]
+    got = run_gpu(case, q=q)
+    assert_index_match(got, run_oracle(case), case.scores_init(), "strided")
+
+
+def test_max_blocks_truncates():
+    """A score row shorter than the request's page count: pages b >= S are not written."""
+    need_gpu()
+    case = synth.make_index_case("idx_trunc", 121, seq_lens=[2000, 700], query_len=1, heads=1,
+                                 max_pages=16)
+    full = run_oracle(case)
+    short = copy.deepcopy(case)
+    short.max_pages = 5
+    got = run_gpu(short)
+    assert got.shape[2] == 5
+    assert_index_match(got, full[:, :, :5], short.scores_init(), "truncated")
+
+
+def test_page_permutation_bit_identical():
+    need_gpu()
+    case = synth.make_index_case("idx_perm", 122, seq_lens=[500, 1300, 64], query_len=4,
+                                 heads=2, max_pages=12)
+    base = run_gpu(case)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(case.pages.shape[0])
+    c2 = copy.deepcopy(case)
+    c2.pages = np.empty_like(case.pages)
+    c2.pages[perm] = case.pages
+    c2.block_table = np.where(case.block_table >= 0, perm[np.maximum(case.block_table, 0)],
+                              -1).astype(np.int32)
+    got = run_gpu(c2)
+    assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
