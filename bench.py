@@ -1,13 +1,16 @@
-"""Benchmark of one quantized paged-attention decode step on one MI355X.
+"""Benchmark of the quantized paged-attention hot path on one MI355X.
 
-A step is uq_paged_decode + uq_paged_reduce over one batch of the high-batch fp8
-workload (B=128, Hk=8, QG=8, D=128, L ~ U[4096, 16384], block 16, 64 partitions of 256
-tokens, per-tensor e4m3 K/V).  Inputs are generated once, copied to HBM, and are
-resident before the timed region starts.
+Default workload (the headline): one decode step = uq_paged_decode + uq_paged_reduce over
+the high-batch fp8 batch (B=128, Hk=8, QG=8, D=128, L ~ U[4096, 16384], block 16, 64
+partitions of 256 tokens, per-tensor e4m3 K/V).  Other workloads (--workload):
+fp8_mid (B=16, L=16384), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions,
+e2m1 + e4m3 group scales, in-kernel rotation), nvfp4_index_ql{QL}_h{H} (32 requests,
+L ~ U[1024, 32768]: one uq_index_score call is a step).  Inputs are generated once,
+copied to HBM, and are resident before the timed region starts.
 
-Prints ONE JSON line: value = effective KV-stream GB/s (KV code bytes of every visible
-(token, head) / step time), with the decode kernel's roofline (HIP events on the launch
-stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: value = effective KV-stream GB/s (algorithmic bytes of every visible
+(token, head) / step wall time), with the dominant kernel's roofline (HIP events on the
+launch stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -26,30 +29,48 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs/decode step + KV-stream GB/s (% of HBM peak) at B=128 ctx=16k"
 CSRC = os.path.join(ROOT, "quantized_paged_attention_amd", "csrc")
-# Sources that decide the decode kernel's code and launch shape.
-DECODE_SRCS = ("decode_fp8.hip", "uq_device.h", "uq_kernels.h", "uq_abi.cpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fp8_high_traffic.json")
+COMMON_SRCS = ("uq_device.h", "uq_kernels.h", "uq_abi.cpp")
+# kernel source and committed rocprofv3 traffic record of each workload family
+KERNEL_SRC = {"fp8": "decode_fp8.hip", "fp4": "decode_fp4.hip", "index": "index_score.hip"}
 
 
-def source_hash() -> str:
+def family(workload: str) -> str:
+    return "index" if workload.startswith("nvfp4_index") else workload.split("_")[0]
+
+
+def source_hash(fam: str = "fp8") -> str:
     h = hashlib.sha256()
-    for name in DECODE_SRCS:
+    for name in (KERNEL_SRC[fam],) + COMMON_SRCS:
         h.update(open(os.path.join(CSRC, name), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(units_per_launch: float):
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3 PMC
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC
+    record of this workload, if it was taken on the current kernel sources; else None."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(TRAFFIC_FILE))
-    if rec.get("kernel_source_sha256_16") != source_hash():
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != source_hash(family(workload)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, n_seqs: int, min_seconds: float = 10.0):
+def _timed_passes(fn, min_seconds: float, max_passes: int = 8):
+    passes, t0 = 0, time.perf_counter()
+    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        fn()
+        passes += 1
+        print(f"cpu baseline: oracle pass {passes} done", file=sys.stderr, flush=True)
+    return passes, time.perf_counter() - t0
+
+
+def cpu_baseline_decode(case, n_seqs: int, min_seconds: float = 10.0):
     """fp64 oracle on the first n_seqs sequences (all kv heads) of the workload, repeated
     until at least min_seconds of wall time have been spent (at most 8 passes)."""
     from oracle import oracle
@@ -57,21 +78,50 @@ def cpu_baseline(case, n_seqs: int, min_seconds: float = 10.0):
     sub.q = case.q[:n_seqs]
     sub.block_table = case.block_table[:n_seqs]
     sub.seq_lens = case.seq_lens[:n_seqs]
-    passes, t0 = 0, time.perf_counter()
-    while passes < 8 and (passes == 0 or time.perf_counter() - t0 < min_seconds):
-        oracle.decode(sub.q, sub.cache, sub.block_table, sub.seq_lens,
-                      num_kv_heads=sub.num_kv_heads, kv_format=sub.kv_format,
-                      softmax_scale=sub.softmax_scale, k_scale=sub.k_scale,
-                      v_scale=sub.v_scale)
-        passes += 1
-        print(f"cpu baseline: oracle pass {passes} done", file=sys.stderr, flush=True)
-    dt = time.perf_counter() - t0
-    threads = oracle.num_threads()
+    passes, dt = _timed_passes(
+        lambda: oracle.decode(sub.q, sub.cache, sub.block_table, sub.seq_lens,
+                              num_kv_heads=sub.num_kv_heads, kv_format=sub.kv_format,
+                              softmax_scale=sub.softmax_scale, k_scale=sub.k_scale,
+                              v_scale=sub.v_scale, rot_signs=sub.rot_signs), min_seconds)
     return {"value": round(passes * sub.kv_bytes() / dt / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {n_seqs} of {case.B} sequences, all {case.num_kv_heads} kv heads "
                       f"({sub.kv_bytes() / 1e6:.1f} MB of KV) x {passes} passes, fp64, "
                       f"{dt:.2f} s wall"}
+
+
+def cpu_baseline_index(case, min_seconds: float = 10.0):
+    """fp64 oracle scorer on the whole index workload, repeated as above."""
+    from oracle import oracle
+    passes, dt = _timed_passes(
+        lambda: oracle.index_score(case.q, case.pages, case.block_table, case.seq_lens,
+                                   query_len=case.query_len, scores_init=case.scores_init()),
+        min_seconds)
+    return {"value": round(passes * case.page_bytes() / dt / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"all {case.num_reqs} requests ({case.page_bytes() / 1e6:.1f} MB of "
+                      f"pages) x {passes} passes, fp64, {dt:.2f} s wall"}
+
+
+def make_case(workload: str):
+    from quantized_paged_attention_amd import synth
+    if workload == "fp8_high":
+        return synth.fp8_high(), ("fp8_high: B=128 Hk=8 QG=8 D=128 L~U[4096,16384] block=16 "
+                                  "P=64 per-tensor e4m3 K/V, bf16 Q")
+    if workload == "fp8_mid":
+        return synth.fp8_mid(), ("fp8_mid: B=16 Hk=8 QG=8 D=128 L=16384 block=16 P=64 "
+                                 "per-tensor e4m3 K/V, bf16 Q")
+    if workload.startswith("fp4_d256_qg"):
+        qg = int(workload[len("fp4_d256_qg"):])
+        return synth.fp4_d256(qg), (f"{workload}: B=4 Hk=2 QG={qg} D=256 L=75000 block=64 "
+                                    "P=512 e2m1 K/V with e4m3 group-of-32 scales, 272-byte "
+                                    "slot, rotated keys, bf16 Q")
+    if workload.startswith("nvfp4_index_ql"):
+        ql, h = workload[len("nvfp4_index_ql"):].split("_h")
+        case = synth.nvfp4_index(int(ql), int(h))
+        return case, (f"{workload}: 32 requests QL={ql} H={h} D=128 L~U[1024,32768] "
+                      "128-token nvfp4 pages (9216 B), e4m3 Q")
+    raise SystemExit(f"bench.py: unknown workload {workload!r}")
 
 
 def main():
@@ -79,8 +129,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="fp8_high",
+                    help="fp8_high (default), fp8_mid, fp4_d256_qg{6,8,16}, "
+                         "nvfp4_index_ql{1,2,4,8}_h{1,2,4}")
     ap.add_argument("--cpu-seqs", type=int, default=128,
-                    help="sequences of the workload the CPU oracle baseline runs")
+                    help="sequences of a decode workload the CPU oracle baseline runs")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 launches), "
@@ -94,7 +147,7 @@ def main():
     import numpy as np
     import torch
 
-    from quantized_paged_attention_amd import synth, uq
+    from quantized_paged_attention_amd import uq
 
     if args.copy_calibration:
         n = args.copy_calibration << 20
@@ -110,57 +163,85 @@ def main():
 
     uq.load_library()
     dev = "cuda"
-    case = synth.fp8_high()
-    B, Hq, D, hk, P = case.B, case.Hq, case.D, case.num_kv_heads, case.num_partitions
-    q = torch.from_numpy(case.q).to(torch.bfloat16).to(dev)
-    cache = torch.from_numpy(case.cache).to(dev)
-    bt = torch.from_numpy(case.block_table).to(dev)
-    sl = torch.from_numpy(case.seq_lens).to(dev)
-    ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev)
-    vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev)
-    po, pm, pl = uq.alloc_partials(B, hk, case.QG, D, P, dev)
-    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
-    max_len = case.max_seq_len
+    workload = args.workload
+    fam = family(workload)
+    case, desc = make_case(workload)
     stream = torch.cuda.current_stream()
 
-    def decode():
-        uq.paged_decode(q, cache, bt, sl, kv_format=case.kv_format, max_seq_len=max_len,
-                        num_partitions=P, part_out=po, part_max=pm, part_sum=pl,
-                        softmax_scale=case.softmax_scale, k_scale=ks, v_scale=vs,
-                        stream=stream)
+    if fam == "index":
+        q = torch.from_numpy(case.q).to(dev)
+        pages = torch.from_numpy(case.pages).to(dev)
+        bt = torch.from_numpy(case.block_table).to(dev)
+        sl = torch.from_numpy(case.seq_lens).to(dev)
+        scores = torch.from_numpy(case.scores_init().copy()).to(dev)
 
-    def reduce():
-        uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, stream=stream)
+        def kernels():
+            uq.index_score(q, pages, bt, sl, scores, query_len=case.query_len, stream=stream)
+        algo_bytes = case.page_bytes()
+        names = ("index_score",)
+        dtype = "f16"
+    else:
+        B, Hq, D, hk, P = case.B, case.Hq, case.D, case.num_kv_heads, case.num_partitions
+        qdt = torch.float32 if case.q_dtype == "f32" else torch.bfloat16
+        q = torch.from_numpy(case.q).to(qdt).to(dev)
+        cache = torch.from_numpy(case.cache).to(dev)
+        bt = torch.from_numpy(case.block_table).to(dev)
+        sl = torch.from_numpy(case.seq_lens).to(dev)
+        is_fp8 = fam == "fp8"
+        ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev) if is_fp8 else None
+        vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev) if is_fp8 else None
+        rot = torch.from_numpy(case.rot_signs).to(dev) if case.rot_signs is not None else None
+        po, pm, pl = uq.alloc_partials(B, hk, case.QG, D, P, dev)
+        out = torch.empty(B, Hq, D, dtype=qdt, device=dev)
+        max_len = case.max_seq_len
+
+        def decode():
+            uq.paged_decode(q, cache, bt, sl, kv_format=case.kv_format, max_seq_len=max_len,
+                            num_partitions=P, part_out=po, part_max=pm, part_sum=pl,
+                            softmax_scale=case.softmax_scale, k_scale=ks, v_scale=vs,
+                            rot_signs=rot, stream=stream)
+
+        def reduce():
+            uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, stream=stream)
+
+        def kernels():
+            decode()
+            reduce()
+        algo_bytes = case.kv_bytes()
+        names = (f"decode_{fam}", "reduce")
+        dtype = "fp8" if is_fp8 else "f16"
 
     for _ in range(args.warmup):
-        decode()
-        reduce()
+        kernels()
     torch.cuda.synchronize()
 
+    # per step: an event before the step, then one after each kernel
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    nk = len(names)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        decode()
-        ev[i][1].record(stream)
-        reduce()
-        ev[i][2].record(stream)
+        if fam == "index":
+            kernels()
+            ev[i][1].record(stream)
+        else:
+            decode()
+            ev[i][1].record(stream)
+            reduce()
+            ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    dec_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    red_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    k_ms = [np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]) for j in range(nk)]
     step_ms = wall * 1e3 / K
-    kv_bytes = case.kv_bytes()
-    value = kv_bytes / (step_ms * 1e-3) / 1e9
-    dec_avg = float(dec_ms.mean())
-    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
-    traffic = measured_traffic(1)
+    value = algo_bytes / (step_ms * 1e-3) / 1e9
+    dom_avg = float(k_ms[0].mean())          # the dominant kernel: decode, or the scorer
+    achieved = algo_bytes / (dom_avg * 1e-3) / 1e9
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if fam != "index" else "µs/index call + K-page GB/s (% of HBM peak)",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -172,24 +253,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {
-            "workload": "fp8_high: B=128 Hk=8 QG=8 D=128 L~U[4096,16384] block=16 P=64 "
-                        "per-tensor e4m3 K/V, bf16 Q",
-            "kv_bytes": kv_bytes,
-            "global_batch": B,
-            "seq_len_max": max_len,
-        },
-        "kernels_us": {"decode_fp8_avg": round(dec_avg * 1e3, 2),
-                       "decode_fp8_median": round(float(np.median(dec_ms)) * 1e3, 2),
-                       "reduce_avg": round(float(red_ms.mean()) * 1e3, 2)},
+        "config": {"workload": desc, "algorithmic_bytes": algo_bytes},
+        "kernels_us": {f"{nm}_avg": round(float(k_ms[j].mean()) * 1e3, 2)
+                       for j, nm in enumerate(names)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": measured_traffic(workload)},
     }
+    res["kernels_us"][f"{names[0]}_median"] = round(float(np.median(k_ms[0])) * 1e3, 2)
+    if fam != "index":
+        res["config"].update(global_batch=case.B, seq_len_max=case.max_seq_len)
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(case, min(args.cpu_seqs, B))
+        res["cpu_baseline"] = (cpu_baseline_index(case) if fam == "index" else
+                               cpu_baseline_decode(case, min(args.cpu_seqs, case.B)))
     print(json.dumps(res), flush=True)
 
 
