@@ -90,7 +90,13 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  *   part_max      f32  [num_seqs, num_kv_heads, P, QG]  natural-log-domain maxima m
  *   part_sum      f32  [num_seqs, num_kv_heads, P, QG]  sums l
  * Only partitions that own at least one token (p < ceil(L_b / 256)) are written; the
- * others keep their contents and are never read by uq_paged_reduce.
+ * others keep their contents and are never read by uq_paged_reduce.  The partials are a
+ * flash-combine workspace: the decode may merge the statistics of a set of consecutive
+ * partitions into the first of them (m, l, o of their union) and write the others of the
+ * set as empty (m = -inf, l = 0, o rows left unwritten).  Combining all written states
+ * with uq_paged_reduce gives the attention output either way.  The fp8 kernel merges
+ * the partitions of one workgroup (2 or 4); the fp4 kernel writes every partition.
+ * With num_partitions = 1 part_* hold exactly the statistics above.
  * Supported: (UQ_KV_FP8_E4M3, D = 128, QG <= 8) and (UQ_KV_FP4_E2M1_E4M3S, D = 256,
  * QG <= 16); anything else returns UQ_ERR_UNSUPPORTED.
  * Device preconditions: 0 <= seq_lens[b] <= max_seq_len (larger values are clamped to
@@ -109,9 +115,10 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq,
 
 /* uq_paged_reduce -- flash-combine of the partials of uq_paged_decode ([P3] partition
  * split + parallel reduce; empty-partition handling).  For every (b, h, g), over the
- * partitions p < n_b = min(P, ceil(L_b / 256)) that hold tokens:
+ * partitions p < n_b = min(P, ceil(L_b / 256)) with l_p > 0:
  *   M = max_p m_p,  w_p = l_p exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p
- * and out = 0 when n_b = 0.
+ * and out = 0 when there is none.  Partial rows of partitions with l_p = 0 are not
+ * read (their bytes may be anything).
  *   part_out / part_max / part_sum   as written by uq_paged_decode (same shapes and P)
  *   out        [num_seqs, num_kv_heads * qg, head_dim] of out_dtype (UQ_F32 or UQ_BF16;
  *              the query dtype, [P3] output dtype follows the query), element strides

@@ -71,6 +71,36 @@ __device__ __forceinline__ const uint8_t* slot_ptr(const DecodeArgs& a, int ids,
          (int64_t)h * a.slot_bytes;
 }
 
+struct Chunk {
+  i32x4 kc[2][2];   // K codes of tiles 0, 1: bytes [32 q, 32 q + 16), [32 q + 16, 32 q + 32)
+  uint32_t ksw[2];  // K scale word of tiles 0, 1
+  i32x2 vc[8];      // V codes, dims 16 n .. 16 n + 15, of the 8 tokens of the PV k-slots
+  uint32_t vsw[8];  // V scale word of those tokens
+};
+
+__device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int ids, int blk_lo, int t0,
+                                            int L, int h, int n, int q) {
+  Chunk c;
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    int t = t0 + 16 * T + n;
+    t = t < L ? t : L - 1;
+    const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
+    c.kc[T][0] = *reinterpret_cast<const i32x4*>(sp + 32 * q);
+    c.kc[T][1] = *reinterpret_cast<const i32x4*>(sp + 32 * q + 16);
+    c.ksw[T] = *reinterpret_cast<const uint32_t*>(sp + kKScales + 4 * (q >> 1));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    int t = t0 + (e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4));
+    t = t < L ? t : L - 1;
+    const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
+    c.vc[e] = *reinterpret_cast<const i32x2*>(sp + kVCodes + 8 * n);
+    c.vsw[e] = *reinterpret_cast<const uint32_t*>(sp + kVScales + 4 * (n >> 3));
+  }
+  return c;
+}
+
 template <typename QT>
 __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   // Rotated query (f16, row stride kD + 8 halves) during the stream; the four waves'
@@ -213,31 +243,19 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
     const int ids = a.bt[(int64_t)b * a.bt_stride + bi];
     const int nchunk = nvis >= 64 ? 2 : (nvis + 31) / 32;
 
+    // ---- loads of a 32-token step: K of two 16-token tiles (lane = token n, bytes 32 q ..
+    //      32 q + 31 and the scale word holding groups 2q, 2q + 1), V of 8 tokens (lane =
+    //      dims 16 n .. 16 n + 15).  Tokens past L are clamped to L - 1 (a visible slot)
+    //      and masked below.  The next step's loads are issued before this step's math.
+    Chunk cur = load_chunk(a, ids, blk_lo, start, L, h, n, q);
     for (int ck = 0; ck < nchunk; ++ck) {
       const int t0 = start + 32 * ck;
-      // ---- loads: K of two 16-token tiles (lane = token n, bytes 32 q .. 32 q + 31 and
-      //      the scale word holding groups 2q, 2q + 1), V of 8 tokens (lane = dims 16 n ..)
-      i32x4 kc[2][2];
-      uint32_t ksw[2];
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        int t = t0 + 16 * T + n;
-        t = t < L ? t : L - 1;
-        const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
-        kc[T][0] = *reinterpret_cast<const i32x4*>(sp + 32 * q);
-        kc[T][1] = *reinterpret_cast<const i32x4*>(sp + 32 * q + 16);
-        ksw[T] = *reinterpret_cast<const uint32_t*>(sp + kKScales + 4 * (q >> 1));
-      }
-      i32x2 vc[8];
-      uint32_t vsw[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int t = t0 + (e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4));
-        t = t < L ? t : L - 1;
-        const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
-        vc[e] = *reinterpret_cast<const i32x2*>(sp + kVCodes + 8 * n);
-        vsw[e] = *reinterpret_cast<const uint32_t*>(sp + kVScales + 4 * (n >> 3));
-      }
+      Chunk nxt;
+      if (ck + 1 < nchunk) nxt = load_chunk(a, ids, blk_lo, t0 + 32, L, h, n, q);
+      const auto& kc = cur.kc;
+      const auto& ksw = cur.ksw;
+      const auto& vc = cur.vc;
+      const auto& vsw = cur.vsw;
 
       // ---- QK: s[T][jj] = score of token t0 + 16 T + 4 q + jj, head n
       f32x4 s[2];
@@ -324,6 +342,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         UQ_PV_BYTE(3)
 #undef UQ_PV_BYTE
       }
+      cur = nxt;
     }
   }
 

@@ -7,25 +7,35 @@
 // STEP G): for a work unit (sequence b, kv head h, partition p) the softmax statistics
 // (m, l, o = v_scale * sum exp(s - m) v / l) of the tokens of tile-groups p, p+P, ...
 //
-// Design (one 64-lane wave per work unit, no LDS, KV streamed once):
-//   * A tile-group (256 tokens = 16 tiles of 16) is processed in three phases, so the
-//     softmax needs one max and no running rescale inside the group:
-//       A. QK for all 16 tiles: per tile two 16x16x128 fp8 MFMAs with A = the K codes
-//          straight from HBM (lane = token, 32 head dims per lane) and B = the query
-//          group as an e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q) / lo(q s_q) in the
-//          first MFMA and the swapped order in the second, so every column ends with
-//          hi + lo of its row.  s_q is a per-row power of two: the pair reproduces a bf16
-//          query exactly.  Scores stay in registers (4 tokens x 16 tiles per lane).
-//       B. Softmax over the group: max across the 4 token lanes (xor 16 / xor 32),
-//          p = 2^(s - m + 8) (the 2^8 keeps small p normal in e4m3), P as hi/lo pair.
-//       C. PV: V^T comes from registers -- each lane loads 8 head dims of 4 tokens per
-//          tile and a v_perm byte transpose forms the 16x16x32 fp8 A operand; B = P with
-//          hi in columns 0-7 and lo in columns 8-15; accumulators stay in the MFMA
-//          output layout (lane = query column), added hi + lo once in the epilogue.
-//     Several tile-groups per unit (few partitions) merge with one rescale per group.
-//   * KV loads are buffer loads from a scalar per-tile base and constant per-lane
-//     offsets, non-temporal, issued several tiles ahead of their use; only the tail
-//     tile-group pays for masking.
+// Design (a workgroup of W = 4 waves per group of consecutive partitions of one
+// (sequence, kv head); KV streamed once):
+//   * Wave w streams R consecutive partitions (R = 2 for large batches, else 1; a
+//     partition that owns several strided tile-groups when P is small) as one online
+//     softmax.  The W wave states meet in LDS at the end and are merged into the
+//     statistics of the group's first partition; the group's other partitions are
+//     written as empty (m = -inf, l = 0), which the flash-combine reduce treats as
+//     absent.  The partial rows written to HBM shrink W * R times (11 MB instead of
+//     88 MB at B = 128, ctx 16k).
+//   * Measured on MI355X: partial-row write-backs interleaved with the KV read stream
+//     cost far more than their bytes (88 MB of partials: +90 us on a 480 us stream);
+//     the same stores kept L2-resident cost ~4 us.  With non-temporal KV loads and the
+//     8-fold merge the partials stay in L2 until the kernel ends and the store cost
+//     vanishes.
+//   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
+//     from HBM (lane = token, 32 head dims per lane: bytes [16r, 16r+16) and
+//     [64+16r, 64+16r+16)) and B = the query group as an e4m3 hi/lo pair -- columns
+//     0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row rotate.  s_q is a per-row
+//     power of two: the pair reproduces a bf16 query exactly.
+//   * Softmax is online in exp2 units against a reference max raised (with 4 units of
+//     headroom) only when a score exceeds it, p = 2^(s - ref + 8) <= 256 split into an
+//     e4m3 hi/lo pair in columns 0-7 / 8-15.  PV is a 16x16x32 fp8 MFMA per 8 head dims
+//     with A = V^T: each lane pair loads 16 dims of 4 tokens with 16-byte loads, swaps
+//     halves (DPP) and byte-transposes (v_perm), so V codes go to the MFMA untouched.
+//   * Loads are buffer loads through a descriptor per tile whose record count ends at
+//     the sequence's last visible token (invisible tokens read as zero, no branches);
+//     block ids come from a window preloaded before the stream.  The next tile pair's
+//     K and V loads are issued while the current pair is computed; sched_barrier fences
+//     keep that order (vector loads retire in order: a misplaced wait drains them all).
 #include "uq_device.h"
 #include "uq_kernels.h"
 
@@ -34,7 +44,7 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kTiles = 16;     // tiles of 16 tokens per tile-group
-constexpr int kAuxNT = 0;      // buffer cache policy bits (0: default)
+constexpr int kAuxNT = 2;      // KV loads non-temporal (buffer aux bit 1, see below)
 
 struct KTile {
   i32x4 a, b;  // K bytes [16r, 16r+16) and [64+16r, 64+16r+16) of token n
@@ -45,36 +55,45 @@ struct VTile {
 
 template <typename QT, int W>
 __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
-  // per-wave staging of one partition's bf16 output rows (QG <= 8 rows of 256 bytes)
-  __shared__ __attribute__((aligned(16))) uint16_t o_stage[W][8 * kD];
+  // staging of the merged partition's bf16 output rows (QG <= 8 rows of 256 bytes), and
+  // the states of waves 1..W-1 handed to wave 0 (per lane: 32 accumulators, m_run,
+  // m_true, l)
+  __shared__ __attribute__((aligned(16))) uint16_t o_stage[8 * kD];
+  __shared__ __attribute__((aligned(16))) float st_acc[W > 1 ? W - 1 : 1][32][64];
+  __shared__ float st_ml[W > 1 ? W - 1 : 1][3][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t item = (int64_t)blockIdx.x * W + wave;
-  if (item >= (int64_t)a.runs * a.B * a.Hk) return;
+  const int64_t item = blockIdx.x;  // (sequence, kv head, group of W runs)
   const int h = (int)(item % a.Hk);
   const int b = (int)((item / a.Hk) % a.B);
-  const int run = (int)(item / ((int64_t)a.Hk * a.B));
+  const int grp = (int)(item / ((int64_t)a.Hk * a.B));
 
   int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);  // wave-uniform
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int ntg = (L + kTileGroup - 1) / kTileGroup;
-  // The wave's tile-groups: first_tg, first_tg + step, ...  With one tile-group per
-  // partition (run_len > 0) a run covers partitions [run * run_len, +run_len), each
-  // flushed on its own; otherwise the wave owns partition `run` and its strided
-  // tile-groups p, p+P, ... (the partition -> tile-group map of the FP4 decode page).
+  // Partitions that hold tokens: p < pmax.  The workgroup owns partitions
+  // [part_first, part_first + W * R): wave w streams R of them (R = run_len when every
+  // partition is one tile-group, else 1), and the W wave states are merged into the
+  // statistics of partition part_first; the workgroup's other partitions are written as
+  // empty (m = -inf, l = 0).  The flash-combine of the reduce gives the same result as
+  // for separate partitions, and the partial rows written to HBM shrink W * R times.
+  const int pmax = a.P < ntg ? a.P : ntg;
+  const int R = a.run_len > 0 ? a.run_len : 1;
+  const int part_first = grp * W * R;
+  if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
   int first_tg, n_tg, step;
   if (a.run_len > 0) {
-    first_tg = run * a.run_len;
-    const int lim = (a.P < ntg ? a.P : ntg) - first_tg;
-    n_tg = lim < a.run_len ? lim : a.run_len;
+    first_tg = part_first + wave * R;
+    const int lim = pmax - first_tg;
+    n_tg = lim < 0 ? 0 : (lim < R ? lim : R);
     step = 1;
   } else {
-    first_tg = run;
-    n_tg = run < ntg ? (ntg - run + a.P - 1) / a.P : 0;
+    // partition part_first + wave owns the strided tile-groups p, p + P, ...
+    first_tg = part_first + wave;
+    n_tg = first_tg < pmax ? (ntg - first_tg + a.P - 1) / a.P : 0;
     n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
     step = a.P;
   }
-  if (n_tg <= 0) return;  // empty partitions: nothing written, never read by the reduce
 
   const int r = lane >> 4, n = lane & 15;
   const int g = n & 7;
@@ -327,53 +346,83 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- partition epilogue: add lo columns into hi columns, normalise, store
-    if (a.run_len > 0 || k + 1 == n_tg) {
-      const int part = a.run_len > 0 ? tg : first_tg;
-      const float l_tot = sum_across_rows(l_run);
-      const float inv = v_scale / (l_tot > 0.f ? l_tot : 1.f);
-      // Every lane joins the DPP exchange (lanes of the lo columns feed the hi columns).
-      // The bf16 rows go through LDS so that the partial is written with whole-line
-      // stores: written from registers directly it would be 16-byte pieces at 64-byte
-      // stride, and such scattered partial-line writes slow the concurrent KV stream.
-      const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part) * a.QG;
-      uint16_t* stage = o_stage[threadIdx.x >> 6];
+  }
+
+  // ---- merge the W wave states into partition part_first: a lane's state belongs to
+  //      its column (query head), so the merge is lane-local once the states meet in LDS
+  const float l_tot = sum_across_rows(l_run);
+  if constexpr (W > 1) {
+    if (wave > 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        i32x4 w;
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float o0 = (acc[2 * e][j] + row_ror8(acc[2 * e][j])) * inv;
-          const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
-          w[e] = (int)pack_bf16x2(o0, o1);
-        }
-        if (n < a.QG) *reinterpret_cast<i32x4*>(stage + n * kD + 32 * r + 8 * j) = w;
+        for (int j = 0; j < 4; ++j) st_acc[wave - 1][4 * m + j][lane] = acc[m][j];
+      st_ml[wave - 1][0][lane] = m_run;
+      st_ml[wave - 1][1][lane] = m_true;
+      st_ml[wave - 1][2][lane] = l_tot;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+  }
+  // statistics relative to the true maximum M over the workgroup's tokens
+  float M = m_true;
+#pragma unroll
+  for (int w = 1; w < W; ++w) M = fmaxf(M, st_ml[w - 1][1][lane]);
+  float f0 = fast_exp2(m_run - 8.f - M);  // 0 for a wave without tokens (m_run = -inf)
+  float l_all = l_tot * f0;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] *= f0;
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    const float fw = fast_exp2(st_ml[w - 1][0][lane] - 8.f - M);
+    l_all += st_ml[w - 1][2][lane] * fw;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] += st_acc[w - 1][4 * m + j][lane] * fw;
+  }
+  {
+    const float inv = v_scale / (l_all > 0.f ? l_all : 1.f);
+    // Every lane joins the DPP exchange (lanes of the lo columns feed the hi columns).
+    // The bf16 rows go through LDS so that the partial is written with whole-line
+    // stores: written from registers directly it would be 16-byte pieces at 64-byte
+    // stride, and such scattered partial-line writes slow the concurrent KV stream.
+    const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * a.QG;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      i32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float o0 = (acc[2 * e][j] + row_ror8(acc[2 * e][j])) * inv;
+        const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
+        w[e] = (int)pack_bf16x2(o0, o1);
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
-      __builtin_amdgcn_wave_barrier();
-      {
-        const int nbytes = a.QG * kD * 2;  // contiguous partial rows of this unit
-        uint16_t* out = a.part_o + row0 * kD;
+      if (n < a.QG) *reinterpret_cast<i32x4*>(o_stage + n * kD + 32 * r + 8 * j) = w;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int nbytes = a.QG * kD * 2;  // contiguous partial rows of this partition
+    uint16_t* out = a.part_o + row0 * kD;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int byte = c * 1024 + 16 * lane;
-          if (byte < nbytes)
-            *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
-                *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) + byte);
-        }
+    for (int c = 0; c < 2; ++c) {
+      const int byte = c * 1024 + 16 * lane;
+      if (byte < nbytes)
+        *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
+            *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(o_stage) + byte);
+    }
+    if (n < a.QG && r == 0) {
+      a.part_m[row0 + n] = M * kLn2;
+      a.part_l[row0 + n] = l_all;
+    }
+    // the workgroup's other partitions that hold tokens: empty states
+    int p_end = part_first + W * R;
+    p_end = p_end < pmax ? p_end : pmax;
+    for (int pe = part_first + 1 + r; pe < p_end; pe += 4) {
+      if (n < a.QG) {
+        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + pe) * a.QG + n;
+        a.part_m[row] = -INFINITY;
+        a.part_l[row] = 0.f;
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the stage is reused
-      __builtin_amdgcn_wave_barrier();
-      const int64_t row = row0 + n;
-      if (n < a.QG && r == 0) {  // statistics relative to the true maximum
-        a.part_m[row] = m_true * kLn2;
-        a.part_l[row] = l_tot * fast_exp2(m_run - m_true - 8.f);
-      }
-      m_run = -INFINITY;
-      m_true = -INFINITY;
-      l_run = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -381,9 +430,13 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t stream) {
-  constexpr int W = 2;
-  const int64_t items = (int64_t)a.runs * a.B * a.Hk;
-  const dim3 grid((unsigned)((items + W - 1) / W));
+  constexpr int W = 4;
+  const int R = a.run_len > 0 ? a.run_len : 1;
+  const int64_t groups = ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
+  const int64_t items = groups * a.B * a.Hk;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)items);
   if (q_is_f32)
     hipLaunchKernelGGL((decode_fp8_kernel<float, W>), grid, dim3(64 * W), 0, stream, a);
   else

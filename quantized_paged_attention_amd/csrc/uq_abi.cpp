@@ -125,14 +125,13 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
   a.block_size = block_size;
   // Work items: with one tile-group per partition a wave streams a run of consecutive
   // partitions of one (sequence, kv head), so the per-item start-up chain (length ->
-  // block table -> first KV loads) is paid once per run.  Long runs leave a ragged tail
-  // of waves at the end of the grid (the sequences' lengths differ), so runs stay at two
-  // partitions, and only when there are at least 64 items per compute unit.
+  // block table -> first KV loads) is paid once per run and fewer partial rows are
+  // written.  Runs of two, once there are at least 16 items per compute unit (shorter
+  // grids would leave compute units idle).
   if (a.TGPP == 1) {
     const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
     const int64_t work = (int64_t)num_seqs * num_kv_heads * pmax;
-    const int64_t rl = work >= 2 * 64 * 256 ? 2 : 1;
-    a.run_len = (int)rl;
+    a.run_len = work >= 16 * 256 ? 2 : 1;
     a.runs = (pmax + a.run_len - 1) / a.run_len;
   } else {
     a.run_len = 0;

@@ -204,3 +204,37 @@ def test_partition_runs_ragged_batch():
     case = small(lens=tuple(int(x) for x in lens), hk=8, qg=8, seed=57)
     got, _ = run_decode(case, P=32)
     assert_decode_close(got, oracle_decode(case), "runs ragged")
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("P", [40, 700])
+def test_reduce_skips_empty_partitions(D, P):
+    """Synthetic partials with some partitions empty (l = 0, m = -inf) whose partial rows
+    hold NaN: the reduce must not read them into the sum.  P = 700 exceeds the partitions
+    the reduce keeps in registers (its batched path).  Reference: the oracle's reduce on
+    the same statistics with those rows zeroed (an empty partition's o is 0 there)."""
+    need_gpu()
+    from oracle import oracle
+    rng = np.random.default_rng(58 + P + D)
+    B, hk, qg = 3, 2, 4
+    seq_lens = np.array([P * 256, 5 * 256 - 17, 0], np.int32)
+    pm = rng.normal(0.0, 3.0, (B, hk, P, qg))
+    pl = rng.uniform(0.5, 50.0, (B, hk, P, qg))
+    po = rng.normal(0.0, 1.0, (B, hk, P, qg, D))
+    empty = rng.random((B, hk, P, qg)) < 0.4
+    empty[:, :, 0] = False
+    pm[empty], pl[empty] = -np.inf, 0.0
+    po_t = torch.from_numpy(po).to(torch.bfloat16)
+    po_clean = po_t.double().numpy().copy()
+    po_clean[empty] = 0.0
+    po_t[torch.from_numpy(empty)] = float("nan")
+    pm32 = torch.from_numpy(pm).float()
+    pl32 = torch.from_numpy(pl).float()
+    want = oracle.reduce(po_clean, pm32.double().numpy(), pl32.double().numpy(), seq_lens)
+    out = torch.empty(B, hk * qg, D, dtype=torch.float32, device="cuda")
+    uq.paged_reduce(po_t.cuda(), pm32.cuda(), pl32.cuda(), torch.from_numpy(seq_lens).cuda(), out,
+                    max_seq_len=int(seq_lens.max()))
+    got = out.cpu().double().numpy()
+    assert np.isfinite(got).all()
+    assert np.all(got[2] == 0)
+    np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
