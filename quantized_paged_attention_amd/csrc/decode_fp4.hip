@@ -61,16 +61,6 @@ __device__ __forceinline__ float e4m3_byte(uint32_t word, int byte_idx) {
   return e4m3_to_f<0>((int)(word >> (8 * byte_idx)));
 }
 
-// Address of the slot of token t (0 <= t < L) of kv head h: the block id comes from
-// lane `(t / bs) - blk_lo` of `ids` (the wave's preloaded block ids).
-__device__ __forceinline__ const uint8_t* slot_ptr(const DecodeArgs& a, int ids, int blk_lo,
-                                                   int t, int h) {
-  const int blk = t / a.block_size;
-  const int phys = __shfl(ids, blk - blk_lo, 64);
-  return a.cache + (int64_t)phys * a.blk_stride + (int64_t)(t - blk * a.block_size) * a.pos_stride +
-         (int64_t)h * a.slot_bytes;
-}
-
 struct Chunk {
   i32x4 kc[2][2];   // K codes of tiles 0, 1: bytes [32 q, 32 q + 16), [32 q + 16, 32 q + 32)
   uint32_t ksw[2];  // K scale word of tiles 0, 1
@@ -78,25 +68,64 @@ struct Chunk {
   uint32_t vsw[8];  // V scale word of those tokens
 };
 
-__device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int ids, int blk_lo, int t0,
-                                            int L, int h, int n, int q) {
+// Byte offsets of a lane's loads inside a 16-token tile (constant for the kernel).
+struct LaneOffsets {
+  uint32_t k;      // K codes of token n, bytes 32 q ..
+  uint32_t ks;     // K scale word of token n holding groups 2q, 2q + 1
+  uint32_t v[4];   // V codes of token 4q + e, dims 16 n ..
+  uint32_t vs[4];  // V scale word of token 4q + e holding group n / 2
+};
+
+// Buffer resource of the 16-token tile starting at token `tok` (a multiple of 16) of kv
+// head h: base = the tile's first slot of the head, record count = its visible tokens
+// only, so every byte of a token past L reads as zero with no branch and no access.
+// The block id comes from lane (tok / bs - blk_lo) of the wave's preloaded ids.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const DecodeArgs& a, int ids,
+                                                           int blk_lo, int tok, int L, int h,
+                                                           int bs_shift) {
+  const int blk = tok >> bs_shift;
+  const int phys = __builtin_amdgcn_readlane(ids, blk - blk_lo);
+  int nvis = L - tok;
+  nvis = nvis < 0 ? 0 : (nvis > 16 ? 16 : nvis);
+  const uint64_t base = (uint64_t)(a.cache + (int64_t)phys * a.blk_stride +
+                                   (int64_t)(tok & (a.block_size - 1)) * a.pos_stride +
+                                   (int64_t)h * a.slot_bytes);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                           (short)0,
+                                           __builtin_amdgcn_readfirstlane(nvis * a.pos_stride),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, int ids,
+                                            int blk_lo, int t0, int L, int h, int bs_shift) {
   Chunk c;
+  LaneOffsets o;  // (recomputed per step: cheaper than keeping 10 registers live)
+  {
+    const uint32_t pos = (uint32_t)a.pos_stride;
+    o.k = n * pos + 32 * q;
+    o.ks = o.k - 32 * q + kKScales + 4 * (q >> 1);
 #pragma unroll
-  for (int T = 0; T < 2; ++T) {
-    int t = t0 + 16 * T + n;
-    t = t < L ? t : L - 1;
-    const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
-    c.kc[T][0] = *reinterpret_cast<const i32x4*>(sp + 32 * q);
-    c.kc[T][1] = *reinterpret_cast<const i32x4*>(sp + 32 * q + 16);
-    c.ksw[T] = *reinterpret_cast<const uint32_t*>(sp + kKScales + 4 * (q >> 1));
+    for (int e = 0; e < 4; ++e) {
+      o.v[e] = (4 * q + e) * pos + kVCodes + 8 * n;
+      o.vs[e] = o.v[e] - kVCodes - 8 * n + kVScales + 4 * (n >> 3);
+    }
   }
+  const auto r0 = tile_rsrc(a, ids, blk_lo, t0, L, h, bs_shift);
+  const auto r1 = tile_rsrc(a, ids, blk_lo, t0 + 16, L, h, bs_shift);
+  c.kc[0][0] = __builtin_amdgcn_raw_buffer_load_b128(r0, o.k, 0, 0);
+  c.kc[0][1] = __builtin_amdgcn_raw_buffer_load_b128(r0, o.k + 16, 0, 0);
+  c.ksw[0] = __builtin_amdgcn_raw_buffer_load_b32(r0, o.ks, 0, 0);
+  c.kc[1][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, o.k, 0, 0);
+  c.kc[1][1] = __builtin_amdgcn_raw_buffer_load_b128(r1, o.k + 16, 0, 0);
+  c.ksw[1] = __builtin_amdgcn_raw_buffer_load_b32(r1, o.ks, 0, 0);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    int t = t0 + (e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4));
-    t = t < L ? t : L - 1;
-    const uint8_t* sp = slot_ptr(a, ids, blk_lo, t, h);
-    c.vc[e] = *reinterpret_cast<const i32x2*>(sp + kVCodes + 8 * n);
-    c.vsw[e] = *reinterpret_cast<const uint32_t*>(sp + kVScales + 4 * (n >> 3));
+  for (int e = 0; e < 4; ++e) {
+    c.vc[e] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r0, o.v[e], 0, 0));
+    c.vsw[e] = __builtin_amdgcn_raw_buffer_load_b32(r0, o.vs[e], 0, 0);
+    c.vc[4 + e] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r1, o.v[e], 0, 0));
+    c.vsw[4 + e] = __builtin_amdgcn_raw_buffer_load_b32(r1, o.vs[e], 0, 0);
   }
   return c;
 }
@@ -114,17 +143,78 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int unit = blockIdx.x;
-  const int p = unit % a.P;
-  const int h = (unit / a.P) % a.Hk;
-  const int b = unit / (a.P * a.Hk);
+  // workgroup = (kv head h, sequence b, group grp), kv head fastest: workgroups that run
+  // together read neighbouring slots of the same tokens
+  const int64_t unit = blockIdx.x;
+  const int h = (int)(unit % a.Hk);
+  const int b = (int)((unit / a.Hk) % a.B);
+  const int grp = (int)(unit / ((int64_t)a.Hk * a.B));
 
   int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int ntg = (L + kTileGroup - 1) / kTileGroup;
-  if (p >= ntg) return;  // empty partition (uniform over the workgroup): nothing written
-  int n_tg = (ntg - p + a.P - 1) / a.P;
-  n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+  // Partitions with tokens: p < pmax.  With one tile-group per partition the workgroup
+  // owns the run of partitions [part_first, part_first + R) (R = run_len) and merges
+  // them into partition part_first (the others are written as empty); otherwise it owns
+  // partition part_first and its strided tile-groups p, p + P, ...
+  const int pmax = a.P < ntg ? a.P : ntg;
+  const int R = a.run_len > 0 ? a.run_len : 1;
+  const int part_first = grp * R;
+  if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
+  int n_tg, tg_step;
+  if (a.run_len > 0) {
+    n_tg = pmax - part_first < R ? pmax - part_first : R;
+    tg_step = 1;
+  } else {
+    n_tg = (ntg - part_first + a.P - 1) / a.P;
+    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+    tg_step = a.P;
+  }
+  const int p = part_first;
+
+  const int n = lane & 15;   // query head of the QK / softmax layout; PV column group
+  const int q = lane >> 4;   // lane row group
+
+  // ---- the stream.  Wave w takes tokens [64w, 64w + 64) of each of the workgroup's
+  //      tile-groups.  The first step's loads go out before the query rotation, so the
+  //      rotation runs under their latency.
+  const int blk_per_wave = 64 / a.block_size > 0 ? 64 / a.block_size : 1;
+  const int bs_shift = 31 - __builtin_clz(a.block_size);
+  // The wave's stream: 32-token steps c = 0, 1, ... ; step c covers tokens
+  // [s_k + 32 (c & 1), + 32) of tile-group k = c >> 1, s_k = 256 tg_k + 64 wave.  Steps
+  // holding tokens form a prefix.  Block ids of a window of tile-groups are preloaded
+  // (lane i: tile-group kw + i / bpw, block i % bpw of its 64 tokens, clamped to the last
+  // visible block so that no table entry past the sequence is read).
+  const int bpw = blk_per_wave;
+  const int win_tgs = 64 / bpw;
+  int ids = 0, kw = -win_tgs;
+  auto s_of = [&](int k) { return (part_first + k * tg_step) * kTileGroup + 64 * wave; };
+  auto load_ids = [&](int k0) {
+    kw = k0;
+    const int k = k0 + lane / bpw;
+    int v = 0;
+    if (k < n_tg) {
+      const int sk = s_of(k);
+      if (sk < L) {
+        int bi = (sk >> bs_shift) + lane % bpw;
+        const int blk_last = (L - 1) >> bs_shift;
+        bi = bi > blk_last ? blk_last : bi;
+        v = a.bt[(int64_t)b * a.bt_stride + bi];
+      }
+    }
+    ids = v;
+  };
+  auto step_t0 = [&](int c) { return s_of(c >> 1) + 32 * (c & 1); };
+  auto step_ok = [&](int c) { return c < 2 * n_tg && step_t0(c) < L; };
+  auto load_step = [&](int c, Chunk& dst) {
+    const int k = c >> 1;
+    if (k >= kw + win_tgs) load_ids(k);
+    const int sk = s_of(k);
+    dst = load_chunk(a, n, q, ids, (sk >> bs_shift) - (k - kw) * bpw, step_t0(c), L, h, bs_shift);
+  };
+  Chunk cA, cB;
+  if (step_ok(0)) load_step(0, cA);
+
 
   // ---- rotated query: wave w, lane (row 4w + lane/16, dims 16 c .. 16 c + 15)
   {
@@ -214,13 +304,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  const int n = lane & 15;   // query head of the QK / softmax layout; PV column group
-  const int q = lane >> 4;   // lane row group
-  // B operand of QK: head n, dims 64 q + 8 kk .. + 8 for kk = 0..7
-  f16x8 qb[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    qb[kk] = *reinterpret_cast<const f16x8*>(lds_q + n * kQStride + 64 * q + 8 * kk);
+  // B operand of QK (head n, dims 64 q + 8 kk .. + 8) is read from LDS at each use
+  const _Float16* qrow = lds_q + n * kQStride + 64 * q;
   const float fac = lds_fac[n];
 
   float m_run = -INFINITY;  // reference of head n (exp2 units); acc/l are relative to it
@@ -229,29 +314,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 #pragma unroll
   for (int mm = 0; mm < 16; ++mm) acc[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int blk_per_wave = 64 / a.block_size > 0 ? 64 / a.block_size : 1;
-  for (int k = 0; k < n_tg; ++k) {
-    const int start = (p + k * a.P) * kTileGroup + 64 * wave;
-    const int nvis = L - start;
-    if (nvis <= 0) continue;  // no tokens of this wave in this tile-group
-    // block ids of the wave's 64 tokens (lane i < blocks: block blk_lo + i), clamped to
-    // the last visible block so that no table entry past the sequence is dereferenced
-    const int blk_lo = start / a.block_size;
-    const int blk_last = (L - 1) / a.block_size;
-    int bi = blk_lo + (lane < blk_per_wave ? lane : 0);
-    bi = bi > blk_last ? blk_last : bi;
-    const int ids = a.bt[(int64_t)b * a.bt_stride + bi];
-    const int nchunk = nvis >= 64 ? 2 : (nvis + 31) / 32;
-
-    // ---- loads of a 32-token step: K of two 16-token tiles (lane = token n, bytes 32 q ..
-    //      32 q + 31 and the scale word holding groups 2q, 2q + 1), V of 8 tokens (lane =
-    //      dims 16 n .. 16 n + 15).  Tokens past L are clamped to L - 1 (a visible slot)
-    //      and masked below.  The next step's loads are issued before this step's math.
-    Chunk cur = load_chunk(a, ids, blk_lo, start, L, h, n, q);
-    for (int ck = 0; ck < nchunk; ++ck) {
-      const int t0 = start + 32 * ck;
-      Chunk nxt;
-      if (ck + 1 < nchunk) nxt = load_chunk(a, ids, blk_lo, t0 + 32, L, h, n, q);
+  // one 32-token step: QK, online softmax, PV
+  auto step = [&](const Chunk& cur, const int t0) {
       const auto& kc = cur.kc;
       const auto& ksw = cur.ksw;
       const auto& vc = cur.vc;
@@ -270,7 +334,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
           const f16x2 sc = kk < 4 ? s0 : s1;
           const f16x8 A = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc,
                                fp4_pair<2>(wd) * sc, fp4_pair<3>(wd) * sc);
-          c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[kk], c4, 0, 0, 0);
+          const f16x8 qb = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
+          c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb, c4, 0, 0, 0);
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -280,6 +345,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         s[T] = c4;
       }
 
+      __builtin_amdgcn_sched_barrier(0);
       // ---- online softmax (reference moves only when a score exceeds it)
       float mloc = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
@@ -308,6 +374,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
       const f16x8 pa = f16x8{(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3],
                              (_Float16)pv[4], (_Float16)pv[5], (_Float16)pv[6], (_Float16)pv[7]};
 
+      __builtin_amdgcn_sched_barrier(0);
       // ---- PV.  Token pair u = (2u, 2u+1); X / Y hold per byte the even / odd dim of the
       //      byte's position for both tokens (low nibble: token 2u).
       f16x2 vs[4];
@@ -337,12 +404,27 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, by, acc[8 * hh + 2 * KB + 1], 0, 0, 0);      \
   }
         UQ_PV_BYTE(0)
+        __builtin_amdgcn_sched_barrier(0);
         UQ_PV_BYTE(1)
+        __builtin_amdgcn_sched_barrier(0);
         UQ_PV_BYTE(2)
+        __builtin_amdgcn_sched_barrier(0);
         UQ_PV_BYTE(3)
+        __builtin_amdgcn_sched_barrier(0);
 #undef UQ_PV_BYTE
       }
-      cur = nxt;
+  };
+  // two step buffers, alternating: the next step's loads are issued before this step
+  if (step_ok(0)) {
+    for (int c = 0;; c += 2) {
+      const bool ok1 = step_ok(c + 1);
+      if (ok1) load_step(c + 1, cB);
+      step(cA, step_t0(c));
+      if (!ok1) break;
+      const bool ok2 = step_ok(c + 2);
+      if (ok2) load_step(c + 2, cA);
+      step(cB, step_t0(c + 1));
+      if (!ok2) break;
     }
   }
 
@@ -374,6 +456,12 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + hd;
         a.part_m[row] = M * kLn2;
         a.part_l[row] = lsum;
+        // the run's other partitions that hold tokens: empty states
+        const int p_end = a.run_len > 0 ? (part_first + R < pmax ? part_first + R : pmax) : 0;
+        for (int pe = part_first + 1; pe < p_end; ++pe) {
+          a.part_m[row + (int64_t)(pe - p) * a.QG] = -INFINITY;
+          a.part_l[row + (int64_t)(pe - p) * a.QG] = 0.f;
+        }
       }
     }
 #pragma unroll
@@ -414,7 +502,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, hipStream_t stream) {
-  const int64_t units = (int64_t)a.B * a.Hk * a.P;
+  const int64_t units = (int64_t)a.B * a.Hk * a.runs;  // runs: workgroups per (b, h)
   if (units <= 0) return hipSuccess;
   if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)units), block(64 * kW);

@@ -201,6 +201,18 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
     win_hi = one(w0 + 4 + (lane >> 4));
   };
   load_window(0);
+  auto load_half_window = [&](int w0) {  // tile-groups w0 .. w0+3 into their half
+    auto one = [&](int k) {
+      int v = 0;
+      if (k < n_tg) {
+        const int tok = (first_tg + k * step) * kTileGroup + 16 * (lane & 15);
+        if (tok < L) v = bt_row[tok >> bs_shift];
+      }
+      return v;
+    };
+    const int v = one(w0 + (lane >> 4));
+    if (w0 & 4) win_hi = v; else win_lo = v;
+  };
 
   // Buffer resource of tile t (0..15) of work tile-group kk (in the current window):
   // base = the tile's first slot of this head, record count = its visible tokens only
@@ -238,14 +250,17 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   // flight while the wave computes; the register footprint stays small enough for four
   // waves per SIMD, which is what keeps the memory system busy.  No data-dependent
   // branches except a rare wave-uniform softmax rescale.
-  KTile kp[2];
+  KTile kp[2][2];  // [pair parity][tile]: K is loaded two pairs ahead
   VTile vp[2];
   {
     const auto r0 = rsrc_of(0, 0), r1 = rsrc_of(0, 1);
-    load_k(r0, kp[0]);
-    load_k(r1, kp[1]);
+    load_k(r0, kp[0][0]);
+    load_k(r1, kp[0][1]);
     load_v(r0, vp[0]);
     load_v(r1, vp[1]);
+    const auto r2 = rsrc_of(0, 2), r3 = rsrc_of(0, 3);
+    load_k(r2, kp[1][0]);
+    load_k(r3, kp[1][1]);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -257,7 +272,12 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       const int pair_start = tg_start + 32 * pr;
       const int pf_k = pr + 1 < kTiles / 2 ? k : k + 1;  // the next pair
       const int pf_t0 = pr + 1 < kTiles / 2 ? 2 * (pr + 1) : 0;
-      if (pr == kTiles / 2 - 1 && (k & 7) == 7 && k + 1 < n_tg) load_window(k + 1);  // rare
+      const int pk_k = pr + 2 < kTiles / 2 ? k : k + 1;  // the pair after next (K)
+      const int pk_t0 = pr + 2 < kTiles / 2 ? 2 * (pr + 2) : 2 * (pr + 2 - kTiles / 2);
+      // rolling window: the half that will hold tile-groups k+1 .. k+4 is refilled when
+      // the K prefetch first reaches tile-group k+1 (rare: only for more than 8)
+      if (pr == kTiles / 2 - 2 && ((k + 1) & 3) == 0 && k + 1 >= 8 && k + 1 < n_tg)
+        load_half_window(k + 1);
       // the pair boundary is a scheduling fence: the next pair's QK (and its wait for
       // K loads issued one pair earlier) must not be hoisted above this pair's PV work
       __builtin_amdgcn_sched_barrier(0);
@@ -265,8 +285,8 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       float s[2][4];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const i32x8 kop = {kp[tt].a[0], kp[tt].a[1], kp[tt].a[2], kp[tt].a[3],
-                           kp[tt].b[0], kp[tt].b[1], kp[tt].b[2], kp[tt].b[3]};
+        const KTile& kt = kp[pr & 1][tt];
+        const i32x8 kop = {kt.a[0], kt.a[1], kt.a[2], kt.a[3], kt.b[0], kt.b[1], kt.b[2], kt.b[3]};
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own, z, 0, 0, 0, 127, 0, 127);
 #pragma unroll
@@ -279,9 +299,11 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       // instructions that free their registers, nor sink them below later waits (vector
       // loads retire in order, so a misplaced load turns a partial wait into a drain).
       __builtin_amdgcn_sched_barrier(0);
-      const auto rs0 = rsrc_of(pf_k, pf_t0), rs1 = rsrc_of(pf_k, pf_t0 + 1);
-      load_k(rs0, kp[0]);
-      load_k(rs1, kp[1]);
+      {
+        const auto rk0 = rsrc_of(pk_k, pk_t0), rk1 = rsrc_of(pk_k, pk_t0 + 1);
+        load_k(rk0, kp[pr & 1][0]);
+        load_k(rk1, kp[pr & 1][1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax against a reference max m_run >= every score seen.  It is raised
@@ -335,8 +357,11 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         transpose4x4_bytes_sel(hi4, &vtr[tt][4], sel_a, sel_b);
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_v(rs0, vp[0]);
-      load_v(rs1, vp[1]);
+      {
+        const auto rv0 = rsrc_of(pf_k, pf_t0), rv1 = rsrc_of(pf_k, pf_t0 + 1);
+        load_v(rv0, vp[0]);
+        load_v(rv1, vp[1]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // ---- PV: acc[m][j'] holds O^T[d = 32 r' + 8 j' + m][column n']
 #pragma unroll

@@ -126,12 +126,13 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
   // Work items: with one tile-group per partition a wave streams a run of consecutive
   // partitions of one (sequence, kv head), so the per-item start-up chain (length ->
   // block table -> first KV loads) is paid once per run and fewer partial rows are
-  // written.  Runs of two, once there are at least 16 items per compute unit (shorter
-  // grids would leave compute units idle).
+  // written.  Measured on MI355X (B=16 / B=128, ctx up to 16k, 64 partitions): runs of
+  // three pay off from 128 partitions per compute unit, runs of two from 16 (shorter
+  // grids would leave compute units idle at the end).
   if (a.TGPP == 1) {
     const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
     const int64_t work = (int64_t)num_seqs * num_kv_heads * pmax;
-    a.run_len = work >= 16 * 256 ? 2 : 1;
+    a.run_len = work >= 128 * 256 ? 3 : (work >= 16 * 256 ? 2 : 1);
     a.runs = (pmax + a.run_len - 1) / a.run_len;
   } else {
     a.run_len = 0;
@@ -160,6 +161,15 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
       return fail(UQ_ERR_INVALID_ARG, "rot_signs must be 16-byte aligned");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache needs slot_bytes a multiple of 16");
     if (num_seqs == 0) return ok();
+    // one workgroup streams a run of partitions (one query rotation, one merged partial).
+    // Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions): runs of 3 or 4 beat 2
+    // (59 / 62 us) and 1 (78 us); runs of 3 once there are 2 of them per compute unit.
+    if (a.TGPP == 1) {
+      const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
+      const int64_t work = (int64_t)num_seqs * num_kv_heads * pmax;
+      a.run_len = work >= 3 * 2 * 256 ? 3 : (work >= 2 * 2 * 256 ? 2 : 1);
+      a.runs = (pmax + a.run_len - 1) / a.run_len;
+    }
     return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
                          "decode_fp4");
   }

@@ -193,15 +193,19 @@ def test_high_config_sampled():
     assert_decode_close(got[pick], ref, "fp8_high sample")
 
 
-def test_partition_runs_ragged_batch():
-    """A batch large enough that each wave streams a run of two partitions (B=128, Hk=8,
-    P=32, i.e. 32768 (sequence, head, partition) items): ragged lengths end a sequence in
-    the first or the second partition of a run, on and off tile-group edges."""
+@pytest.mark.parametrize("B,run", [(32, 2), (128, 3)])
+def test_partition_runs_ragged_batch(B, run):
+    """Batches large enough that each wave streams a run of several partitions (Hk=8,
+    P=32: B=32 gives 8192 (sequence, head, partition) items and runs of two, B=128 gives
+    32768 and runs of three; four waves merge their runs): ragged lengths end a sequence
+    at every position of a run and of a merged group, on and off tile-group edges."""
     need_gpu()
-    rng = np.random.default_rng(57)
-    lens = rng.integers(1, 8193, size=128)
+    rng = np.random.default_rng(57 + B)
+    lens = rng.integers(1, 8193, size=B)
     lens[:8] = [1, 255, 256, 257, 511, 512, 8192, 4097]
-    case = small(lens=tuple(int(x) for x in lens), hk=8, qg=8, seed=57)
+    lens[8:20] = 256 * np.arange(1, 13) + 1       # 1..12 partitions + 1 token
+    case = small(lens=tuple(int(x) for x in lens), hk=8, qg=8, seed=57 + B)
+    log(f"case fp8 runs B={B} (run length {run})")
     got, _ = run_decode(case, P=32)
     assert_decode_close(got, oracle_decode(case), "runs ragged")
 
