@@ -159,13 +159,19 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   // partition part_first and its strided tile-groups p, p + P, ...
   const int pmax = a.P < ntg ? a.P : ntg;
   const int R = a.run_len > 0 ? a.run_len : 1;
-  const int part_first = grp * R;
-  if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
-  int n_tg, tg_step;
+  int part_first, p_end, n_tg, tg_step;
   if (a.run_len > 0) {
-    n_tg = pmax - part_first < R ? pmax - part_first : R;
+    // this sequence's pmax partitions in G nearly equal runs of at most R
+    const int G = (pmax + R - 1) / R;
+    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
+    part_first = (int)((int64_t)grp * pmax / G);
+    p_end = (int)((int64_t)(grp + 1) * pmax / G);
+    n_tg = p_end - part_first;
     tg_step = 1;
   } else {
+    part_first = grp;
+    if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
+    p_end = part_first + 1;
     n_tg = (ntg - part_first + a.P - 1) / a.P;
     n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
     tg_step = a.P;
@@ -456,8 +462,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + hd;
         a.part_m[row] = M * kLn2;
         a.part_l[row] = lsum;
-        // the run's other partitions that hold tokens: empty states
-        const int p_end = a.run_len > 0 ? (part_first + R < pmax ? part_first + R : pmax) : 0;
+        // the run's other partitions: empty states
         for (int pe = part_first + 1; pe < p_end; ++pe) {
           a.part_m[row + (int64_t)(pe - p) * a.QG] = -INFINITY;
           a.part_l[row + (int64_t)(pe - p) * a.QG] = 0.f;

@@ -72,22 +72,31 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
   const int ntg = (L + kTileGroup - 1) / kTileGroup;
   // Partitions that hold tokens: p < pmax.  The workgroup owns partitions
-  // [part_first, part_first + W * R): wave w streams R of them (R = run_len when every
-  // partition is one tile-group, else 1), and the W wave states are merged into the
-  // statistics of partition part_first; the workgroup's other partitions are written as
-  // empty (m = -inf, l = 0).  The flash-combine of the reduce gives the same result as
-  // for separate partitions, and the partial rows written to HBM shrink W * R times.
+  // [part_first, p_end): with one tile-group per partition a run of consecutive ones per
+  // wave (up to R = run_len), else one partition (with its strided tile-groups) per wave.
+  // The W wave states are merged into the statistics of partition part_first and the
+  // workgroup's other partitions are written as empty (m = -inf, l = 0).  The
+  // flash-combine of the reduce gives the same result as for separate partitions, and
+  // the partial rows written to HBM shrink up to W * R times.
   const int pmax = a.P < ntg ? a.P : ntg;
   const int R = a.run_len > 0 ? a.run_len : 1;
-  const int part_first = grp * W * R;
-  if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
-  int first_tg, n_tg, step;
+  int part_first, p_end, first_tg, n_tg, step;
   if (a.run_len > 0) {
-    first_tg = part_first + wave * R;
-    const int lim = pmax - first_tg;
-    n_tg = lim < 0 ? 0 : (lim < R ? lim : R);
+    // this sequence's pmax partitions in G nearly equal groups of at most W * R, and a
+    // group's m partitions nearly equally over its W waves (no wave idles at the merge
+    // for a whole run)
+    const int G = (pmax + W * R - 1) / (W * R);
+    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
+    part_first = (int)((int64_t)grp * pmax / G);
+    p_end = (int)((int64_t)(grp + 1) * pmax / G);
+    const int m = p_end - part_first;
+    first_tg = part_first + wave * m / W;
+    n_tg = part_first + (wave + 1) * m / W - first_tg;
     step = 1;
   } else {
+    part_first = grp * W;
+    if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
+    p_end = part_first + W < pmax ? part_first + W : pmax;
     // partition part_first + wave owns the strided tile-groups p, p + P, ...
     first_tg = part_first + wave;
     n_tg = first_tg < pmax ? (ntg - first_tg + a.P - 1) / a.P : 0;
@@ -440,8 +449,6 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       a.part_l[row0 + n] = l_all;
     }
     // the workgroup's other partitions that hold tokens: empty states
-    int p_end = part_first + W * R;
-    p_end = p_end < pmax ? p_end : pmax;
     for (int pe = part_first + 1 + r; pe < p_end; pe += 4) {
       if (n < a.QG) {
         const int64_t row = (((int64_t)b * a.Hk + h) * a.P + pe) * a.QG + n;

@@ -7,8 +7,9 @@
 // q[r QL + j, h, :] . k[t, :], with k = e2m1(code) * e4m3(scale of its 16-dim group);
 // -inf when the page holds no such token.
 //
-// Design: a workgroup of four waves per (request, 16 consecutive pages); wave w scores
-// pages w, w + 4, w + 8, w + 12 of them, loading the next page while scoring one.
+// Design: one wave per (request, page), four waves per workgroup (measured on MI355X:
+// more pages per wave, with the next page loaded under the current one, lose to the
+// extra waves in flight).  The code keeps the multi-page loop (kPagesPerWave).
 //   * Every e2m1 * e4m3 product and every e4m3 query value is exact in f16, so the page
 //     is dequantised exactly (one v_cvt_scalef32_pk_f16_fp4 with unit scale and one
 //     packed f16 multiply per byte) and the dot products run on v_mfma_f32_16x16x32_f16
@@ -33,7 +34,7 @@ constexpr int kCodeBytes = 64;    // per token: 128 e2m1 codes
 constexpr int kScaleBytes = 8;    // per token: one e4m3 scale per 16 dims
 constexpr int kScaleRegion = kPageTokens * kCodeBytes;
 constexpr int kWaves = 4;
-constexpr int kPagesPerWave = 4;
+constexpr int kPagesPerWave = 1;
 constexpr int kPagesPerGroup = kWaves * kPagesPerWave;
 
 template <int sel>
@@ -76,6 +77,11 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_kernel(IndexArgs a) {
   const int per_req = (a.max_blocks + kPagesPerGroup - 1) / kPagesPerGroup;
   const int r = blockIdx.x / per_req;
   const int b0 = (blockIdx.x % per_req) * kPagesPerGroup + wave;
+  // The table entries are read together with the length (entries below max_blocks are
+  // inside the table row; one past the sequence is read but never used).
+  int pid = 0;
+  if (lane < kPagesPerWave && b0 + kWaves * lane < a.max_blocks)
+    pid = a.bt[(int64_t)r * a.bt_stride + b0 + kWaves * lane];
   const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[r]);
   int nblk = (L + kPageTokens - 1) / kPageTokens;
   nblk = nblk < a.max_blocks ? nblk : a.max_blocks;
@@ -87,9 +93,7 @@ __global__ __launch_bounds__(64 * kWaves) void index_score_kernel(IndexArgs a) {
   const int q = lane >> 4;  // dims 32q .. 32q + 31
   const int R = a.QL * a.H;
 
-  // page ids of this wave's pages (lane i < npg: page b0 + kWaves i), then the first page
-  int pid = 0;
-  if (lane < npg) pid = a.bt[(int64_t)r * a.bt_stride + b0 + kWaves * lane];
+  // page ids of this wave's pages: lane i < npg holds page b0 + kWaves i
   auto page_ptr = [&](int i) {
     const int id = __builtin_amdgcn_readlane(pid, i);
     return a.pages + (int64_t)id * a.page_stride;

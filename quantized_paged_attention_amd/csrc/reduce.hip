@@ -21,12 +21,12 @@
 namespace uq {
 namespace {
 
-template <int D, typename OT, int S>
+template <int D, typename OT, int S, int kChunks>
 __global__ __launch_bounds__(S <= 4 ? 256 : 64 * S) void reduce_kernel(ReduceArgs a) {
   constexpr int LPR = D / 8;       // lanes per partial row (16-byte loads)
   constexpr int G = 64 / LPR;      // partial rows per wave load
-  constexpr int U = 8;             // partial rows in flight per lane
-  constexpr int kChunks = 8;       // (m, l) of up to 64 * kChunks partitions in registers
+  constexpr int U = kChunks == 1 ? 4 : 8;  // partial rows in flight per lane
+  // kChunks: (m, l) of up to 64 * kChunks partitions are held in registers
   constexpr int RPB = S == 1 ? 4 : 1;  // rows per workgroup
   __shared__ int lst_p[RPB][64 * kChunks];    // live partitions of the row, compacted
   __shared__ float lst_w[RPB][64 * kChunks];  // and their weights
@@ -221,30 +221,37 @@ __global__ __launch_bounds__(S <= 4 ? 256 : 64 * S) void reduce_kernel(ReduceArg
   }
 }
 
-template <int D, typename OT>
-hipError_t launch_d(const ReduceArgs& a, int64_t rows, hipStream_t stream) {
+template <int D, typename OT, int C>
+hipError_t launch_dc(const ReduceArgs& a, int64_t rows, hipStream_t stream) {
   // waves per row: the smallest S with rows * S >= 4096 waves, at most 16
   int S = 1;
   while (S < 16 && rows * S < 4096) S *= 2;
   switch (S) {
     case 1:
-      hipLaunchKernelGGL((reduce_kernel<D, OT, 1>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                         stream, a);
+      hipLaunchKernelGGL((reduce_kernel<D, OT, 1, C>), dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                         0, stream, a);
       break;
     case 2:
-      hipLaunchKernelGGL((reduce_kernel<D, OT, 2>), dim3((unsigned)rows), dim3(128), 0, stream, a);
+      hipLaunchKernelGGL((reduce_kernel<D, OT, 2, C>), dim3((unsigned)rows), dim3(128), 0, stream, a);
       break;
     case 4:
-      hipLaunchKernelGGL((reduce_kernel<D, OT, 4>), dim3((unsigned)rows), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((reduce_kernel<D, OT, 4, C>), dim3((unsigned)rows), dim3(256), 0, stream, a);
       break;
     case 8:
-      hipLaunchKernelGGL((reduce_kernel<D, OT, 8>), dim3((unsigned)rows), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((reduce_kernel<D, OT, 8, C>), dim3((unsigned)rows), dim3(512), 0, stream, a);
       break;
     default:
-      hipLaunchKernelGGL((reduce_kernel<D, OT, 16>), dim3((unsigned)rows), dim3(1024), 0, stream, a);
+      hipLaunchKernelGGL((reduce_kernel<D, OT, 16, C>), dim3((unsigned)rows), dim3(1024), 0, stream,
+                         a);
       break;
   }
   return hipGetLastError();
+}
+
+template <int D, typename OT>
+hipError_t launch_d(const ReduceArgs& a, int64_t rows, hipStream_t stream) {
+  // up to 64 partitions: one register chunk of statistics (fewer registers, more waves)
+  return a.P <= 64 ? launch_dc<D, OT, 1>(a, rows, stream) : launch_dc<D, OT, 8>(a, rows, stream);
 }
 
 }  // namespace
