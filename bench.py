@@ -241,7 +241,9 @@ def main():
     achieved = algo_bytes / (dom_avg * 1e-3) / 1e9
 
     res = {
-        "metric": METRIC if fam != "index" else "µs/index call + K-page GB/s (% of HBM peak)",
+        "metric": (METRIC if workload == "fp8_high" else
+                   "µs/index call + K-page GB/s (% of HBM peak)" if fam == "index" else
+                   "µs/decode step + KV-stream GB/s (% of HBM peak)"),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
