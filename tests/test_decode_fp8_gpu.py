@@ -242,3 +242,38 @@ def test_reduce_skips_empty_partitions(D, P):
     assert np.isfinite(got).all()
     assert np.all(got[2] == 0)
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_graph_replay_matches_eager(fmt):
+    """decode + reduce captured in a HIP graph (torch.cuda.graph on the current stream):
+    every one of several replays, with eager work and synchronisations in between, gives
+    the eager result bit for bit (no memset nodes; all state lives in the partials)."""
+    need_gpu()
+    if fmt == "fp8":
+        case = small(lens=(40, 700, 2049, 5000), seed=59, hk=2)
+    else:
+        case = synth.make_fp4_case("fp4_graph", 95, seq_lens=[300, 1000, 3000], num_kv_heads=2,
+                                   qg=8, head_dim=256, block_size=64, rotate=True, spare_blocks=3)
+    dev = device_case(case)
+    q = q_tensor(case)
+    P = 8
+    B, Hq, D = q.shape
+    partials = uq.alloc_partials(B, case.num_kv_heads, Hq // case.num_kv_heads, D, P)
+    out = torch.empty(B, Hq, D, dtype=q.dtype, device="cuda")
+    eager, _ = run_decode(case, P=P, dev=dev, q=q, partials=partials, out=out)
+    out.fill_(float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        uq.paged_attention(q, dev["cache"], dev["bt"], dev["sl"], kv_format=case.kv_format,
+                           max_seq_len=case.max_seq_len, num_partitions=P, partials=partials,
+                           out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"],
+                           v_scale=dev["vs"], rot_signs=dev["rot"])
+    for i in range(4):
+        out.fill_(float("nan"))
+        partials[0].fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, eager), f"replay {i}"
+        _ = (q.float() * 2).sum().item()      # eager work between replays
