@@ -143,9 +143,18 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // workgroup = (kv head h, sequence b, group grp), kv head fastest: workgroups that run
-  // together read neighbouring slots of the same tokens
-  const int64_t unit = blockIdx.x;
+  // workgroup = (kv head h, sequence b, group grp), kv head fastest.  The kv heads of one
+  // (sequence, group) share cache lines (a 272-byte slot is not line aligned), so they are
+  // placed on one XCD -- workgroups are dealt to the 8 XCDs round robin, so the heads go
+  // 8 apart in launch order -- and read the shared lines through one L2 (measured on
+  // MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 % faster).  A bijection when the
+  // workgroup count is a multiple of 8 Hk; otherwise the plain order is kept.
+  const int64_t unit0 = blockIdx.x;
+  int64_t unit = unit0;
+  if (((int64_t)a.B * a.Hk * a.runs) % (8 * a.Hk) == 0) {
+    const int64_t xc = unit0 % 8, j = unit0 / 8;
+    unit = ((j / a.Hk) * 8 + xc) * a.Hk + j % a.Hk;
+  }
   const int h = (int)(unit % a.Hk);
   const int b = (int)((unit / a.Hk) % a.B);
   const int grp = (int)(unit / ((int64_t)a.Hk * a.B));
