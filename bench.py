@@ -35,7 +35,9 @@ KERNEL_SRC = {"fp8": "decode_fp8.hip", "fp4": "decode_fp4.hip", "index": "index_
 
 
 def family(workload: str) -> str:
-    return "index" if workload.startswith("nvfp4_index") else workload.split("_")[0]
+    if workload.startswith("nvfp4_index"):
+        return "index"
+    return "fp4" if workload.startswith("fp4") else workload.split("_")[0]
 
 
 def source_hash(fam: str = "fp8") -> str:
@@ -111,11 +113,13 @@ def make_case(workload: str):
     if workload == "fp8_mid":
         return synth.fp8_mid(), ("fp8_mid: B=16 Hk=8 QG=8 D=128 L=16384 block=16 P=64 "
                                  "per-tensor e4m3 K/V, bf16 Q")
-    if workload.startswith("fp4_d256_qg"):
-        qg = int(workload[len("fp4_d256_qg"):])
-        return synth.fp4_d256(qg), (f"{workload}: B=4 Hk=2 QG={qg} D=256 L=75000 block=64 "
-                                    "P=512 e2m1 K/V with e4m3 group-of-32 scales, 272-byte "
-                                    "slot, rotated keys, bf16 Q")
+    if workload.startswith("fp4_d256_qg") or workload.startswith("fp4ue_d256_qg"):
+        ue = workload.startswith("fp4ue")
+        qg = int(workload.split("_qg")[1])
+        return synth.fp4_d256(qg, "ue8m0" if ue else "e4m3"), (
+            f"{workload}: B=4 Hk=2 QG={qg} D=256 L=75000 block=64 P=512 e2m1 K/V with "
+            f"{'UE8M0' if ue else 'e4m3'} group-of-32 scales, 272-byte slot, rotated keys, "
+            "bf16 Q")
     if workload.startswith("nvfp4_index_ql"):
         ql, h = workload[len("nvfp4_index_ql"):].split("_h")
         case = synth.nvfp4_index(int(ql), int(h))
@@ -130,7 +134,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_high",
-                    help="fp8_high (default), fp8_mid, fp4_d256_qg{6,8,16}, "
+                    help="fp8_high (default), fp8_mid, fp4_d256_qg{6,8,16}, fp4ue_d256_qg{6,8,16}, "
                          "nvfp4_index_ql{1,2,4,8}_h{1,2,4}")
     ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of a decode workload the CPU oracle baseline runs")

@@ -53,8 +53,8 @@ enum { UQ_F32 = 0, UQ_BF16 = 1 };
  *                         per 32 dims; element 2i is the low nibble of byte i ([P1] slot
  *                         layout: 0/128/136/264, 272 bytes at D=256).  Supported for
  *                         D = 256.
- *   UQ_KV_FP4_E2M1_UE8M0S same slot with UE8M0 scales 2^(byte-127) ([P1] STEP F scale
- *                         words).  Declared, not yet implemented: UQ_ERR_UNSUPPORTED. */
+ *   UQ_KV_FP4_E2M1_UE8M0S same slot with UE8M0 scales 2^(byte-127), byte 0 = 0.0 ([P1]
+ *                         STEP F scale words).  Supported for D = 256. */
 enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 };
 
 /* uq_paged_decode -- one decode step of paged attention, split over context partitions.
@@ -97,8 +97,8 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  * with uq_paged_reduce gives the attention output either way.  The fp8 kernel merges
  * the partitions of one workgroup (2 or 4); the fp4 kernel writes every partition.
  * With num_partitions = 1 part_* hold exactly the statistics above.
- * Supported: (UQ_KV_FP8_E4M3, D = 128, QG <= 8) and (UQ_KV_FP4_E2M1_E4M3S, D = 256,
- * QG <= 16); anything else returns UQ_ERR_UNSUPPORTED.
+ * Supported: (UQ_KV_FP8_E4M3, D = 128, QG <= 8) and (UQ_KV_FP4_E2M1_E4M3S or
+ * UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else returns UQ_ERR_UNSUPPORTED.
  * Device preconditions: 0 <= seq_lens[b] <= max_seq_len (larger values are clamped to
  * max_seq_len); block_table[b][t / block_size] in [0, num_blocks) for every t < L_b;
  * entries past a sequence's last block are never read; slot bytes of tokens t >= L_b are

@@ -62,8 +62,9 @@ __device__ __forceinline__ float e4m3_byte(uint32_t word, int byte_idx) {
 }
 
 struct Chunk {
-  i32x4 kc[2][2];   // K codes of tiles 0, 1: bytes [32 q, 32 q + 16), [32 q + 16, 32 q + 32)
-  uint32_t ksw[2];  // K scale word of tiles 0, 1
+  i32x4 kc[2][2];      // K codes of tiles 0, 1 (e4m3 scales: bytes [32q, +16), [32q + 16,
+                       // +16); UE8M0 scales: bytes [16q, +16) and [64 + 16q, +16))
+  uint32_t ksw[2][2];  // K scale words of tiles 0, 1 (UE8M0: all 8 scale bytes)
   i32x2 vc[8];      // V codes, dims 16 n .. 16 n + 15, of the 8 tokens of the PV k-slots
   uint32_t vsw[8];  // V scale word of those tokens
 };
@@ -98,14 +99,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const DecodeArgs& a,
                                            0x00020000);
 }
 
+template <bool UE>
 __device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, int ids,
                                             int blk_lo, int t0, int L, int h, int bs_shift) {
   Chunk c;
   LaneOffsets o;  // (recomputed per step: cheaper than keeping 10 registers live)
   {
     const uint32_t pos = (uint32_t)a.pos_stride;
-    o.k = n * pos + 32 * q;
-    o.ks = o.k - 32 * q + kKScales + 4 * (q >> 1);
+    // e4m3 scales: 64 consecutive dims per lane, dequantised before the MFMA; UE8M0: one
+    // 32-dim scale group per lane and 128-dim step, scaled inside the MFMA
+    o.k = n * pos + (UE ? 16 : 32) * q;
+    o.ks = n * pos + kKScales + (UE ? 0 : 4 * (q >> 1));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       o.v[e] = (4 * q + e) * pos + kVCodes + 8 * n;
@@ -114,12 +118,22 @@ __device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, i
   }
   const auto r0 = tile_rsrc(a, ids, blk_lo, t0, L, h, bs_shift);
   const auto r1 = tile_rsrc(a, ids, blk_lo, t0 + 16, L, h, bs_shift);
+  constexpr uint32_t k2 = UE ? 64 : 16;  // offset of the lane's second 16 code bytes
   c.kc[0][0] = __builtin_amdgcn_raw_buffer_load_b128(r0, o.k, 0, 0);
-  c.kc[0][1] = __builtin_amdgcn_raw_buffer_load_b128(r0, o.k + 16, 0, 0);
-  c.ksw[0] = __builtin_amdgcn_raw_buffer_load_b32(r0, o.ks, 0, 0);
+  c.kc[0][1] = __builtin_amdgcn_raw_buffer_load_b128(r0, o.k + k2, 0, 0);
   c.kc[1][0] = __builtin_amdgcn_raw_buffer_load_b128(r1, o.k, 0, 0);
-  c.kc[1][1] = __builtin_amdgcn_raw_buffer_load_b128(r1, o.k + 16, 0, 0);
-  c.ksw[1] = __builtin_amdgcn_raw_buffer_load_b32(r1, o.ks, 0, 0);
+  c.kc[1][1] = __builtin_amdgcn_raw_buffer_load_b128(r1, o.k + k2, 0, 0);
+  if constexpr (UE) {
+    const i32x2 s0 = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r0, o.ks, 0, 0));
+    const i32x2 s1 = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r1, o.ks, 0, 0));
+    c.ksw[0][0] = s0[0];
+    c.ksw[0][1] = s0[1];
+    c.ksw[1][0] = s1[0];
+    c.ksw[1][1] = s1[1];
+  } else {
+    c.ksw[0][0] = __builtin_amdgcn_raw_buffer_load_b32(r0, o.ks, 0, 0);
+    c.ksw[1][0] = __builtin_amdgcn_raw_buffer_load_b32(r1, o.ks, 0, 0);
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     c.vc[e] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(r0, o.v[e], 0, 0));
@@ -130,7 +144,7 @@ __device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, i
   return c;
 }
 
-template <typename QT>
+template <typename QT, bool UE>
 __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   // Rotated query (f16, row stride kD + 8 halves) during the stream; the four waves'
   // scaled accumulators in the merge (reused after a barrier).
@@ -139,7 +153,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   __shared__ float lds_m[kW][16];
   __shared__ float lds_l[kW][16];
   _Float16* lds_q = reinterpret_cast<_Float16*>(&lds_acc[0][0][0]);
-  constexpr int kQStride = kD + 8;
+  constexpr int kQStride = kD + 8;        // f16 query row (halves)
+  constexpr int kQBStride = 2 * kD + 16;  // e4m3 hi row then lo row (bytes)
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -225,7 +240,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
     const int k = c >> 1;
     if (k >= kw + win_tgs) load_ids(k);
     const int sk = s_of(k);
-    dst = load_chunk(a, n, q, ids, (sk >> bs_shift) - (k - kw) * bpw, step_t0(c), L, h, bs_shift);
+    dst = load_chunk<UE>(a, n, q, ids, (sk >> bs_shift) - (k - kw) * bpw, step_t0(c), L, h,
+                         bs_shift);
   };
   Chunk cA, cB;
   if (step_ok(0)) load_step(0, cA);
@@ -298,29 +314,58 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
     for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    // 2^sh puts amax in [2^14, 2^15)
-    int sh = 0;
-    if (amax > 0.f) {
-      const int E = (int)((f_bits(amax) >> 23) & 0xFF) - 127;  // amax in [2^E, 2^(E+1))
-      sh = 14 - (E < -126 ? -126 : E);
-      sh = sh > 126 ? 126 : sh;
-    }
-    const float up = __builtin_ldexpf(1.f, sh);
-    uint32_t w[8];
+    if constexpr (!UE) {
+      // f16: 2^sh puts amax in [2^14, 2^15)
+      int sh = 0;
+      if (amax > 0.f) {
+        const int E = (int)((f_bits(amax) >> 23) & 0xFF) - 127;  // amax in [2^E, 2^(E+1))
+        sh = 14 - (E < -126 ? -126 : E);
+        sh = sh > 126 ? 126 : sh;
+      }
+      const float up = __builtin_ldexpf(1.f, sh);
+      uint32_t w[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const f16x2 hv = f16x2{(_Float16)(x[2 * e] * up), (_Float16)(x[2 * e + 1] * up)};
-      w[e] = __builtin_bit_cast(uint32_t, hv);
+      for (int e = 0; e < 8; ++e) {
+        const f16x2 hv = f16x2{(_Float16)(x[2 * e] * up), (_Float16)(x[2 * e + 1] * up)};
+        w[e] = __builtin_bit_cast(uint32_t, hv);
+      }
+      uint8_t* dst = reinterpret_cast<uint8_t*>(lds_q + row * kQStride + 16 * c);
+      *reinterpret_cast<i32x4*>(dst) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      *reinterpret_cast<i32x4*>(dst + 16) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+      if (c == 0) lds_fac[row] = a.softmax_scale * kLog2e * __builtin_ldexpf(1.f, -sh);
+    } else {
+      // e4m3 hi + lo pair of q' s_q, s_q = 2^(7 - E) putting amax in [64, 128): the pair
+      // carries about 8 significant bits (the scaled MFMA takes fp8 for the query)
+      int E = 0;
+      if (amax > 0.f) {
+        E = (int)((f_bits(amax) >> 23) & 0xFF) - 126;  // amax in [2^(E-1), 2^E)
+        E = E < -100 ? -100 : (E > 100 ? 100 : E);
+      }
+      const float s_q = __builtin_ldexpf(1.f, 7 - E);
+      int hw[4], lw[4];
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        const float y0 = x[4 * w4] * s_q, y1 = x[4 * w4 + 1] * s_q;
+        const float y2 = x[4 * w4 + 2] * s_q, y3 = x[4 * w4 + 3] * s_q;
+        int hv = cvt_pk_e4m3<false>(y0, y1, 0);
+        hv = cvt_pk_e4m3<true>(y2, y3, hv);
+        int lv = cvt_pk_e4m3<false>(y0 - e4m3_to_f<0>(hv), y1 - e4m3_to_f<1>(hv), 0);
+        lv = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hv), y3 - e4m3_to_f<3>(hv), lv);
+        hw[w4] = hv;
+        lw[w4] = lv;
+      }
+      uint8_t* dst = reinterpret_cast<uint8_t*>(lds_q) + row * kQBStride + 16 * c;
+      *reinterpret_cast<i32x4*>(dst) = i32x4{hw[0], hw[1], hw[2], hw[3]};
+      *reinterpret_cast<i32x4*>(dst + kD) = i32x4{lw[0], lw[1], lw[2], lw[3]};
+      if (c == 0) lds_fac[row] = a.softmax_scale * kLog2e / s_q;
     }
-    uint8_t* dst = reinterpret_cast<uint8_t*>(lds_q + row * kQStride + 16 * c);
-    *reinterpret_cast<i32x4*>(dst) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    *reinterpret_cast<i32x4*>(dst + 16) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    if (c == 0) lds_fac[row] = a.softmax_scale * kLog2e * __builtin_ldexpf(1.f, -sh);
   }
   __syncthreads();
 
-  // B operand of QK (head n, dims 64 q + 8 kk .. + 8) is read from LDS at each use
+  // B operand of QK is read from LDS at each use: f16 head n, dims 64 q + 8 kk .. + 8
+  // (e4m3 scales), or e4m3 hi/lo bytes of head n from dim 16 q on (UE8M0 scales)
   const _Float16* qrow = lds_q + n * kQStride + 64 * q;
+  const uint8_t* qbrow = reinterpret_cast<const uint8_t*>(lds_q) + n * kQBStride + 16 * q;
   const float fac = lds_fac[n];
 
   float m_run = -INFINITY;  // reference of head n (exp2 units); acc/l are relative to it
@@ -340,17 +385,39 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
       f32x4 s[2];
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
-        const f16x2 s0 = splat_h(e4m3_byte(ksw[T], 2 * (q & 1)));
-        const f16x2 s1 = splat_h(e4m3_byte(ksw[T], 2 * (q & 1) + 1));
         f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!UE) {
+          const f16x2 s0 = splat_h(e4m3_byte(ksw[T][0], 2 * (q & 1)));
+          const f16x2 s1 = splat_h(e4m3_byte(ksw[T][0], 2 * (q & 1) + 1));
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const uint32_t wd = (uint32_t)kc[T][kk >> 2][kk & 3];
-          const f16x2 sc = kk < 4 ? s0 : s1;
-          const f16x8 A = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc,
-                               fp4_pair<2>(wd) * sc, fp4_pair<3>(wd) * sc);
-          const f16x8 qb = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
-          c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb, c4, 0, 0, 0);
+          for (int kk = 0; kk < 8; ++kk) {
+            const uint32_t wd = (uint32_t)kc[T][kk >> 2][kk & 3];
+            const f16x2 sc = kk < 4 ? s0 : s1;
+            const f16x8 A = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc,
+                                 fp4_pair<2>(wd) * sc, fp4_pair<3>(wd) * sc);
+            const f16x8 qb = *reinterpret_cast<const f16x8*>(qrow + 8 * kk);
+            c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb, c4, 0, 0, 0);
+          }
+        } else {
+          // scaled fp4 x fp8 MFMA per 128-dim step s: A = this lane's 32 K codes (its
+          // 32-dim group 4s + q of token n) with that group's UE8M0 byte as the block
+          // scale; B = the query's e4m3 hi, then lo, in the matching k order (bytes
+          // [16q, +16) and [64 + 16q, +16) of the step's 128 dims)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int scale = (int)((ksw[T][st] >> (8 * q)) & 0xFFu);
+            const i32x4 kv = kc[T][st];
+            const i32x8 A = {kv[0], kv[1], kv[2], kv[3], 0, 0, 0, 0};
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {  // hi, lo
+              const uint8_t* qb = qbrow + part * kD + 128 * st;
+              const i32x4 b0 = *reinterpret_cast<const i32x4*>(qb);
+              const i32x4 b1 = *reinterpret_cast<const i32x4*>(qb + 64);
+              const i32x8 Bq = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+              c4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bq, c4, 4, 0, 0, scale, 0,
+                                                                     127);
+            }
+          }
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -390,6 +457,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
                              (_Float16)pv[4], (_Float16)pv[5], (_Float16)pv[6], (_Float16)pv[7]};
 
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!UE) {
       // ---- PV.  Token pair u = (2u, 2u+1); X / Y hold per byte the even / odd dim of the
       //      byte's position for both tokens (low nibble: token 2u).
       f16x2 vs[4];
@@ -427,6 +495,62 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         UQ_PV_BYTE(3)
         __builtin_amdgcn_sched_barrier(0);
 #undef UQ_PV_BYTE
+      }
+      } else {
+        // ---- PV in bf16 (a UE8M0 scale can leave the f16 range).  Each token's bytes are
+        //      converted with its own power-of-two scale (exactly the operand of
+        //      v_cvt_scalef32_pk_bf16_fp4; a scale byte of 0 gives 0), then v_perm pairs
+        //      tokens 2u, 2u+1 per B register.
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, i32x4{(int)pack_bf16x2(pv[0], pv[1]), (int)pack_bf16x2(pv[2], pv[3]),
+                          (int)pack_bf16x2(pv[4], pv[5]), (int)pack_bf16x2(pv[6], pv[7])});
+        float vsc[8];
+        uint32_t vcw[8][2];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t eb = (vsw[e] >> (8 * ((n >> 1) & 3))) & 0xFFu;
+          vsc[e] = bits_f(eb << 23);
+          vcw[e][0] = eb ? (uint32_t)vc[e][0] : 0u;
+          vcw[e][1] = eb ? (uint32_t)vc[e][1] : 0u;
+        }
+#define UQ_PV_BF(HH, KB)                                                                      \
+  {                                                                                           \
+    uint32_t cv[8];                                                                           \
+    _Pragma("unroll") for (int e = 0; e < 8; ++e) cv[e] = __builtin_bit_cast(                 \
+        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vcw[e][HH], vsc[e], KB));         \
+    const bf16x8 bx = __builtin_bit_cast(                                                     \
+        bf16x8, i32x4{(int)__builtin_amdgcn_perm(cv[1], cv[0], 0x05040100u),                   \
+                      (int)__builtin_amdgcn_perm(cv[3], cv[2], 0x05040100u),                   \
+                      (int)__builtin_amdgcn_perm(cv[5], cv[4], 0x05040100u),                   \
+                      (int)__builtin_amdgcn_perm(cv[7], cv[6], 0x05040100u)});                 \
+    const bf16x8 by = __builtin_bit_cast(                                                     \
+        bf16x8, i32x4{(int)__builtin_amdgcn_perm(cv[1], cv[0], 0x07060302u),                   \
+                      (int)__builtin_amdgcn_perm(cv[3], cv[2], 0x07060302u),                   \
+                      (int)__builtin_amdgcn_perm(cv[5], cv[4], 0x07060302u),                   \
+                      (int)__builtin_amdgcn_perm(cv[7], cv[6], 0x07060302u)});                 \
+    acc[8 * HH + 2 * KB] =                                                                    \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, bx, acc[8 * HH + 2 * KB], 0, 0, 0);       \
+    acc[8 * HH + 2 * KB + 1] =                                                                \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, by, acc[8 * HH + 2 * KB + 1], 0, 0, 0);   \
+  }
+        UQ_PV_BF(0, 0)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(0, 1)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(0, 2)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(0, 3)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(1, 0)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(1, 1)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(1, 2)
+        __builtin_amdgcn_sched_barrier(0);
+        UQ_PV_BF(1, 3)
+        __builtin_amdgcn_sched_barrier(0);
+#undef UQ_PV_BF
       }
   };
   // two step buffers, alternating: the next step's loads are issued before this step
@@ -515,15 +639,22 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, hipStream_t stream) {
+hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, bool ue8m0, hipStream_t stream) {
   const int64_t units = (int64_t)a.B * a.Hk * a.runs;  // runs: workgroups per (b, h)
   if (units <= 0) return hipSuccess;
   if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)units), block(64 * kW);
-  if (q_is_f32)
-    hipLaunchKernelGGL(decode_fp4_kernel<float>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_fp4_kernel<uint16_t>, grid, block, 0, stream, a);
+  if (ue8m0) {
+    if (q_is_f32)
+      hipLaunchKernelGGL((decode_fp4_kernel<float, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_fp4_kernel<uint16_t, true>), grid, block, 0, stream, a);
+  } else {
+    if (q_is_f32)
+      hipLaunchKernelGGL((decode_fp4_kernel<float, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_fp4_kernel<uint16_t, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -154,7 +154,7 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
     return launch_status(uq::launch_decode_fp8(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
                          "decode_fp8");
   }
-  if (kv_format == UQ_KV_FP4_E2M1_E4M3S) {
+  if (kv_format == UQ_KV_FP4_E2M1_E4M3S || kv_format == UQ_KV_FP4_E2M1_UE8M0S) {
     if (head_dim != 256) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports head_dim 256 only");
     if (k_scale || v_scale) return fail(UQ_ERR_INVALID_ARG, "per-tensor scales apply to fp8 caches only");
     if (reinterpret_cast<uintptr_t>(rot_signs) & 15)
@@ -170,7 +170,8 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
       a.run_len = work >= 3 * 2 * 256 ? 3 : (work >= 2 * 2 * 256 ? 2 : 1);
       a.runs = (pmax + a.run_len - 1) / a.run_len;
     }
-    return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
+    return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, kv_format == UQ_KV_FP4_E2M1_UE8M0S,
+                                               static_cast<hipStream_t>(stream)),
                          "decode_fp4");
   }
   return fail(UQ_ERR_UNSUPPORTED, "kv_format %d is not implemented", kv_format);

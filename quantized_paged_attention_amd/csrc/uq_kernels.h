@@ -55,7 +55,7 @@ struct IndexArgs {
 
 // Each returns the hipError_t of its launch.
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t stream);
-hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, hipStream_t stream);
+hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, bool ue8m0, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, bool out_is_f32, hipStream_t stream);
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream);
 

@@ -276,10 +276,11 @@ def fp8_high() -> DecodeCase:
                          max_blocks=1024)
 
 
-def fp4_d256(qg=16) -> DecodeCase:
-    return make_fp4_case(f"fp4_d256_qg{qg}", 4, seq_lens=[75000] * 4, num_kv_heads=2, qg=qg,
+def fp4_d256(qg=16, scale_kind="e4m3") -> DecodeCase:
+    tag = "" if scale_kind == "e4m3" else "_ue8m0"
+    return make_fp4_case(f"fp4_d256_qg{qg}{tag}", 4, seq_lens=[75000] * 4, num_kv_heads=2, qg=qg,
                          head_dim=256, block_size=64, num_partitions=512,
-                         softmax_scale=1.0 / 16.0)
+                         softmax_scale=1.0 / 16.0, scale_kind=scale_kind)
 
 
 # ------------------------------------------------------------------ index workloads

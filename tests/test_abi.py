@@ -65,7 +65,7 @@ def decode_args(**over):
     (dict(D=64, slot=128), uq.UQ_ERR_UNSUPPORTED),        # fp8 supports D=128 only
     (dict(Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),             # fp8 QG up to 8
     (dict(rot=FAKE), uq.UQ_ERR_UNSUPPORTED),              # rotation needs an fp4 cache
-    (dict(fmt=uq.UQ_KV_FP4_E2M1_UE8M0S, D=256, slot=272, Hq=8 * 8), uq.UQ_ERR_UNSUPPORTED),
+    (dict(fmt=uq.UQ_KV_FP4_E2M1_UE8M0S, D=128, slot=144, Hq=8 * 8), uq.UQ_ERR_UNSUPPORTED),
     (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=128, slot=144, Hq=8 * 4), uq.UQ_ERR_UNSUPPORTED),
     (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 8, rot=FAKE + 8),
      uq.UQ_ERR_INVALID_ARG),                              # rotation signs not 16-byte aligned
