@@ -10,7 +10,8 @@
 // Layout of the work: a 16-byte load covers 8 dims of one partial row, so one wave load
 // reads 64 / (D / 8) whole partial rows (4 at D = 128, 2 at D = 256).  A row's partitions
 // are shared by S waves of one workgroup (S chosen on the host so that there are enough
-// waves to fill the chip when there are few rows and many partitions).  All (m, l) of a
+// waves to fill the chip when there are few rows and many partitions, while every wave
+// keeps at least 64 of the partitions a row can have).  All (m, l) of a
 // row are loaded at once (up to 512 partitions in registers), M and the denominator are
 // reduced across the wave, the partitions with l > 0 are compacted into an LDS list
 // (ballot + mbcnt), and the waves stream only those partial rows, 8 per lane in flight;
@@ -223,9 +224,14 @@ __global__ __launch_bounds__(S <= 4 ? 256 : 64 * S) void reduce_kernel(ReduceArg
 
 template <int D, typename OT, int C>
 hipError_t launch_dc(const ReduceArgs& a, int64_t rows, hipStream_t stream) {
-  // waves per row: the smallest S with rows * S >= 4096 waves, at most 16
+  // waves per row: the smallest S with rows * S >= 4096 waves, at most 16, and at least 64
+  // partitions a row can have per wave (measured on MI355X: with 128 rows of 293
+  // partitions, 4 waves per row take 8.5 us, 16 take 11.6 us; the cross-wave merge costs
+  // more than the split gains once a wave has few partial rows)
+  int64_t parts = ((int64_t)a.max_seq_len + 255) / 256;
+  if (parts > a.P) parts = a.P;
   int S = 1;
-  while (S < 16 && rows * S < 4096) S *= 2;
+  while (S < 16 && rows * S < 4096 && parts >= 128 * S) S *= 2;
   switch (S) {
     case 1:
       hipLaunchKernelGGL((reduce_kernel<D, OT, 1, C>), dim3((unsigned)((rows + 3) / 4)), dim3(256),

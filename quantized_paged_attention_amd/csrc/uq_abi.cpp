@@ -33,6 +33,20 @@ int launch_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Compute units of the current device (queried once per device; 256 on MI355X).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 bool valid_block_size(int bs) {
   return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
 }
@@ -161,13 +175,26 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
       return fail(UQ_ERR_INVALID_ARG, "rot_signs must be 16-byte aligned");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache needs slot_bytes a multiple of 16");
     if (num_seqs == 0) return ok();
-    // one workgroup streams a run of partitions (one query rotation, one merged partial).
-    // Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions): runs of 3 or 4 beat 2
-    // (59 / 62 us) and 1 (78 us); runs of 3 once there are 2 of them per compute unit.
+    // One workgroup streams a run of R partitions (one query rotation, one merged
+    // partial).  Two workgroups fit a compute unit, and the time goes as (rounds of
+    // resident workgroups) x (R + about one partition of fixed cost per workgroup:
+    // rotation, start-up, merge), so R in [1, 8] minimises ceil(groups / slots) * (R + 1)
+    // (ties: the shorter run).  Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions,
+    // 512 slots): R = 5 (470 groups, one round) 48 us; R = 1, 3, 4, 6: 78, 56, 54, 51 us.
     if (a.TGPP == 1) {
       const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
-      const int64_t work = (int64_t)num_seqs * num_kv_heads * pmax;
-      a.run_len = work >= 3 * 2 * 256 ? 3 : (work >= 2 * 2 * 256 ? 2 : 1);
+      const int64_t slots = 2LL * device_cus();
+      int best_r = 1;
+      int64_t best_cost = -1;
+      for (int r = 1; r <= 8; ++r) {
+        const int64_t groups = (int64_t)num_seqs * num_kv_heads * ((pmax + r - 1) / r);
+        const int64_t cost = (groups + slots - 1) / slots * (r + 1);
+        if (best_cost < 0 || cost < best_cost) {
+          best_cost = cost;
+          best_r = r;
+        }
+      }
+      a.run_len = best_r;
       a.runs = (pmax + a.run_len - 1) / a.run_len;
     }
     return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, kv_format == UQ_KV_FP4_E2M1_UE8M0S,

@@ -175,3 +175,18 @@ def test_ue8m0_one_hot_gather_bit_exact():
         _, v = dense_kv(c, 0, 0)
         for g in range(8):
             assert np.array_equal(got[0, g], v[tstar]), (tstar, g)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_runs_ragged_batch(kind):
+    """B=16 ragged lengths up to 40000 with 160 partitions: the launcher streams runs of
+    several partitions per workgroup (five here), merged into one partial; lengths end a
+    sequence at every position of a run."""
+    need_gpu()
+    rng = np.random.default_rng(97)
+    lens = rng.integers(1, 40001, size=16)
+    lens[:6] = [1, 256, 257, 5 * 256, 5 * 256 + 1, 40000]
+    case = small(lens=tuple(int(x) for x in lens), hk=2, qg=8, seed=97, kind=kind)
+    log(f"case fp4 runs ragged scales={kind}")
+    got, _ = run_decode(case, P=160)
+    assert_decode_close(got, oracle_decode(case), f"fp4 runs ragged {kind}")

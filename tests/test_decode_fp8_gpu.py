@@ -211,12 +211,14 @@ def test_partition_runs_ragged_batch(B, run):
 
 
 @pytest.mark.parametrize("D", [128, 256])
-@pytest.mark.parametrize("P", [40, 700])
+@pytest.mark.parametrize("P", [40, 130, 300, 700, 2100])
 def test_reduce_skips_empty_partitions(D, P):
     """Synthetic partials with some partitions empty (l = 0, m = -inf) whose partial rows
-    hold NaN: the reduce must not read them into the sum.  P = 700 exceeds the partitions
-    the reduce keeps in registers (its batched path).  Reference: the oracle's reduce on
-    the same statistics with those rows zeroed (an empty partition's o is 0 there)."""
+    hold NaN: the reduce must not read them into the sum.  With 24 rows the launcher splits
+    a row over 1, 2, 4, 8 and 16 waves for these P (at least 64 partitions per wave); P = 700
+    and 2100 exceed the partitions the reduce keeps in registers (its batched path).
+    Reference: the oracle's reduce on the same statistics with those rows zeroed (an empty
+    partition's o is 0 there)."""
     need_gpu()
     from oracle import oracle
     rng = np.random.default_rng(58 + P + D)
