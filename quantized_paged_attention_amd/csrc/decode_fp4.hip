@@ -162,14 +162,12 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   // (sequence, group) share cache lines (a 272-byte slot is not line aligned), so they are
   // placed on one XCD -- workgroups are dealt to the 8 XCDs round robin, so the heads go
   // 8 apart in launch order -- and read the shared lines through one L2 (measured on
-  // MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 % faster).  A bijection when the
-  // workgroup count is a multiple of 8 Hk; otherwise the plain order is kept.
+  // MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 % faster).  The grid is padded to
+  // a multiple of 8 Hk, which makes the map a bijection; the padding workgroups exit here.
   const int64_t unit0 = blockIdx.x;
-  int64_t unit = unit0;
-  if (((int64_t)a.B * a.Hk * a.runs) % (8 * a.Hk) == 0) {
-    const int64_t xc = unit0 % 8, j = unit0 / 8;
-    unit = ((j / a.Hk) * 8 + xc) * a.Hk + j % a.Hk;
-  }
+  const int64_t xc = unit0 % 8, j = unit0 / 8;
+  const int64_t unit = ((j / a.Hk) * 8 + xc) * a.Hk + j % a.Hk;
+  if (unit >= (int64_t)a.B * a.Hk * a.runs) return;  // workgroup-uniform, before any barrier
   const int h = (int)(unit % a.Hk);
   const int b = (int)((unit / a.Hk) % a.B);
   const int grp = (int)(unit / ((int64_t)a.Hk * a.B));
@@ -642,8 +640,11 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, bool ue8m0, hipStream_t stream) {
   const int64_t units = (int64_t)a.B * a.Hk * a.runs;  // runs: workgroups per (b, h)
   if (units <= 0) return hipSuccess;
-  if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)units), block(64 * kW);
+  // padded to a multiple of 8 Hk for the XCD placement of the kv heads (see the kernel)
+  const int64_t pad = 8 * (int64_t)a.Hk;
+  const int64_t wgs = (units + pad - 1) / pad * pad;
+  if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)wgs), block(64 * kW);
   if (ue8m0) {
     if (q_is_f32)
       hipLaunchKernelGGL((decode_fp4_kernel<float, true>), grid, block, 0, stream, a);
