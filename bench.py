@@ -6,7 +6,10 @@ partitions of 256 tokens, per-tensor e4m3 K/V).  Other workloads (--workload):
 fp8_mid (B=16, L=16384), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions,
 e2m1 + e4m3 group scales, in-kernel rotation), nvfp4_index_ql{QL}_h{H} (32 requests,
 L ~ U[1024, 32768]: one uq_index_score call is a step).  Inputs are generated once,
-copied to HBM, and are resident before the timed region starts.
+copied to HBM, and are resident before the timed region starts.  The KV cache (or the
+index pages) is held in as many copies as make at least 1 GiB, and step i reads copy
+i mod n: no step finds its bytes in L2 or the 256 MB MALL left there by the step before,
+as after a >= 1 GiB cache flush, while the timed steps still run back to back.
 
 Prints ONE JSON line: value = effective KV-stream GB/s (algorithmic bytes of every visible
 (token, head) / step wall time), with the dominant kernel's roofline (HIP events on the
@@ -27,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 1 << 30   # KV bytes cycled through before a copy is read again
 METRIC = "µs/decode step + KV-stream GB/s (% of HBM peak) at B=128 ctx=16k"
 CSRC = os.path.join(ROOT, "quantized_paged_attention_amd", "csrc")
 COMMON_SRCS = ("uq_device.h", "uq_kernels.h", "uq_abi.cpp")
@@ -105,6 +109,11 @@ def cpu_baseline_index(case, min_seconds: float = 10.0):
                       f"pages) x {passes} passes, fp64, {dt:.2f} s wall"}
 
 
+def copies_for(nbytes: int) -> int:
+    """Copies of an nbytes input that together stream at least COLD_BYTES."""
+    return max(1, -(-COLD_BYTES // max(1, nbytes)))
+
+
 def make_case(workload: str):
     from quantized_paged_attention_amd import synth
     if workload == "fp8_high":
@@ -174,12 +183,13 @@ def main():
 
     if fam == "index":
         q = torch.from_numpy(case.q).to(dev)
-        pages = torch.from_numpy(case.pages).to(dev)
+        pages0 = torch.from_numpy(case.pages).to(dev)
+        inputs = [pages0] + [pages0.clone() for _ in range(copies_for(pages0.nbytes) - 1)]
         bt = torch.from_numpy(case.block_table).to(dev)
         sl = torch.from_numpy(case.seq_lens).to(dev)
         scores = torch.from_numpy(case.scores_init().copy()).to(dev)
 
-        def kernels():
+        def kernels(pages):
             uq.index_score(q, pages, bt, sl, scores, query_len=case.query_len, stream=stream)
         algo_bytes = case.page_bytes()
         names = ("index_score",)
@@ -188,7 +198,8 @@ def main():
         B, Hq, D, hk, P = case.B, case.Hq, case.D, case.num_kv_heads, case.num_partitions
         qdt = torch.float32 if case.q_dtype == "f32" else torch.bfloat16
         q = torch.from_numpy(case.q).to(qdt).to(dev)
-        cache = torch.from_numpy(case.cache).to(dev)
+        cache0 = torch.from_numpy(case.cache).to(dev)
+        inputs = [cache0] + [cache0.clone() for _ in range(copies_for(cache0.nbytes) - 1)]
         bt = torch.from_numpy(case.block_table).to(dev)
         sl = torch.from_numpy(case.seq_lens).to(dev)
         is_fp8 = fam == "fp8"
@@ -199,7 +210,7 @@ def main():
         out = torch.empty(B, Hq, D, dtype=qdt, device=dev)
         max_len = case.max_seq_len
 
-        def decode():
+        def decode(cache):
             uq.paged_decode(q, cache, bt, sl, kv_format=case.kv_format, max_seq_len=max_len,
                             num_partitions=P, part_out=po, part_max=pm, part_sum=pl,
                             softmax_scale=case.softmax_scale, k_scale=ks, v_scale=vs,
@@ -208,15 +219,16 @@ def main():
         def reduce():
             uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, stream=stream)
 
-        def kernels():
-            decode()
+        def kernels(cache):
+            decode(cache)
             reduce()
         algo_bytes = case.kv_bytes()
         names = (f"decode_{fam}", "reduce")
         dtype = "fp8" if is_fp8 else "f16"
 
-    for _ in range(args.warmup):
-        kernels()
+    n_in = len(inputs)
+    for i in range(args.warmup):
+        kernels(inputs[i % n_in])
     torch.cuda.synchronize()
 
     # per step: an event before the step, then one after each kernel
@@ -228,10 +240,10 @@ def main():
     for i in range(K):
         ev[i][0].record(stream)
         if fam == "index":
-            kernels()
+            kernels(inputs[i % n_in])
             ev[i][1].record(stream)
         else:
-            decode()
+            decode(inputs[i % n_in])
             ev[i][1].record(stream)
             reduce()
             ev[i][2].record(stream)
@@ -261,7 +273,8 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": desc, "algorithmic_bytes": algo_bytes},
+        "config": {"workload": desc, "algorithmic_bytes": algo_bytes,
+                   "input_copies_cycled": n_in},
         "kernels_us": {f"{nm}_avg": round(float(k_ms[j].mean()) * 1e3, 2)
                        for j, nm in enumerate(names)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

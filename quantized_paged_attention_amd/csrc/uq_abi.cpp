@@ -180,7 +180,8 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
     // resident workgroups) x (R + about one partition of fixed cost per workgroup:
     // rotation, start-up, merge), so R in [1, 8] minimises ceil(groups / slots) * (R + 1)
     // (ties: the shorter run).  Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions,
-    // 512 slots): R = 5 (470 groups, one round) 48 us; R = 1, 3, 4, 6: 78, 56, 54, 51 us.
+    // 512 slots, 20 launches back to back): R = 5 (472 groups, one round) 38.6 us;
+    // R = 3, 4, 6, 8: 51.7, 48.9, 42.3, 50.9 us.
     if (a.TGPP == 1) {
       const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
       const int64_t slots = 2LL * device_cus();
