@@ -69,8 +69,13 @@ def _load():
         lib.uqo_decode.restype = i32
         lib.uqo_decode.argtypes = [P, i64, i64, P, i64, i32, i32, i32, i32, f64, f64, P,
                                    P, i32, P, i32, i32, i32, f64, P, i32, P, P, P]
+        lib.uqo_decode_q.restype = i32
+        lib.uqo_decode_q.argtypes = [P, i64, i64, P, i64, i32, i32, i32, i32, f64, f64, P,
+                                     P, i32, P, i32, i32, i32, i32, f64, P, i32, P, P, P]
         lib.uqo_reduce.restype = None
         lib.uqo_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P]
+        lib.uqo_reduce_q.restype = None
+        lib.uqo_reduce_q.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
         lib.uqo_index_score.restype = i32
         lib.uqo_index_score.argtypes = [P, i64, i64, P, i64, i64, P, i32, P, i32, i32, i32,
                                         i32, P, i64, i64]
@@ -125,33 +130,36 @@ def rotate(q: np.ndarray, signs: np.ndarray) -> np.ndarray:
 def decode(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
            *, num_kv_heads: int, kv_format: int, softmax_scale: float,
            k_scale: float = 1.0, v_scale: float = 1.0, rot_signs: np.ndarray | None = None,
-           num_partitions: int = 0):
-    """Masked-softmax decode attention in fp64.
+           num_partitions: int = 0, query_len: int = 1):
+    """Masked-softmax decode attention in fp64, query_len query rows per sequence.
 
-    q: [B, Hq, D] (any float dtype; widened exactly), cache: [num_blocks, BS, Hk, slot]
-    uint8, block_table: [B, max_blocks] int32, seq_lens: [B] int32.
-    Returns out [B, Hq, D] float64, and (part_m, part_l, part_o) when num_partitions > 0
-    (shapes [B, Hk, P, QG], [B, Hk, P, QG], [B, Hk, P, QG, D]).
+    q: [B*QL, Hq, D] (any float dtype; widened exactly; row b*QL + j is query j of sequence
+    b, which sees tokens t < L_b - QL + 1 + j), cache: [num_blocks, BS, Hk, slot] uint8,
+    block_table: [B, max_blocks] int32, seq_lens: [B] int32.
+    Returns out [B*QL, Hq, D] float64, and (part_m, part_l, part_o) when num_partitions > 0
+    (shapes [B, Hk, P, QL*QG], [B, Hk, P, QL*QG], [B, Hk, P, QL*QG, D]; row j*QG + g).
     """
     q = _c(q, np.float64)
-    B, Hq, D = q.shape
+    rows, Hq, D = q.shape
+    QL = int(query_len)
     cache = np.ascontiguousarray(cache, dtype=np.uint8)
     nb, bs, hk, slot = cache.shape
     assert hk == num_kv_heads
     bt = _c(block_table, np.int32)
     sl = _c(seq_lens, np.int32)
-    assert bt.shape[0] == B and sl.shape == (B,)
+    B = sl.shape[0]
+    assert QL >= 1 and rows == B * QL and bt.shape[0] == B
     QG = Hq // hk
     P = int(num_partitions)
-    out = np.zeros((B, Hq, D), np.float64)
-    pm = np.zeros((B, hk, max(P, 1), QG), np.float64)
+    out = np.zeros((B * QL, Hq, D), np.float64)
+    pm = np.zeros((B, hk, max(P, 1), QL * QG), np.float64)
     pl = np.zeros_like(pm)
-    po = np.zeros((B, hk, max(P, 1), QG, D), np.float64)
+    po = np.zeros((B, hk, max(P, 1), QL * QG, D), np.float64)
     rot = None if rot_signs is None else _c(rot_signs, np.int8)
-    st = _load().uqo_decode(_ptr(q), Hq * D, D, _ptr(cache), nb, bs, hk, slot, kv_format,
-                            float(k_scale), float(v_scale), _ptr(rot), _ptr(bt), bt.shape[1],
-                            _ptr(sl), B, Hq, D, float(softmax_scale), _ptr(out), P, _ptr(pm),
-                            _ptr(pl), _ptr(po))
+    st = _load().uqo_decode_q(_ptr(q), Hq * D, D, _ptr(cache), nb, bs, hk, slot, kv_format,
+                              float(k_scale), float(v_scale), _ptr(rot), _ptr(bt), bt.shape[1],
+                              _ptr(sl), B, QL, Hq, D, float(softmax_scale), _ptr(out), P,
+                              _ptr(pm), _ptr(pl), _ptr(po))
     if st != 0:
         raise ValueError(f"oracle decode rejected its inputs (status {st})")
     if P > 0:
@@ -160,15 +168,20 @@ def decode(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray, seq_lens: 
 
 
 def reduce(part_o: np.ndarray, part_m: np.ndarray, part_l: np.ndarray,
-           seq_lens: np.ndarray) -> np.ndarray:
-    """Flash-combine of partials [B, Hk, P, QG(, D)] into [B, Hk*QG, D] (fp64)."""
+           seq_lens: np.ndarray, query_len: int = 1) -> np.ndarray:
+    """Flash-combine of partials [B, Hk, P, QL*QG(, D)] (row j*QG + g) into
+    [B*QL, Hk*QG, D] (fp64)."""
     po = _c(part_o, np.float64)
     pm = _c(part_m, np.float64)
     pl = _c(part_l, np.float64)
     sl = _c(seq_lens, np.int32)
-    B, Hk, P, QG, D = po.shape
-    out = np.zeros((B, Hk * QG, D), np.float64)
-    _load().uqo_reduce(_ptr(po), _ptr(pm), _ptr(pl), _ptr(sl), B, Hk, QG, D, P, _ptr(out))
+    B, Hk, P, QR, D = po.shape
+    QL = int(query_len)
+    assert QL >= 1 and QR % QL == 0
+    QG = QR // QL
+    out = np.zeros((B * QL, Hk * QG, D), np.float64)
+    _load().uqo_reduce_q(_ptr(po), _ptr(pm), _ptr(pl), _ptr(sl), B, Hk, QL, QG, D, P,
+                         _ptr(out))
     return out
 
 

@@ -151,17 +151,20 @@ void uqo_rotate(const double* q, const int8_t* signs, int D, double* out) {
 
 /* ------------------------------------------------------------ decode ---------------- */
 
-/* Paged decode attention, fp64.
+/* Paged decode attention, fp64, for query_len (QL) query rows per sequence.
  *
- * q        : [B, Hq, D] widened to fp64, element strides q_ss (sequence), q_sh (head)
+ * q        : [B * QL, Hq, D] widened to fp64, element strides q_ss (query row), q_sh
+ *            (head); row b * QL + j is query j of sequence b
  * cache    : [num_blocks, block_size, Hk, slot_bytes] bytes
  * bt       : [B, bt_stride] int32 physical block ids; only entries for visible tokens
  *            (t < seq_lens[b]) are read
  * rot      : NULL, or +-1 signs of the query rotation (fp4 formats)
- * Per (b, h, g) with Hq = Hk * QG and head index h*QG + g:
- *   s_t = softmax_scale * k_scale * (q' . k_t)   for every t < L_b
+ * Per (b, j, h, g) with Hq = Hk * QG and head index h*QG + g, query j sees the tokens
+ * t < L_bj = L_b - QL + 1 + j (the last query row sees the whole sequence: [P3] MTP
+ * causal window of each query row):
+ *   s_t = softmax_scale * k_scale * (q' . k_t)   for every t < L_bj
  *   out = v_scale * sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
- * L_b = 0 gives a zero row.
+ * A row with L_bj <= 0 is zero.  QL = 1 is single-token decode.
  *
  * If num_partitions > 0 the per-partition statistics are also produced.  Partition p
  * owns the 256-token tile-groups p, p+P, p+2P, ... ([P1] builder comment on the strided
@@ -169,19 +172,22 @@ void uqo_rotate(const double* q, const int8_t* signs, int D, double* out) {
  *   part_m = max s_t,  part_l = sum exp(s_t - part_m),
  *   part_o = v_scale * sum exp(s_t - part_m) v_t / part_l
  * and an empty partition is (m = -inf, l = 0, o = 0) ([P1] STEP G; [P3] empty-partition
- * fix).  Layouts: part_o [B, Hk, P, QG, D], part_m / part_l [B, Hk, P, QG].
+ * fix).  Layouts: part_o [B, Hk, P, QL*QG, D], part_m / part_l [B, Hk, P, QL*QG], row
+ * j*QG + g; out [B * QL, Hq, D].
  *
  * Returns 0, or -1 if a visible token's block id is outside [0, num_blocks), or -2 on
  * bad sizes. */
-int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache,
-               int64_t num_blocks, int block_size, int num_kv_heads, int slot_bytes,
-               int kv_format, double k_scale, double v_scale, const int8_t* rot,
-               const int32_t* bt, int bt_stride, const int32_t* seq_lens, int num_seqs,
-               int num_q_heads, int head_dim, double softmax_scale, double* out,
-               int num_partitions, double* part_m, double* part_l, double* part_o) {
-  const int B = num_seqs, Hk = num_kv_heads, D = head_dim;
-  if (Hk <= 0 || num_q_heads % Hk != 0 || D <= 0 || block_size <= 0) return -2;
+int uqo_decode_q(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache,
+                 int64_t num_blocks, int block_size, int num_kv_heads, int slot_bytes,
+                 int kv_format, double k_scale, double v_scale, const int8_t* rot,
+                 const int32_t* bt, int bt_stride, const int32_t* seq_lens, int num_seqs,
+                 int query_len, int num_q_heads, int head_dim, double softmax_scale,
+                 double* out, int num_partitions, double* part_m, double* part_l,
+                 double* part_o) {
+  const int B = num_seqs, Hk = num_kv_heads, D = head_dim, QL = query_len;
+  if (Hk <= 0 || num_q_heads % Hk != 0 || D <= 0 || block_size <= 0 || QL < 1) return -2;
   const int QG = num_q_heads / Hk;
+  const int QR = QL * QG; /* partial rows per (sequence, kv head) */
   const int P = num_partitions;
   if (slot_bytes < uqo_slot_content_bytes(kv_format, D) ||
       uqo_slot_content_bytes(kv_format, D) == 0)
@@ -191,15 +197,15 @@ int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache
 #pragma omp parallel for collapse(2) schedule(dynamic)
   for (int b = 0; b < B; ++b) {
     for (int h = 0; h < Hk; ++h) {
-      const int L = seq_lens[b];
-      double* K = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * D);
-      double* V = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * D);
-      double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+      const int Lseq = seq_lens[b];
+      double* K = (double*)malloc(sizeof(double) * (size_t)(Lseq > 0 ? Lseq : 1) * D);
+      double* V = (double*)malloc(sizeof(double) * (size_t)(Lseq > 0 ? Lseq : 1) * D);
+      double* s = (double*)malloc(sizeof(double) * (size_t)(Lseq > 0 ? Lseq : 1));
       double* qr = (double*)malloc(sizeof(double) * D);
       double* qv = (double*)malloc(sizeof(double) * D);
       int bad = 0;
       /* gather and decode every visible token of this (sequence, kv head) */
-      for (int t = 0; t < L && !bad; ++t) {
+      for (int t = 0; t < Lseq && !bad; ++t) {
         const int64_t blk = bt[(int64_t)b * bt_stride + t / block_size];
         if (blk < 0 || blk >= num_blocks) {
           bad = 1;
@@ -213,9 +219,13 @@ int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache
 #pragma omp atomic write
         status = -1;
       }
-      for (int g = 0; g < QG && !bad; ++g) {
+      for (int r = 0; r < QR && !bad; ++r) {
+        const int j = r / QG, g = r % QG;
+        /* the tokens this query row sees */
+        const int L = Lseq - QL + 1 + j > 0 ? Lseq - QL + 1 + j : 0;
         const int qh = h * QG + g;
-        for (int d = 0; d < D; ++d) qv[d] = q[(int64_t)b * q_ss + (int64_t)qh * q_sh + d];
+        const int64_t qrow = (int64_t)b * QL + j;
+        for (int d = 0; d < D; ++d) qv[d] = q[qrow * q_ss + (int64_t)qh * q_sh + d];
         if (rot)
           uqo_rotate(qv, rot, D, qr);
         else
@@ -227,7 +237,7 @@ int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache
           s[t] = softmax_scale * k_scale * dot;
         }
         /* full softmax over all visible tokens */
-        double* o = out + ((int64_t)b * num_q_heads + qh) * D;
+        double* o = out + (qrow * num_q_heads + qh) * D;
         for (int d = 0; d < D; ++d) o[d] = 0.0;
         if (L > 0) {
           double mx = -INFINITY;
@@ -242,7 +252,7 @@ int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache
         }
         /* per-partition statistics: partition p holds tile-groups p, p+P, p+2P, ... */
         for (int p = 0; p < P; ++p) {
-          const int64_t ml = (((int64_t)b * Hk + h) * P + p) * QG + g;
+          const int64_t ml = (((int64_t)b * Hk + h) * P + p) * QR + r;
           double* po = part_o + ml * D;
           double mx = -INFINITY, den = 0.0;
           int any = 0;
@@ -280,32 +290,48 @@ int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache
   return status;
 }
 
-/* Flash-combine ([P3] partition split + parallel reduce): for each (b, h, g),
+int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache,
+               int64_t num_blocks, int block_size, int num_kv_heads, int slot_bytes,
+               int kv_format, double k_scale, double v_scale, const int8_t* rot,
+               const int32_t* bt, int bt_stride, const int32_t* seq_lens, int num_seqs,
+               int num_q_heads, int head_dim, double softmax_scale, double* out,
+               int num_partitions, double* part_m, double* part_l, double* part_o) {
+  return uqo_decode_q(q, q_ss, q_sh, cache, num_blocks, block_size, num_kv_heads, slot_bytes,
+                      kv_format, k_scale, v_scale, rot, bt, bt_stride, seq_lens, num_seqs, 1,
+                      num_q_heads, head_dim, softmax_scale, out, num_partitions, part_m,
+                      part_l, part_o);
+}
+
+/* Flash-combine ([P3] partition split + parallel reduce): for each (b, j, h, g),
  *   M = max_p part_m,  w_p = part_l * exp(part_m - M),
  *   out = sum_p w_p part_o / sum_p w_p
- * over the partitions p < min(P, ceil(L_b / 256)) that hold tokens; a row with no
- * tokens is zero.  Partials use the layouts of uqo_decode; out is [B, Hk*QG, D]. */
-void uqo_reduce(const double* part_o, const double* part_m, const double* part_l,
-                const int32_t* seq_lens, int num_seqs, int num_kv_heads, int qg, int head_dim,
-                int num_partitions, double* out) {
-  const int Hk = num_kv_heads, QG = qg, D = head_dim, P = num_partitions;
+ * over the partitions p < min(P, ceil(L_b / 256)) that hold tokens of the row (l > 0); a
+ * row with no tokens is zero.  Partials use the layouts of uqo_decode_q (rows j*QG + g);
+ * out is [B * QL, Hk*QG, D]. */
+void uqo_reduce_q(const double* part_o, const double* part_m, const double* part_l,
+                  const int32_t* seq_lens, int num_seqs, int num_kv_heads, int query_len,
+                  int qg, int head_dim, int num_partitions, double* out) {
+  const int Hk = num_kv_heads, QL = query_len, QG = qg, D = head_dim, P = num_partitions;
+  const int QR = QL * QG;
   for (int b = 0; b < num_seqs; ++b) {
     const int L = seq_lens[b];
     const int ntg = (L + UQO_TILE_GROUP - 1) / UQO_TILE_GROUP;
     const int n = ntg < P ? ntg : P;
     for (int h = 0; h < Hk; ++h) {
-      for (int g = 0; g < QG; ++g) {
-        double* o = out + ((int64_t)b * Hk * QG + h * QG + g) * D;
+      for (int r = 0; r < QR; ++r) {
+        const int j = r / QG, g = r % QG;
+        double* o = out + (((int64_t)b * QL + j) * Hk * QG + h * QG + g) * D;
         double M = -INFINITY;
         for (int p = 0; p < n; ++p) {
-          const double m = part_m[(((int64_t)b * Hk + h) * P + p) * QG + g];
+          const double m = part_m[(((int64_t)b * Hk + h) * P + p) * QR + r];
           M = m > M ? m : M;
         }
         double den = 0.0;
         for (int d = 0; d < D; ++d) o[d] = 0.0;
         if (n == 0) continue;
         for (int p = 0; p < n; ++p) {
-          const int64_t ml = (((int64_t)b * Hk + h) * P + p) * QG + g;
+          const int64_t ml = (((int64_t)b * Hk + h) * P + p) * QR + r;
+          if (part_l[ml] == 0.0) continue; /* no tokens of this row */
           const double w = part_l[ml] * exp(part_m[ml] - M);
           den += w;
           for (int d = 0; d < D; ++d) o[d] += w * part_o[ml * D + d];
@@ -314,6 +340,13 @@ void uqo_reduce(const double* part_o, const double* part_m, const double* part_l
       }
     }
   }
+}
+
+void uqo_reduce(const double* part_o, const double* part_m, const double* part_l,
+                const int32_t* seq_lens, int num_seqs, int num_kv_heads, int qg, int head_dim,
+                int num_partitions, double* out) {
+  uqo_reduce_q(part_o, part_m, part_l, seq_lens, num_seqs, num_kv_heads, 1, qg, head_dim,
+               num_partitions, out);
 }
 
 /* ------------------------------------------------------------ index scorer ---------- */

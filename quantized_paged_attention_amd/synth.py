@@ -117,7 +117,7 @@ def fp4_quantize(x: np.ndarray, group: int, scale_kind: str):
 @dataclasses.dataclass
 class DecodeCase:
     name: str
-    q: np.ndarray               # [B, Hq, D] float32 (bf16-representable when q_dtype == 'bf16')
+    q: np.ndarray               # [B*QL, Hq, D] float32 (bf16-representable when q_dtype == 'bf16')
     q_dtype: str                # 'f32' or 'bf16'
     cache: np.ndarray           # [num_blocks, block_size, Hk, slot_bytes] uint8
     block_table: np.ndarray     # [B, max_blocks] int32, -1 past each sequence's blocks
@@ -129,10 +129,11 @@ class DecodeCase:
     v_scale: float
     num_partitions: int
     rot_signs: np.ndarray | None = None   # [D] int8 of +-1 (fp4 rotated-K workloads)
+    query_len: int = 1          # query rows per sequence (row b*QL + j: query j of b)
 
     @property
     def B(self):
-        return self.q.shape[0]
+        return self.seq_lens.shape[0]
 
     @property
     def Hq(self):
@@ -192,7 +193,7 @@ def _poison(cache, bt, seq_lens, used_ids):
 def make_fp8_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=128, block_size=16,
                   q_dtype="bf16", values="uniform_codes", k_scale=1.0, v_scale=1.0,
                   num_partitions=None, spare_blocks=None, slot_bytes=None,
-                  softmax_scale=None, max_blocks=None) -> DecodeCase:
+                  softmax_scale=None, max_blocks=None, query_len=1) -> DecodeCase:
     """fp8 e4m3 per-tensor-scaled cache in the AoS slot [K codes D | V codes D]."""
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, np.int32)
@@ -211,17 +212,19 @@ def make_fp8_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=128, block
     else:
         raise ValueError(values)
     _poison(cache, bt, seq_lens, used)
-    q = rng.standard_normal((B, Hk * qg, D), dtype=np.float32)
+    q = rng.standard_normal((B * query_len, Hk * qg, D), dtype=np.float32)
     if q_dtype == "bf16":
         q = bf16_round(q)
     P = num_partitions or max(1, -(-int(seq_lens.max()) // TILE_GROUP))
     return DecodeCase(name, q, q_dtype, cache, bt, seq_lens, Hk, FMT_FP8_E4M3,
-                      softmax_scale or 1.0 / math.sqrt(D), k_scale, v_scale, P)
+                      softmax_scale or 1.0 / math.sqrt(D), k_scale, v_scale, P,
+                      query_len=query_len)
 
 
 def make_fp4_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=256, block_size=64,
                   scale_kind="e4m3", rotate=True, num_partitions=None, spare_blocks=16,
-                  slot_bytes=None, softmax_scale=None, q_dtype="bf16") -> DecodeCase:
+                  slot_bytes=None, softmax_scale=None, q_dtype="bf16",
+                  query_len=1) -> DecodeCase:
     """fp4 e2m1 cache with 32-dim group scales in the 272-byte AoS slot
     [Kc D/2 | Ks D/32 | Vc D/2 | Vs D/32].  With `rotate`, K is drawn directly in the
     rotated domain: for iid N(0,1) keys k and an orthogonal R, kR is again iid N(0,1),
@@ -247,13 +250,14 @@ def make_fp4_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=256, block
             cache[b0:b1, :, :, o:o + w] = part
             o += w
     _poison(cache, bt, seq_lens, used)
-    q = rng.standard_normal((B, Hk * qg, D), dtype=np.float32)
+    q = rng.standard_normal((B * query_len, Hk * qg, D), dtype=np.float32)
     if q_dtype == "bf16":
         q = bf16_round(q)
     signs = (rng.integers(0, 2, size=D) * 2 - 1).astype(np.int8) if rotate else None
     P = num_partitions or max(1, -(-int(seq_lens.max()) // TILE_GROUP))
     return DecodeCase(name, q, q_dtype, cache, bt, seq_lens, Hk, fmt,
-                      softmax_scale or 1.0 / math.sqrt(D), 1.0, 1.0, P, signs)
+                      softmax_scale or 1.0 / math.sqrt(D), 1.0, 1.0, P, signs,
+                      query_len=query_len)
 
 
 def tiny_fp8() -> DecodeCase:

@@ -77,23 +77,32 @@ def sylvester_rotation(signs: np.ndarray) -> np.ndarray:
 
 
 def sdpa_reference(case) -> np.ndarray:
-    """torch scaled_dot_product_attention (fp64, CPU) over the dense gathered cache."""
+    """torch scaled_dot_product_attention (fp64, CPU) over the dense gathered cache.  With
+    query_len QL, query row j of sequence b attends under a boolean mask to the tokens
+    t <= L_b - QL + j; a row that sees no token is zero."""
     B, Hq, D, Hk, QG = case.B, case.Hq, case.D, case.num_kv_heads, case.QG
+    QL = getattr(case, "query_len", 1)
     q = case.q.astype(np.float64)
     if case.rot_signs is not None:
         q = q @ sylvester_rotation(case.rot_signs)
-    out = np.zeros((B, Hq, D))
+    out = np.zeros((B * QL, Hq, D))
     for b in range(B):
-        if int(case.seq_lens[b]) == 0:
+        L = int(case.seq_lens[b])
+        if L == 0:
             continue
         for h in range(Hk):
             k, v = dense_kv(case, b, h)
-            qt = torch.from_numpy(q[b, h * QG:(h + 1) * QG])[:, None, :]     # [QG, 1, D]
             kt = torch.from_numpy(k)[None].expand(QG, -1, -1)
             vt = torch.from_numpy(v)[None].expand(QG, -1, -1)
-            o = torch.nn.functional.scaled_dot_product_attention(
-                qt, kt, vt, scale=case.softmax_scale * case.k_scale)
-            out[b, h * QG:(h + 1) * QG] = o[:, 0].numpy() * case.v_scale
+            for j in range(QL):
+                last = L - QL + j                      # last visible token of row j
+                if last < 0:
+                    continue
+                mask = torch.from_numpy(np.arange(L) <= last)[None, None, :].expand(QG, 1, -1)
+                qt = torch.from_numpy(q[b * QL + j, h * QG:(h + 1) * QG])[:, None, :]
+                o = torch.nn.functional.scaled_dot_product_attention(
+                    qt, kt, vt, attn_mask=mask, scale=case.softmax_scale * case.k_scale)
+                out[b * QL + j, h * QG:(h + 1) * QG] = o[:, 0].numpy() * case.v_scale
     return out
 
 

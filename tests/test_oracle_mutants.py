@@ -41,10 +41,16 @@ MUTANTS = {
                           "k[d] = e2m1_at(codes, d) * uqo_e4m3(sc[d / 32]);"),
     "index_head_stride": ("qv[d] = uqo_e4m3(q[row * q_st + h * q_sh + d]);",
                           "qv[d] = uqo_e4m3(q[row * q_st + d]);"),
+    "mtp_no_causal_window": ("const int L = Lseq - QL + 1 + j > 0 ? Lseq - QL + 1 + j : 0;",
+                             "const int L = Lseq;"),
+    "mtp_query_row": ("const int64_t qrow = (int64_t)b * QL + j;",
+                      "const int64_t qrow = (int64_t)b * QL + (QL - 1 - j);"),
+    "mtp_reduce_row_map": ("double* o = out + (((int64_t)b * QL + j) * Hk * QG + h * QG + g) * D;",
+                           "double* o = out + (((int64_t)b * QL) * Hk * QG + h * QR + r) * D;"),
 }
 
 PIN_SUITES = ["tests/test_oracle_codecs.py", "tests/test_oracle_attention.py",
-              "tests/test_oracle_index.py"]
+              "tests/test_oracle_index.py", "tests/test_oracle_mtp.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
