@@ -4,8 +4,10 @@ Default workload (the headline): one decode step = uq_paged_decode + uq_paged_re
 the high-batch fp8 batch (B=128, Hk=8, QG=8, D=128, L ~ U[4096, 16384], block 16, 64
 partitions of 256 tokens, per-tensor e4m3 K/V).  Other workloads (--workload):
 fp8_mid (B=16, L=16384), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions,
-e2m1 + e4m3 group scales, in-kernel rotation), nvfp4_index_ql{QL}_h{H} (32 requests,
-L ~ U[1024, 32768]: one uq_index_score call is a step).  Inputs are generated once,
+e2m1 + e4m3 group scales, in-kernel rotation), the same fp8 and FP4 shapes with QL query
+rows per sequence (fp8_high_mtp{QL}_qg{QG}, fp4_d256_mtp{QL}_qg{QG}: each row has its own
+causal window), nvfp4_index_ql{QL}_h{H} (32 requests, L ~ U[1024, 32768]: one
+uq_index_score call is a step).  Inputs are generated once,
 copied to HBM, and are resident before the timed region starts.  The KV cache (or the
 index pages) is held in as many copies as make at least 1 GiB, and step i reads copy
 i mod n: no step finds its bytes in L2 or the 256 MB MALL left there by the step before,
@@ -81,14 +83,15 @@ def cpu_baseline_decode(case, n_seqs: int, min_seconds: float = 10.0):
     until at least min_seconds of wall time have been spent (at most 8 passes)."""
     from oracle import oracle
     sub = copy.copy(case)
-    sub.q = case.q[:n_seqs]
+    sub.q = case.q[:n_seqs * case.query_len]
     sub.block_table = case.block_table[:n_seqs]
     sub.seq_lens = case.seq_lens[:n_seqs]
     passes, dt = _timed_passes(
         lambda: oracle.decode(sub.q, sub.cache, sub.block_table, sub.seq_lens,
                               num_kv_heads=sub.num_kv_heads, kv_format=sub.kv_format,
                               softmax_scale=sub.softmax_scale, k_scale=sub.k_scale,
-                              v_scale=sub.v_scale, rot_signs=sub.rot_signs), min_seconds)
+                              v_scale=sub.v_scale, rot_signs=sub.rot_signs,
+                              query_len=sub.query_len), min_seconds)
     return {"value": round(passes * sub.kv_bytes() / dt / 1e9, 4), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {n_seqs} of {case.B} sequences, all {case.num_kv_heads} kv heads "
@@ -119,6 +122,18 @@ def make_case(workload: str):
     if workload == "fp8_high":
         return synth.fp8_high(), ("fp8_high: B=128 Hk=8 QG=8 D=128 L~U[4096,16384] block=16 "
                                   "P=64 per-tensor e4m3 K/V, bf16 Q")
+    if workload.startswith("fp8_high_mtp"):
+        ql, qg = (int(x) for x in workload[len("fp8_high_mtp"):].split("_qg"))
+        return synth.fp8_high_mtp(ql, qg), (
+            f"{workload}: B=128 Hk=8 QL={ql} query rows x QG={qg} D=128 L~U[4096,16384] "
+            "block=16 P=64 per-tensor e4m3 K/V, bf16 Q, causal window per query row")
+    if workload.startswith("fp4_d256_mtp") or workload.startswith("fp4ue_d256_mtp"):
+        ue = workload.startswith("fp4ue")
+        ql, qg = (int(x) for x in workload.split("_mtp")[1].split("_qg"))
+        return synth.fp4_d256_mtp(ql, qg, "ue8m0" if ue else "e4m3"), (
+            f"{workload}: B=4 Hk=2 QL={ql} query rows x QG={qg} D=256 L=75000 block=64 "
+            f"P=512 e2m1 K/V with {'UE8M0' if ue else 'e4m3'} group-of-32 scales, 272-byte "
+            "slot, rotated keys, bf16 Q, causal window per query row")
     if workload == "fp8_mid":
         return synth.fp8_mid(), ("fp8_mid: B=16 Hk=8 QG=8 D=128 L=16384 block=16 P=64 "
                                  "per-tensor e4m3 K/V, bf16 Q")
@@ -144,6 +159,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_high",
                     help="fp8_high (default), fp8_mid, fp4_d256_qg{6,8,16}, fp4ue_d256_qg{6,8,16}, "
+                         "fp8_high_mtp{QL}_qg{QG} (QL*QG <= 8), "
+                         "fp4[ue]_d256_mtp{QL}_qg{QG} (QL*QG <= 16), "
                          "nvfp4_index_ql{1,2,4,8}_h{1,2,4}")
     ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of a decode workload the CPU oracle baseline runs")
@@ -196,6 +213,7 @@ def main():
         dtype = "f16"
     else:
         B, Hq, D, hk, P = case.B, case.Hq, case.D, case.num_kv_heads, case.num_partitions
+        QL = case.query_len
         qdt = torch.float32 if case.q_dtype == "f32" else torch.bfloat16
         q = torch.from_numpy(case.q).to(qdt).to(dev)
         cache0 = torch.from_numpy(case.cache).to(dev)
@@ -206,18 +224,19 @@ def main():
         ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev) if is_fp8 else None
         vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev) if is_fp8 else None
         rot = torch.from_numpy(case.rot_signs).to(dev) if case.rot_signs is not None else None
-        po, pm, pl = uq.alloc_partials(B, hk, case.QG, D, P, dev)
-        out = torch.empty(B, Hq, D, dtype=qdt, device=dev)
+        po, pm, pl = uq.alloc_partials(B, hk, QL * case.QG, D, P, dev)
+        out = torch.empty(B * QL, Hq, D, dtype=qdt, device=dev)
         max_len = case.max_seq_len
 
         def decode(cache):
             uq.paged_decode(q, cache, bt, sl, kv_format=case.kv_format, max_seq_len=max_len,
                             num_partitions=P, part_out=po, part_max=pm, part_sum=pl,
                             softmax_scale=case.softmax_scale, k_scale=ks, v_scale=vs,
-                            rot_signs=rot, stream=stream)
+                            rot_signs=rot, query_len=QL, stream=stream)
 
         def reduce():
-            uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, stream=stream)
+            uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, query_len=QL,
+                            stream=stream)
 
         def kernels(cache):
             decode(cache)
@@ -283,7 +302,8 @@ def main():
     }
     res["kernels_us"][f"{names[0]}_median"] = round(float(np.median(k_ms[0])) * 1e3, 2)
     if fam != "index":
-        res["config"].update(global_batch=case.B, seq_len_max=case.max_seq_len)
+        res["config"].update(global_batch=case.B, seq_len_max=case.max_seq_len,
+                             query_len=case.query_len)
     if not args.no_cpu:
         res["cpu_baseline"] = (cpu_baseline_index(case) if fam == "index" else
                                cpu_baseline_decode(case, min(args.cpu_seqs, case.B)))

@@ -94,8 +94,9 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  * flash-combine workspace: the decode may merge the statistics of a set of consecutive
  * partitions into the first of them (m, l, o of their union) and write the others of the
  * set as empty (m = -inf, l = 0, o rows left unwritten).  Combining all written states
- * with uq_paged_reduce gives the attention output either way.  The fp8 kernel merges
- * the partitions of one workgroup (2 or 4); the fp4 kernel writes every partition.
+ * with uq_paged_reduce gives the attention output either way.  Both kernels merge the
+ * run of consecutive partitions one workgroup streams (its length is chosen by the
+ * launcher from the problem size and the device's compute units).
  * With num_partitions = 1 part_* hold exactly the statistics above.
  * Supported: (UQ_KV_FP8_E4M3, D = 128, QG <= 8) and (UQ_KV_FP4_E2M1_E4M3S or
  * UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else returns UQ_ERR_UNSUPPORTED.
@@ -129,6 +130,41 @@ int uq_paged_reduce(const void* part_out, const float* part_max, const float* pa
                     int32_t qg, int32_t head_dim, int32_t num_partitions,
                     int32_t max_seq_len, void* out, int out_dtype, int64_t o_stride_seq,
                     int64_t o_stride_head, void* stream);
+
+/* uq_paged_decode_mtp -- uq_paged_decode for query_len >= 1 query rows per sequence
+ * (multi-token decode, [P3] MTP path with query_length > 1).  Query row j of sequence b
+ * sees the tokens t < L_b - query_len + 1 + j ([P3] causal window of each query row: the
+ * last row sees the whole sequence); a row that sees no token of a partition leaves that
+ * partition empty for the row (m = -inf, l = 0), and a row that sees no token at all
+ * reduces to 0.  Arguments as uq_paged_decode, except:
+ *   query         [num_seqs * query_len, num_q_heads, head_dim]; row b*query_len + j is
+ *                 query j of sequence b; q_stride_seq is the stride between query rows.
+ *   part_out      bf16 [num_seqs, num_kv_heads, P, query_len * QG, head_dim]
+ *   part_max,     f32  [num_seqs, num_kv_heads, P, query_len * QG]; row j*QG + g holds
+ *   part_sum      query j, head h*QG + g (uq_decode_workspace_bytes with qg = query_len*QG)
+ * Supported: fp8 with query_len * QG <= 8, fp4 with query_len * QG <= 16; query_len = 1
+ * is exactly uq_paged_decode.  query_len < 1 returns UQ_ERR_INVALID_ARG. */
+int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
+                        int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
+                        int kv_format, const float* k_scale, const float* v_scale,
+                        const int8_t* rot_signs, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                        int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                        float softmax_scale, int32_t num_partitions, void* part_out,
+                        float* part_max, float* part_sum, void* stream);
+
+/* uq_paged_reduce_mtp -- uq_paged_reduce of the partials of uq_paged_decode_mtp: for
+ * every (b, j, h, g) the flash-combine above over the partitions with l_p > 0 of partial
+ * row j*qg + g, written to out row b*query_len + j, head h*qg + g.
+ *   out        [num_seqs * query_len, num_kv_heads * qg, head_dim]; o_stride_seq is the
+ *              stride between query rows.
+ * Supported: head_dim in {128, 256}, query_len >= 1, qg >= 1, query_len * qg <= 16. */
+int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float* part_sum,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                        int32_t query_len, int32_t qg, int32_t head_dim, int32_t num_partitions,
+                        int32_t max_seq_len, void* out, int out_dtype, int64_t o_stride_seq,
+                        int64_t o_stride_head, void* stream);
 
 /* uq_index_score -- nvfp4 index scores ([P2] compile_score_decode).  For request r,
  * query row j < query_len, index head h and page b < ceil(L_r / 128):

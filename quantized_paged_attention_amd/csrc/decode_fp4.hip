@@ -200,8 +200,12 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   }
   const int p = part_first;
 
-  const int n = lane & 15;   // query head of the QK / softmax layout; PV column group
+  const int n = lane & 15;   // unit row of the QK / softmax layout; PV column group
   const int q = lane >> 4;   // lane row group
+  // unit rows r = j * QG + g: query row j (of QL per sequence), head g; query row j sees
+  // the tokens t < L - QL + 1 + j (the causal window of its row)
+  const int NR = a.QL * a.QG;
+  const int L_row = L - a.QL + 1 + (n < NR ? n / a.QG : 0);
 
   // ---- the stream.  Wave w takes tokens [64w, 64w + 64) of each of the workgroup's
   //      tile-groups.  The first step's loads go out before the query rotation, so the
@@ -250,9 +254,9 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
     const int row = 4 * wave + (lane >> 4);
     const int c = lane & 15;
     float x[16];
-    if (row < a.QG) {
-      const QT* src = reinterpret_cast<const QT*>(a.q) + (int64_t)b * a.q_ss +
-                      (int64_t)(h * a.QG + row) * a.q_sh + 16 * c;
+    if (row < NR) {
+      const QT* src = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.QL + row / a.QG) * a.q_ss +
+                      (int64_t)(h * a.QG + row % a.QG) * a.q_sh + 16 * c;
       if constexpr (sizeof(QT) == 4) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int t = t0 + 16 * T + 4 * q + jj;
-          c4[jj] = t < L ? c4[jj] * fac : -INFINITY;
+          c4[jj] = t < L_row ? c4[jj] * fac : -INFINITY;
         }
         s[T] = c4;
       }
@@ -431,7 +435,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
                          fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
       if (__builtin_amdgcn_ballot_w64(mloc > m_run)) {
         const float m_new = fmaxf(m_run, max_across_rows(mloc));
-        const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run = -inf
+        // 0 while m_run = -inf; 1 for a row that has seen no token yet (both -inf)
+        const float alpha = m_run == m_new ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
         // accumulator rows are heads 4q + jj: their factors live in lanes 4q + jj
@@ -443,11 +448,13 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) acc[mm][jj] *= al[jj];
       }
+      // a row that has seen no token (m_run = -inf) has only -inf scores: weight 0
+      const float m_ref = m_run == -INFINITY ? 0.f : m_run;
       float pv[8];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pv[4 * T + jj] = fast_exp2(s[T][jj] - m_run);
+        for (int jj = 0; jj < 4; ++jj) pv[4 * T + jj] = fast_exp2(s[T][jj] - m_ref);
 #pragma unroll
       for (int e = 0; e < 8; ++e) l_run += pv[e];
       // A operand of PV: head n, k-slot 8q + e <-> token t0 + (e < 4 ? 4q + e : 16 + 4q + e - 4)
@@ -589,14 +596,14 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
       }
       const float ms = lds_m[wave][hd];
       fself[jj] = (ms == -INFINITY || !(lsum > 0.f)) ? 0.f : fast_exp2(ms - M) / lsum;
-      if (wave == 0 && n == 0 && hd < a.QG) {
-        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + hd;
+      if (wave == 0 && n == 0 && hd < NR) {
+        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * NR + hd;
         a.part_m[row] = M * kLn2;
         a.part_l[row] = lsum;
         // the run's other partitions: empty states
         for (int pe = part_first + 1; pe < p_end; ++pe) {
-          a.part_m[row + (int64_t)(pe - p) * a.QG] = -INFINITY;
-          a.part_l[row + (int64_t)(pe - p) * a.QG] = 0.f;
+          a.part_m[row + (int64_t)(pe - p) * NR] = -INFINITY;
+          a.part_l[row + (int64_t)(pe - p) * NR] = 0.f;
         }
       }
     }
@@ -614,7 +621,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   {
     const int row = 4 * wave + (lane >> 4);
     const int c = lane & 15;
-    if (row < a.QG) {
+    if (row < NR) {
       f32x4 o[4];
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
@@ -623,7 +630,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         for (int w = 1; w < kW; ++w)
           o[k4] += *reinterpret_cast<const f32x4*>(&lds_acc[w][row][16 * c + 4 * k4]);
       }
-      const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + p) * a.QG + row;
+      const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + p) * NR + row;
       uint16_t* dst = a.part_o + prow * kD + 16 * c;
       *reinterpret_cast<i32x4*>(dst) =
           i32x4{(int)pack_bf16x2(o[0][0], o[0][1]), (int)pack_bf16x2(o[0][2], o[0][3]),

@@ -55,7 +55,7 @@ struct VTile {
 
 template <typename QT, int W>
 __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
-  // staging of the merged partition's bf16 output rows (QG <= 8 rows of 256 bytes), and
+  // staging of the merged partition's bf16 output rows (at most 8 rows of 256 bytes), and
   // the states of waves 1..W-1 handed to wave 0 (per lane: 32 accumulators, m_run,
   // m_true, l)
   __shared__ __attribute__((aligned(16))) uint16_t o_stage[8 * kD];
@@ -111,10 +111,15 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   // ---- query operands.  Byte j of lane group r holds head dim
   //      d = j < 16 ? 16 r + j : 64 + 16 r + (j - 16)   (same map as the K loads)
   float x[32];
-  const bool qvalid = g < a.QG;
+  // column g holds unit row g = (query qj, head qh) of QL query rows x QG heads; query qj
+  // sees the tokens t < L_row (the causal window of its row)
+  const int NR = a.QL * a.QG;
+  const bool qvalid = g < NR;
+  const int qj = qvalid ? g / a.QG : 0, qh = qvalid ? g % a.QG : 0;
+  const int L_row = L - a.QL + 1 + qj;
   {
-    const QT* qp = reinterpret_cast<const QT*>(a.q) + (int64_t)b * a.q_ss +
-                   (int64_t)(h * a.QG + (qvalid ? g : 0)) * a.q_sh;
+    const QT* qp = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.QL + qj) * a.q_ss +
+                   (int64_t)(h * a.QG + qh) * a.q_sh;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const QT* src = qp + half * 64 + 16 * r;
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float v = (z[j] + row_ror8(z[j])) * qk_mul;
-          s[tt][j] = pair_start + 16 * tt + 4 * r + j < L ? v : -INFINITY;
+          s[tt][j] = pair_start + 16 * tt + 4 * r + j < L_row ? v : -INFINITY;
         }
       }
       // Stage order is fixed: the scheduler must not hoist the prefetch loads above the
@@ -324,13 +329,15 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       m_true = fmaxf(m_true, mx);
       if (__builtin_amdgcn_ballot_w64(mx > m_run)) {  // wave-uniform
         const float m_new = mx > m_run ? mx + 4.f : m_run;
-        const float alpha = fast_exp2(m_run - m_new);  // 0 when m_run = -inf
+        // 0 when m_run = -inf; 1 for a row that has seen no token yet (both -inf)
+        const float alpha = m_run == m_new ? 1.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int m = 0; m < 8; ++m) acc[m] *= alpha;
         m_run = m_new;
       }
-      const float m8 = m_run - 8.f;
+      // a row that has seen no token (m_run = -inf) has only -inf scores: weight 0
+      const float m8 = m_run == -INFINITY ? 0.f : m_run - 8.f;
       int pw[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -402,13 +409,15 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   float M = m_true;
 #pragma unroll
   for (int w = 1; w < W; ++w) M = fmaxf(M, st_ml[w - 1][1][lane]);
-  float f0 = fast_exp2(m_run - 8.f - M);  // 0 for a wave without tokens (m_run = -inf)
+  // 0 for a wave without tokens of this row (m_run = -inf), and for every wave when the
+  // row saw no token in the workgroup (M = -inf: an empty state m = -inf, l = 0)
+  float f0 = M == -INFINITY ? 0.f : fast_exp2(m_run - 8.f - M);
   float l_all = l_tot * f0;
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] *= f0;
 #pragma unroll
   for (int w = 1; w < W; ++w) {
-    const float fw = fast_exp2(st_ml[w - 1][0][lane] - 8.f - M);
+    const float fw = M == -INFINITY ? 0.f : fast_exp2(st_ml[w - 1][0][lane] - 8.f - M);
     l_all += st_ml[w - 1][2][lane] * fw;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -421,7 +430,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
     // The bf16 rows go through LDS so that the partial is written with whole-line
     // stores: written from registers directly it would be 16-byte pieces at 64-byte
     // stride, and such scattered partial-line writes slow the concurrent KV stream.
-    const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * a.QG;
+    const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * NR;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       i32x4 w;
@@ -431,11 +440,11 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
         w[e] = (int)pack_bf16x2(o0, o1);
       }
-      if (n < a.QG) *reinterpret_cast<i32x4*>(o_stage + n * kD + 32 * r + 8 * j) = w;
+      if (n < NR) *reinterpret_cast<i32x4*>(o_stage + n * kD + 32 * r + 8 * j) = w;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    const int nbytes = a.QG * kD * 2;  // contiguous partial rows of this partition
+    const int nbytes = NR * kD * 2;  // contiguous partial rows of this partition
     uint16_t* out = a.part_o + row0 * kD;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -444,14 +453,14 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
             *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(o_stage) + byte);
     }
-    if (n < a.QG && r == 0) {
+    if (n < NR && r == 0) {
       a.part_m[row0 + n] = M * kLn2;
       a.part_l[row0 + n] = l_all;
     }
     // the workgroup's other partitions that hold tokens: empty states
     for (int pe = part_first + 1 + r; pe < p_end; pe += 4) {
-      if (n < a.QG) {
-        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + pe) * a.QG + n;
+      if (n < NR) {
+        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + pe) * NR + n;
         a.part_m[row] = -INFINITY;
         a.part_l[row] = 0.f;
       }

@@ -2,7 +2,8 @@
 // "pa_decode_tile": cross-workgroup partition split merged by a parallel reduce kernel;
 // its empty-partition fix: partitions without tokens must not contribute).
 //
-// For output row (sequence b, query head hq) with n = min(P, ceil(L / 256)) partitions,
+// For output row (sequence b, query head hq; with several query rows per sequence, query
+// row j of b) with n = min(P, ceil(L / 256)) partitions,
 // over the partitions with l_p > 0 (a partition without tokens, or one whose tokens the
 // decode merged into a neighbouring partition's statistics, has l_p = 0):
 //   M = max_p m_p,  w_p = l_p exp(m_p - M),  out = sum_p w_p o_p / sum_p w_p   (0 if none).
@@ -210,8 +211,9 @@ __global__ __launch_bounds__(S <= 4 ? 256 : 64 * S) void reduce_kernel(ReduceArg
   }
   if (pg != 0) return;
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  OT* dst = reinterpret_cast<OT*>(a.out) + (int64_t)b * a.o_ss + (int64_t)(h * a.QG + g) * a.o_sh +
-            8 * dl;
+  const int qgh = a.QG / a.QL;  // query heads per kv head; row g = query g / qgh, head g % qgh
+  OT* dst = reinterpret_cast<OT*>(a.out) + ((int64_t)b * a.QL + g / qgh) * a.o_ss +
+            (int64_t)(h * qgh + g % qgh) * a.o_sh + 8 * dl;
   if constexpr (sizeof(OT) == 4) {
     *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]} * inv;
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]} * inv;

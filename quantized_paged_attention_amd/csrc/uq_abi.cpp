@@ -73,15 +73,17 @@ size_t uq_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t
   return up(rows * head_dim * 2) + 2 * up(rows * 4);
 }
 
-int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_stride_head,
-                    const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
-                    int32_t num_kv_heads, int32_t slot_bytes, int kv_format,
-                    const float* k_scale, const float* v_scale, const int8_t* rot_signs,
-                    const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
-                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                    int32_t max_seq_len, float softmax_scale, int32_t num_partitions,
-                    void* part_out, float* part_max, float* part_sum, void* stream) {
+int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
+                        int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
+                        int kv_format, const float* k_scale, const float* v_scale,
+                        const int8_t* rot_signs, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                        int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                        float softmax_scale, int32_t num_partitions, void* part_out,
+                        float* part_max, float* part_sum, void* stream) {
   if (num_seqs < 0) return fail(UQ_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (query_len < 1) return fail(UQ_ERR_INVALID_ARG, "query_len must be >= 1 (got %d)", query_len);
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
     return fail(UQ_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, num_kv_heads);
@@ -132,6 +134,7 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
   a.B = num_seqs;
   a.Hk = num_kv_heads;
   a.QG = QG;
+  a.QL = query_len;
   a.P = num_partitions;
   const int ntg = (max_seq_len + uq::kTileGroup - 1) / uq::kTileGroup;
   a.TGPP = ntg == 0 ? 1 : (ntg + num_partitions - 1) / num_partitions;
@@ -161,7 +164,9 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
 
   if (kv_format == UQ_KV_FP8_E4M3) {
     if (head_dim != 128) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports head_dim 128 only");
-    if (QG > 8) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports query groups up to 8");
+    if (query_len * QG > 8)
+      return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports query_len x query group up to 8 rows (got %d x %d)",
+                  query_len, QG);
     if (rot_signs) return fail(UQ_ERR_UNSUPPORTED, "query rotation is supported with fp4 caches only");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache needs slot_bytes a multiple of 16");
     if (num_seqs == 0) return ok();
@@ -174,6 +179,9 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
     if (reinterpret_cast<uintptr_t>(rot_signs) & 15)
       return fail(UQ_ERR_INVALID_ARG, "rot_signs must be 16-byte aligned");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp4 cache needs slot_bytes a multiple of 16");
+    if (query_len * QG > 16)
+      return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports query_len x query group up to 16 rows (got %d x %d)",
+                  query_len, QG);
     if (num_seqs == 0) return ok();
     // One workgroup streams a run of R partitions (one query rotation, one merged
     // partial).  Two workgroups fit a compute unit, and the time goes as (rounds of
@@ -205,13 +213,30 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_
   return fail(UQ_ERR_UNSUPPORTED, "kv_format %d is not implemented", kv_format);
 }
 
-int uq_paged_reduce(const void* part_out, const float* part_max, const float* part_sum,
-                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads, int32_t qg,
-                    int32_t head_dim, int32_t num_partitions, int32_t max_seq_len, void* out,
-                    int out_dtype, int64_t o_stride_seq, int64_t o_stride_head, void* stream) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || qg < 1 || qg > 16)
-    return fail(UQ_ERR_INVALID_ARG, "bad sizes: num_seqs %d, num_kv_heads %d, qg %d", num_seqs,
-                num_kv_heads, qg);
+int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_stride_head,
+                    const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t slot_bytes, int kv_format,
+                    const float* k_scale, const float* v_scale, const int8_t* rot_signs,
+                    const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_seq_len, float softmax_scale, int32_t num_partitions,
+                    void* part_out, float* part_max, float* part_sum, void* stream) {
+  return uq_paged_decode_mtp(query, q_dtype, q_stride_seq, q_stride_head, kv_cache, num_blocks,
+                             block_size, num_kv_heads, slot_bytes, kv_format, k_scale, v_scale,
+                             rot_signs, block_table, bt_stride, seq_lens, num_seqs, 1, num_q_heads,
+                             head_dim, max_seq_len, softmax_scale, num_partitions, part_out,
+                             part_max, part_sum, stream);
+}
+
+int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float* part_sum,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
+                        int32_t query_len, int32_t qg, int32_t head_dim, int32_t num_partitions,
+                        int32_t max_seq_len, void* out, int out_dtype, int64_t o_stride_seq,
+                        int64_t o_stride_head, void* stream) {
+  if (query_len < 1) return fail(UQ_ERR_INVALID_ARG, "query_len must be >= 1 (got %d)", query_len);
+  if (num_seqs < 0 || num_kv_heads <= 0 || qg < 1 || query_len * qg > 16)
+    return fail(UQ_ERR_INVALID_ARG, "bad sizes: num_seqs %d, num_kv_heads %d, query_len %d x qg %d",
+                num_seqs, num_kv_heads, query_len, qg);
   if (head_dim != 128 && head_dim != 256)
     return fail(UQ_ERR_UNSUPPORTED, "reduce supports head_dim 128 and 256 (got %d)", head_dim);
   if (num_partitions < 1) return fail(UQ_ERR_INVALID_ARG, "num_partitions must be >= 1");
@@ -234,7 +259,8 @@ int uq_paged_reduce(const void* part_out, const float* part_max, const float* pa
   a.seq_lens = seq_lens;
   a.B = num_seqs;
   a.Hk = num_kv_heads;
-  a.QG = qg;
+  a.QG = query_len * qg;  // partial rows per (sequence, kv head)
+  a.QL = query_len;
   a.D = head_dim;
   a.P = num_partitions;
   a.max_seq_len = max_seq_len;
@@ -243,6 +269,15 @@ int uq_paged_reduce(const void* part_out, const float* part_max, const float* pa
   a.o_sh = o_stride_head;
   return launch_status(uq::launch_reduce(a, out_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
                        "reduce");
+}
+
+int uq_paged_reduce(const void* part_out, const float* part_max, const float* part_sum,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads, int32_t qg,
+                    int32_t head_dim, int32_t num_partitions, int32_t max_seq_len, void* out,
+                    int out_dtype, int64_t o_stride_seq, int64_t o_stride_head, void* stream) {
+  return uq_paged_reduce_mtp(part_out, part_max, part_sum, seq_lens, num_seqs, num_kv_heads, 1, qg,
+                             head_dim, num_partitions, max_seq_len, out, out_dtype, o_stride_seq,
+                             o_stride_head, stream);
 }
 
 int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head,

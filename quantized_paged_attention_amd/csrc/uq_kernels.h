@@ -22,11 +22,13 @@ struct DecodeArgs {
   int32_t bt_stride;
   const int32_t* seq_lens;
   int32_t B, Hk, QG, P, TGPP, max_seq_len, block_size;
+  int32_t QL;       // query rows per sequence: unit rows r = j * QG + g, query row b*QL + j
+                    // sees tokens t < L_b - QL + 1 + j
   int32_t runs;     // work items per (sequence, kv head)
   int32_t run_len;  // partitions per work item when each partition is one tile-group, else 0
   float softmax_scale;
-  uint16_t* part_o;            // bf16 [B, Hk, P, QG, D]
-  float* part_m;               // [B, Hk, P, QG]
+  uint16_t* part_o;            // bf16 [B, Hk, P, QL*QG, D]
+  float* part_m;               // [B, Hk, P, QL*QG]
   float* part_l;
 };
 
@@ -35,7 +37,9 @@ struct ReduceArgs {
   const float* part_m;
   const float* part_l;
   const int32_t* seq_lens;
-  int32_t B, Hk, QG, D, P, max_seq_len;
+  int32_t B, Hk, QG, D, P, max_seq_len;  // QG: partial rows per (sequence, kv head)
+  int32_t QL;       // query rows per sequence (QG a multiple of QL): row r goes to output
+                    // row b*QL + r / (QG/QL), head h*(QG/QL) + r % (QG/QL)
   void* out;
   int64_t o_ss, o_sh;
 };

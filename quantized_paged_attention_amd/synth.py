@@ -280,6 +280,23 @@ def fp8_high() -> DecodeCase:
                          max_blocks=1024)
 
 
+def fp8_high_mtp(query_len=2, qg=4) -> DecodeCase:
+    """The high-batch fp8 shape (same lengths, table and cache recipe) with query_len
+    query rows per sequence and qg query heads per kv head."""
+    return make_fp8_case(f"fp8_high_mtp{query_len}_qg{qg}", 3, seq_lens=fp8_high_seq_lens(),
+                         num_kv_heads=8, qg=qg, k_scale=0.05, v_scale=0.02, num_partitions=64,
+                         spare_blocks=256, max_blocks=1024, query_len=query_len)
+
+
+def fp4_d256_mtp(query_len=2, qg=8, scale_kind="e4m3") -> DecodeCase:
+    """The FP4 D=256 shape with query_len query rows per sequence."""
+    tag = "" if scale_kind == "e4m3" else "_ue8m0"
+    return make_fp4_case(f"fp4_d256_mtp{query_len}_qg{qg}{tag}", 4, seq_lens=[75000] * 4,
+                         num_kv_heads=2, qg=qg, head_dim=256, block_size=64,
+                         num_partitions=512, softmax_scale=1.0 / 16.0, scale_kind=scale_kind,
+                         query_len=query_len)
+
+
 def fp4_d256(qg=16, scale_kind="e4m3") -> DecodeCase:
     tag = "" if scale_kind == "e4m3" else "_ue8m0"
     return make_fp4_case(f"fp4_d256_qg{qg}{tag}", 4, seq_lens=[75000] * 4, num_kv_heads=2, qg=qg,

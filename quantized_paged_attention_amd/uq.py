@@ -22,7 +22,8 @@ UQ_OK, UQ_ERR_INVALID_ARG, UQ_ERR_UNSUPPORTED, UQ_ERR_LAUNCH = 0, 1, 2, 3
 UQ_F32, UQ_BF16 = 0, 1
 UQ_KV_FP8_E4M3, UQ_KV_FP4_E2M1_E4M3S, UQ_KV_FP4_E2M1_UE8M0S = 0, 1, 2
 
-EXPORTS = ("uq_paged_decode", "uq_paged_reduce", "uq_index_score",
+EXPORTS = ("uq_paged_decode", "uq_paged_reduce", "uq_paged_decode_mtp", "uq_paged_reduce_mtp",
+           "uq_index_score",
            "uq_decode_workspace_bytes", "uq_last_error")
 
 _lock = threading.Lock()
@@ -54,6 +55,13 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         lib.uq_paged_reduce.restype = ctypes.c_int
         lib.uq_paged_reduce.argtypes = [V, V, V, V, i32, i32, i32, i32, i32, i32, V,
                                         ctypes.c_int, i64, i64, V]
+        lib.uq_paged_decode_mtp.restype = ctypes.c_int
+        lib.uq_paged_decode_mtp.argtypes = [V, ctypes.c_int, i64, i64, V, i64, i32, i32, i32,
+                                            ctypes.c_int, V, V, V, V, i32, V, i32, i32, i32,
+                                            i32, i32, f32, i32, V, V, V, V]
+        lib.uq_paged_reduce_mtp.restype = ctypes.c_int
+        lib.uq_paged_reduce_mtp.argtypes = [V, V, V, V, i32, i32, i32, i32, i32, i32, i32, V,
+                                            ctypes.c_int, i64, i64, V]
         lib.uq_index_score.restype = ctypes.c_int
         lib.uq_index_score.argtypes = [V, i64, i64, V, i64, i64, V, i32, V, i32, i32, i32,
                                        i32, i32, i32, V, i64, i64, i32, V]
@@ -118,9 +126,12 @@ def paged_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch
                  num_partitions: int, part_out: torch.Tensor, part_max: torch.Tensor,
                  part_sum: torch.Tensor, softmax_scale: float = 0.0,
                  k_scale: torch.Tensor | None = None, v_scale: torch.Tensor | None = None,
-                 rot_signs: torch.Tensor | None = None, stream=None) -> None:
-    """uq_paged_decode on torch tensors: query [B, Hq, D] (strided over B and Hq, D
-    contiguous); kv_cache [num_blocks, block_size, Hk, slot] uint8."""
+                 rot_signs: torch.Tensor | None = None, query_len: int = 1,
+                 stream=None) -> None:
+    """uq_paged_decode (query_len = 1) or uq_paged_decode_mtp on torch tensors: query
+    [B*QL, Hq, D] (strided over rows and Hq, D contiguous; row b*QL + j is query j of
+    sequence b); kv_cache [num_blocks, block_size, Hk, slot] uint8; partials
+    [B, Hk, P, QL*QG(, D)]."""
     lib = load_library()
     if query.dim() != 3 or query.stride(2) != 1:
         raise ValueError("query must be [B, Hq, D] with a contiguous head dim")
@@ -134,14 +145,18 @@ def paged_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch
     _need(part_out, torch.bfloat16, "part_out")
     _need(part_max, torch.float32, "part_max")
     _need(part_sum, torch.float32, "part_sum")
-    B, Hq, D = query.shape
+    rows, Hq, D = query.shape
+    QL = int(query_len)
+    B = seq_lens.shape[0] if seq_lens.dim() == 1 else -1
+    if QL < 1 or rows != B * QL:
+        raise ValueError("query must hold query_len rows per sequence of seq_lens")
     nb, bs, hk, slot = kv_cache.shape
-    qg = Hq // hk if hk else 0
-    if tuple(part_out.shape) != (B, hk, num_partitions, qg, D) or not part_out.is_contiguous():
-        raise ValueError("part_out must be a contiguous [B, Hk, P, QG, D] tensor")
+    qr = QL * (Hq // hk if hk else 0)
+    if tuple(part_out.shape) != (B, hk, num_partitions, qr, D) or not part_out.is_contiguous():
+        raise ValueError("part_out must be a contiguous [B, Hk, P, QL*QG, D] tensor")
     for t, nm in ((part_max, "part_max"), (part_sum, "part_sum")):
-        if tuple(t.shape) != (B, hk, num_partitions, qg) or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous [B, Hk, P, QG] tensor")
+        if tuple(t.shape) != (B, hk, num_partitions, qr) or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous [B, Hk, P, QL*QG] tensor")
     for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
         if t is not None:
             _need(t, torch.float32, nm)
@@ -149,46 +164,60 @@ def paged_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch
         _need(rot_signs, torch.int8, "rot_signs")
     if seq_lens.shape != (B,) or block_table.shape[0] != B:
         raise ValueError("seq_lens / block_table do not match the batch")
-    _check(lib.uq_paged_decode(
-        _ptr(query), _dtype_code(query.dtype), query.stride(0), query.stride(1), _ptr(kv_cache),
-        nb, bs, hk, slot, kv_format, _ptr(k_scale), _ptr(v_scale), _ptr(rot_signs),
-        _ptr(block_table), block_table.stride(0), _ptr(seq_lens), B, Hq, D, int(max_seq_len),
-        float(softmax_scale), int(num_partitions), _ptr(part_out), _ptr(part_max),
-        _ptr(part_sum), _stream(stream)))
+    head = (_ptr(query), _dtype_code(query.dtype), query.stride(0), query.stride(1),
+            _ptr(kv_cache), nb, bs, hk, slot, kv_format, _ptr(k_scale), _ptr(v_scale),
+            _ptr(rot_signs), _ptr(block_table), block_table.stride(0), _ptr(seq_lens), B)
+    tail = (Hq, D, int(max_seq_len), float(softmax_scale), int(num_partitions),
+            _ptr(part_out), _ptr(part_max), _ptr(part_sum), _stream(stream))
+    if QL == 1:
+        _check(lib.uq_paged_decode(*head, *tail))
+    else:
+        _check(lib.uq_paged_decode_mtp(*head, QL, *tail))
 
 
 def paged_reduce(part_out: torch.Tensor, part_max: torch.Tensor, part_sum: torch.Tensor,
                  seq_lens: torch.Tensor, out: torch.Tensor, *, max_seq_len: int,
-                 stream=None) -> None:
-    """uq_paged_reduce into out [B, Hk*QG, D] (float32 or bfloat16, D contiguous)."""
+                 query_len: int = 1, stream=None) -> None:
+    """uq_paged_reduce (query_len = 1) or uq_paged_reduce_mtp into out [B*QL, Hk*QG, D]
+    (float32 or bfloat16, D contiguous) from partials [B, Hk, P, QL*QG(, D)]."""
     lib = load_library()
     _need(part_out, torch.bfloat16, "part_out")
-    B, hk, P, qg, D = part_out.shape
-    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (B, hk * qg, D):
-        raise ValueError("out must be [B, Hk*QG, D] with a contiguous head dim")
-    _check(lib.uq_paged_reduce(
-        _ptr(part_out), _ptr(part_max), _ptr(part_sum), _ptr(seq_lens), B, hk, qg, D, P,
-        int(max_seq_len), _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
-        _stream(stream)))
+    B, hk, P, qr, D = part_out.shape
+    QL = int(query_len)
+    if QL < 1 or qr % QL:
+        raise ValueError("the partial rows must be query_len x QG")
+    qg = qr // QL
+    if out.dim() != 3 or out.stride(2) != 1 or tuple(out.shape) != (B * QL, hk * qg, D):
+        raise ValueError("out must be [B*QL, Hk*QG, D] with a contiguous head dim")
+    head = (_ptr(part_out), _ptr(part_max), _ptr(part_sum), _ptr(seq_lens), B, hk)
+    tail = (qg, D, P, int(max_seq_len), _ptr(out), _dtype_code(out.dtype), out.stride(0),
+            out.stride(1), _stream(stream))
+    if QL == 1:
+        _check(lib.uq_paged_reduce(*head, *tail))
+    else:
+        _check(lib.uq_paged_reduce_mtp(*head, QL, *tail))
 
 
 def paged_attention(query, kv_cache, block_table, seq_lens, *, kv_format, max_seq_len,
                     num_partitions, out=None, partials=None, softmax_scale=0.0,
-                    k_scale=None, v_scale=None, rot_signs=None, stream=None):
-    """One decode step: uq_paged_decode then uq_paged_reduce; returns out [B, Hq, D] in
-    the query dtype."""
-    B, Hq, D = query.shape
+                    k_scale=None, v_scale=None, rot_signs=None, query_len=1, stream=None):
+    """One decode step: uq_paged_decode then uq_paged_reduce (their _mtp forms for
+    query_len > 1); returns out [B*QL, Hq, D] in the query dtype."""
+    rows, Hq, D = query.shape
+    B = seq_lens.shape[0]
     hk = kv_cache.shape[2]
     if partials is None:
-        partials = alloc_partials(B, hk, Hq // hk, D, num_partitions, query.device)
+        partials = alloc_partials(B, hk, query_len * (Hq // hk), D, num_partitions,
+                                  query.device)
     if out is None:
-        out = torch.empty(B, Hq, D, dtype=query.dtype, device=query.device)
+        out = torch.empty(rows, Hq, D, dtype=query.dtype, device=query.device)
     po, pm, pl = partials
     paged_decode(query, kv_cache, block_table, seq_lens, kv_format=kv_format,
                  max_seq_len=max_seq_len, num_partitions=num_partitions, part_out=po,
                  part_max=pm, part_sum=pl, softmax_scale=softmax_scale, k_scale=k_scale,
-                 v_scale=v_scale, rot_signs=rot_signs, stream=stream)
-    paged_reduce(po, pm, pl, seq_lens, out, max_seq_len=max_seq_len, stream=stream)
+                 v_scale=v_scale, rot_signs=rot_signs, query_len=query_len, stream=stream)
+    paged_reduce(po, pm, pl, seq_lens, out, max_seq_len=max_seq_len, query_len=query_len,
+                 stream=stream)
     return out
 
 

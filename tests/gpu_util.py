@@ -66,13 +66,14 @@ def run_decode(case, P=None, strided=False, dev=None, q=None, partials=None, out
     dev = dev or device_case(case)
     P = P or case.num_partitions
     q = q if q is not None else q_tensor(case, strided)
-    B, Hq, D = q.shape
+    _, Hq, D = q.shape
     hk = case.num_kv_heads
-    partials = partials or uq.alloc_partials(B, hk, Hq // hk, D, P)
+    QL = case.query_len
+    partials = partials or uq.alloc_partials(case.B, hk, QL * (Hq // hk), D, P)
     out = uq.paged_attention(q, dev["cache"], dev["bt"], dev["sl"], kv_format=case.kv_format,
                              max_seq_len=case.max_seq_len, num_partitions=P, partials=partials,
                              out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"],
-                             v_scale=dev["vs"], rot_signs=dev["rot"])
+                             v_scale=dev["vs"], rot_signs=dev["rot"], query_len=QL)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), partials
 
@@ -82,7 +83,8 @@ def oracle_decode(case, P=0):
     return oracle.decode(case.q, case.cache, case.block_table, case.seq_lens,
                          num_kv_heads=case.num_kv_heads, kv_format=case.kv_format,
                          softmax_scale=case.softmax_scale, k_scale=case.k_scale,
-                         v_scale=case.v_scale, rot_signs=case.rot_signs, num_partitions=P)
+                         v_scale=case.v_scale, rot_signs=case.rot_signs, num_partitions=P,
+                         query_len=case.query_len)
 
 
 def rel_err(got, ref):

@@ -83,6 +83,32 @@ def test_decode_zero_sequences_is_a_no_op(lib):
     assert lib.uq_last_error() == b""
 
 
+def decode_mtp_args(QL=2, **over):
+    """uq_paged_decode_mtp arguments: decode_args with query_len after num_seqs."""
+    a = decode_args(**over)
+    return a[:17] + [QL] + a[17:]
+
+
+@pytest.mark.parametrize("QL,over,status", [
+    (0, dict(), uq.UQ_ERR_INVALID_ARG),                    # query_len < 1
+    (-3, dict(), uq.UQ_ERR_INVALID_ARG),
+    (2, dict(), uq.UQ_ERR_UNSUPPORTED),                    # fp8: 2 x 8 rows > 8
+    (3, dict(Hq=8 * 3), uq.UQ_ERR_UNSUPPORTED),            # fp8: 3 x 3 rows > 8
+    (2, dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),
+    (5, dict(fmt=uq.UQ_KV_FP4_E2M1_UE8M0S, D=256, slot=272, Hq=8 * 4), uq.UQ_ERR_UNSUPPORTED),
+    (2, dict(Hq=60), uq.UQ_ERR_INVALID_ARG),               # checks of uq_paged_decode apply
+])
+def test_decode_mtp_validation(lib, QL, over, status):
+    assert lib.uq_paged_decode_mtp(*decode_mtp_args(QL, **over)) == status
+    assert lib.uq_last_error().decode()
+
+
+def test_decode_mtp_zero_sequences_is_a_no_op(lib):
+    assert lib.uq_paged_decode_mtp(*decode_mtp_args(4, B=0, Hq=8 * 2)) == uq.UQ_OK
+    assert lib.uq_paged_decode_mtp(
+        *decode_mtp_args(4, B=0, fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 4)) == uq.UQ_OK
+
+
 def reduce_args(**over):
     a = dict(po=FAKE, pm=FAKE, pl=FAKE, sl=FAKE, B=4, hk=8, qg=8, D=128, P=64, max_len=100,
              out=FAKE, dt=uq.UQ_BF16, o_ss=64 * 128, o_sh=128, stream=None)
@@ -98,6 +124,20 @@ def reduce_args(**over):
 ])
 def test_reduce_validation(lib, over, status):
     assert lib.uq_paged_reduce(*reduce_args(**over)) == status
+
+
+@pytest.mark.parametrize("QL,qg,status", [
+    (0, 8, uq.UQ_ERR_INVALID_ARG), (2, 16, uq.UQ_ERR_INVALID_ARG), (5, 4, uq.UQ_ERR_INVALID_ARG),
+    (3, 0, uq.UQ_ERR_INVALID_ARG),
+])
+def test_reduce_mtp_validation(lib, QL, qg, status):
+    a = reduce_args(qg=qg)
+    assert lib.uq_paged_reduce_mtp(*(a[:6] + [QL] + a[6:])) == status
+
+
+def test_reduce_mtp_zero_sequences_is_a_no_op(lib):
+    a = reduce_args(B=0, qg=4)
+    assert lib.uq_paged_reduce_mtp(*(a[:6] + [4] + a[6:])) == uq.UQ_OK
 
 
 def index_args(**over):
