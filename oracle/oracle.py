@@ -26,6 +26,7 @@ _lib = None
 FMT_FP8_E4M3 = 0
 FMT_FP4_E4M3S = 1
 FMT_FP4_UE8M0S = 2
+FMT_FP8_E4M3_TOK = 3
 
 
 def build(force: bool = True) -> str:
@@ -71,7 +72,8 @@ def _load():
                                    P, i32, P, i32, i32, i32, f64, P, i32, P, P, P]
         lib.uqo_decode_q.restype = i32
         lib.uqo_decode_q.argtypes = [P, i64, i64, P, i64, i32, i32, i32, i32, f64, f64, P,
-                                     P, i32, P, i32, i32, i32, i32, f64, P, i32, P, P, P]
+                                     P, P, P, i32, P, i32, i32, i32, i32, f64, P, i32, P, P,
+                                     P]
         lib.uqo_reduce.restype = None
         lib.uqo_reduce.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P]
         lib.uqo_reduce_q.restype = None
@@ -130,7 +132,8 @@ def rotate(q: np.ndarray, signs: np.ndarray) -> np.ndarray:
 def decode(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
            *, num_kv_heads: int, kv_format: int, softmax_scale: float,
            k_scale: float = 1.0, v_scale: float = 1.0, rot_signs: np.ndarray | None = None,
-           num_partitions: int = 0, query_len: int = 1):
+           num_partitions: int = 0, query_len: int = 1,
+           k_scale_tok: np.ndarray | None = None, v_scale_tok: np.ndarray | None = None):
     """Masked-softmax decode attention in fp64, query_len query rows per sequence.
 
     q: [B*QL, Hq, D] (any float dtype; widened exactly; row b*QL + j is query j of sequence
@@ -138,6 +141,8 @@ def decode(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray, seq_lens: 
     block_table: [B, max_blocks] int32, seq_lens: [B] int32.
     Returns out [B*QL, Hq, D] float64, and (part_m, part_l, part_o) when num_partitions > 0
     (shapes [B, Hk, P, QL*QG], [B, Hk, P, QL*QG], [B, Hk, P, QL*QG, D]; row j*QG + g).
+    With kv_format FMT_FP8_E4M3_TOK, k_scale_tok / v_scale_tok are the float32 per-token
+    scales [num_blocks, Hk, BS] (k_scale / v_scale then stay 1).
     """
     q = _c(q, np.float64)
     rows, Hq, D = q.shape
@@ -156,8 +161,14 @@ def decode(q: np.ndarray, cache: np.ndarray, block_table: np.ndarray, seq_lens: 
     pl = np.zeros_like(pm)
     po = np.zeros((B, hk, max(P, 1), QL * QG, D), np.float64)
     rot = None if rot_signs is None else _c(rot_signs, np.int8)
+    kt = vt = None
+    if kv_format == FMT_FP8_E4M3_TOK:
+        kt = _c(k_scale_tok, np.float32)
+        vt = _c(v_scale_tok, np.float32)
+        assert kt.shape == (nb, hk, bs) and vt.shape == (nb, hk, bs)
     st = _load().uqo_decode_q(_ptr(q), Hq * D, D, _ptr(cache), nb, bs, hk, slot, kv_format,
-                              float(k_scale), float(v_scale), _ptr(rot), _ptr(bt), bt.shape[1],
+                              float(k_scale), float(v_scale), _ptr(kt), _ptr(vt), _ptr(rot),
+                              _ptr(bt), bt.shape[1],
                               _ptr(sl), B, QL, Hq, D, float(softmax_scale), _ptr(out), P,
                               _ptr(pm), _ptr(pl), _ptr(po))
     if st != 0:

@@ -49,6 +49,7 @@ int uqo_num_threads(void) {
 #define UQO_FMT_FP8_E4M3 0       /* slot: K e4m3[D] | V e4m3[D]                          */
 #define UQO_FMT_FP4_E4M3S 1      /* slot: Kc[D/2] | Ks[D/32] | Vc[D/2] | Vs[D/32], e4m3 s */
 #define UQO_FMT_FP4_UE8M0S 2     /* same slot, UE8M0 group scales ([P1] STEP F V path)    */
+#define UQO_FMT_FP8_E4M3_TOK 3   /* fp8 slot, one f32 K and V scale per (block, head, pos) */
 
 #define UQO_TILE_GROUP 256       /* tokens per tile-group: 16 tiles of 16 ([P1] STEP F)    */
 #define UQO_INDEX_PAGE 128       /* tokens per index page ([P2] kernel argument comments)  */
@@ -99,7 +100,7 @@ static double e2m1_at(const uint8_t* codes, int d) {
 
 /* Bytes of slot content for a format and head dim (0 if unsupported). */
 int uqo_slot_content_bytes(int kv_format, int head_dim) {
-  if (kv_format == UQO_FMT_FP8_E4M3) return 2 * head_dim;
+  if (kv_format == UQO_FMT_FP8_E4M3 || kv_format == UQO_FMT_FP8_E4M3_TOK) return 2 * head_dim;
   if (kv_format == UQO_FMT_FP4_E4M3S || kv_format == UQO_FMT_FP4_UE8M0S) {
     if (head_dim % 32) return 0;
     return 2 * (head_dim / 2 + head_dim / 32);
@@ -112,7 +113,7 @@ int uqo_slot_content_bytes(int kv_format, int head_dim) {
  * V_SCALES offset constants): K codes [0, D/2), K group scales [D/2, D/2 + D/32),
  * V codes next, V group scales last; one scale per 32 consecutive dims. */
 static void decode_slot(const uint8_t* slot, int kv_format, int D, double* k, double* v) {
-  if (kv_format == UQO_FMT_FP8_E4M3) {
+  if (kv_format == UQO_FMT_FP8_E4M3 || kv_format == UQO_FMT_FP8_E4M3_TOK) {
     for (int d = 0; d < D; ++d) {
       k[d] = uqo_e4m3(slot[d]);
       v[d] = uqo_e4m3(slot[D + d]);
@@ -166,6 +167,15 @@ void uqo_rotate(const double* q, const int8_t* signs, int D, double* out) {
  *   out = v_scale * sum_t exp(s_t - max s) v_t / sum_t exp(s_t - max s)
  * A row with L_bj <= 0 is zero.  QL = 1 is single-token decode.
  *
+ * Per-token fp8 scales (kv_format UQO_FMT_FP8_E4M3_TOK, [P3] per_token_kv mode): the
+ * slot holds the same e4m3 K and V codes, and token t of a sequence, in physical block
+ * blk at position t mod block_size, has the decoded values
+ *   k_t = e4m3(K codes) * k_tok[(blk * Hk + h) * block_size + t mod block_size]
+ *   v_t = e4m3(V codes) * v_tok[(blk * Hk + h) * block_size + t mod block_size]
+ * (f32 scale tensors [num_blocks, Hk, block_size]); the per-tensor k_scale and v_scale
+ * still multiply on top (the binding passes 1 for them).  Other formats ignore k_tok and
+ * v_tok.
+ *
  * If num_partitions > 0 the per-partition statistics are also produced.  Partition p
  * owns the 256-token tile-groups p, p+P, p+2P, ... ([P1] builder comment on the strided
  * map and STEP F trip count); over its visible tokens:
@@ -179,7 +189,8 @@ void uqo_rotate(const double* q, const int8_t* signs, int D, double* out) {
  * bad sizes. */
 int uqo_decode_q(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache,
                  int64_t num_blocks, int block_size, int num_kv_heads, int slot_bytes,
-                 int kv_format, double k_scale, double v_scale, const int8_t* rot,
+                 int kv_format, double k_scale, double v_scale, const float* k_tok,
+                 const float* v_tok, const int8_t* rot,
                  const int32_t* bt, int bt_stride, const int32_t* seq_lens, int num_seqs,
                  int query_len, int num_q_heads, int head_dim, double softmax_scale,
                  double* out, int num_partitions, double* part_m, double* part_l,
@@ -192,6 +203,7 @@ int uqo_decode_q(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cac
   if (slot_bytes < uqo_slot_content_bytes(kv_format, D) ||
       uqo_slot_content_bytes(kv_format, D) == 0)
     return -2;
+  if (kv_format == UQO_FMT_FP8_E4M3_TOK && (!k_tok || !v_tok)) return -2;
   int status = 0;
 
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -214,6 +226,14 @@ int uqo_decode_q(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cac
         const int64_t slot_index = (blk * block_size + t % block_size) * Hk + h;
         decode_slot(cache + slot_index * slot_bytes, kv_format, D, K + (size_t)t * D,
                     V + (size_t)t * D);
+        if (kv_format == UQO_FMT_FP8_E4M3_TOK) {
+          const int64_t si = (blk * Hk + h) * block_size + t % block_size;
+          const double sk = k_tok[si], sv = v_tok[si];
+          for (int d = 0; d < D; ++d) {
+            K[(size_t)t * D + d] *= sk;
+            V[(size_t)t * D + d] *= sv;
+          }
+        }
       }
       if (bad) {
 #pragma omp atomic write
@@ -297,7 +317,8 @@ int uqo_decode(const double* q, int64_t q_ss, int64_t q_sh, const uint8_t* cache
                int num_q_heads, int head_dim, double softmax_scale, double* out,
                int num_partitions, double* part_m, double* part_l, double* part_o) {
   return uqo_decode_q(q, q_ss, q_sh, cache, num_blocks, block_size, num_kv_heads, slot_bytes,
-                      kv_format, k_scale, v_scale, rot, bt, bt_stride, seq_lens, num_seqs, 1,
+                      kv_format, k_scale, v_scale, NULL, NULL, rot, bt, bt_stride, seq_lens,
+                      num_seqs, 1,
                       num_q_heads, head_dim, softmax_scale, out, num_partitions, part_m,
                       part_l, part_o);
 }

@@ -37,6 +37,7 @@ SCORE_POISON_BITS = 0x7FC0DEAD   # quiet NaN with a payload, pre-filled into sco
 _E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
 
 FMT_FP8_E4M3 = 0
+FMT_FP8_E4M3_TOK = 3
 FMT_FP4_E2M1_E4M3S = 1
 FMT_FP4_E2M1_UE8M0S = 2
 
@@ -130,6 +131,8 @@ class DecodeCase:
     num_partitions: int
     rot_signs: np.ndarray | None = None   # [D] int8 of +-1 (fp4 rotated-K workloads)
     query_len: int = 1          # query rows per sequence (row b*QL + j: query j of b)
+    k_scale_tok: np.ndarray | None = None  # [num_blocks, Hk, block_size] float32 (per-token)
+    v_scale_tok: np.ndarray | None = None
 
     @property
     def B(self):
@@ -157,7 +160,12 @@ class DecodeCase:
 
     def kv_bytes(self) -> int:
         """Algorithmic KV bytes of one decode: every visible slot's content, once."""
-        content = 2 * self.D if self.kv_format == FMT_FP8_E4M3 else 2 * (self.D // 2 + self.D // 32)
+        if self.kv_format == FMT_FP8_E4M3:
+            content = 2 * self.D
+        elif self.kv_format == FMT_FP8_E4M3_TOK:
+            content = 2 * self.D + 8          # codes plus one f32 K and one f32 V scale
+        else:
+            content = 2 * (self.D // 2 + self.D // 32)
         return int(self.seq_lens.astype(np.int64).sum()) * self.num_kv_heads * content
 
 
@@ -190,11 +198,34 @@ def _poison(cache, bt, seq_lens, used_ids):
             cache[bt[b, L // bs], L % bs:] = POISON_BYTE
 
 
+def _tok_scale_poison(sc, bt, seq_lens, used_ids):
+    """NaN in the per-token scales of unreferenced blocks and of positions past a
+    sequence's length in its last block (they must never be used)."""
+    nb, _, bs = sc.shape
+    mask = np.ones(nb, bool)
+    mask[used_ids] = False
+    sc[mask] = np.nan
+    for b, L in enumerate(seq_lens):
+        L = int(L)
+        if L % bs:
+            sc[bt[b, L // bs], :, L % bs:] = np.nan
+
+
 def make_fp8_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=128, block_size=16,
                   q_dtype="bf16", values="uniform_codes", k_scale=1.0, v_scale=1.0,
                   num_partitions=None, spare_blocks=None, slot_bytes=None,
-                  softmax_scale=None, max_blocks=None, query_len=1) -> DecodeCase:
-    """fp8 e4m3 per-tensor-scaled cache in the AoS slot [K codes D | V codes D]."""
+                  softmax_scale=None, max_blocks=None, query_len=1, scales="tensor",
+                  tok_spread=0.5, v_ramp=0.0) -> DecodeCase:
+    """fp8 e4m3 cache in the AoS slot [K codes D | V codes D].
+
+    scales="tensor": one per-tensor K and V scale (k_scale, v_scale).
+    scales="token": one float32 K and V scale per (physical block, kv head, position)
+    ([num_blocks, Hk, block_size]).  With values="normal" every token's K (V) row is
+    x ~ sigma N(0,1), sigma lognormal(0, tok_spread), quantised as a per-token cache is
+    filled: scale = max|x| / 448, codes = e4m3(x / scale).  With values="uniform_codes"
+    the codes are uniform over the finite e4m3 codes and the scales are k_scale (v_scale)
+    times lognormal(0, tok_spread).  v_ramp > 0 multiplies the V scale of logical token t
+    of every sequence by 2^(v_ramp t / 256), so later tokens carry ever larger V scales."""
     rng = np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, np.int32)
     B, Hk, D = len(seq_lens), num_kv_heads, head_dim
@@ -203,22 +234,55 @@ def make_fp8_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=128, block
         spare_blocks = 0
     bt, nb, used = _table_and_blocks(rng, seq_lens, block_size, spare_blocks, max_blocks)
     shape = (nb, block_size, Hk, slot)
-    if values == "uniform_codes":
-        cache = E4M3_FINITE_CODES[rng.integers(0, 254, size=shape, dtype=np.uint8)]
-    elif values == "normal":
-        cache = np.zeros(shape, np.uint8)
-        x = rng.standard_normal((nb, block_size, Hk, 2 * D), dtype=np.float32)
-        cache[..., :2 * D] = e4m3_encode(x)
+    kst = vst = None
+    if scales == "token":
+        tshape = (nb, Hk, block_size)
+        if values == "uniform_codes":
+            cache = E4M3_FINITE_CODES[rng.integers(0, 254, size=shape, dtype=np.uint8)]
+            kst = (k_scale * np.exp(tok_spread * rng.standard_normal(tshape))).astype(np.float32)
+            vst = (v_scale * np.exp(tok_spread * rng.standard_normal(tshape))).astype(np.float32)
+        elif values == "normal":
+            cache = np.zeros(shape, np.uint8)
+            kst = np.zeros(tshape, np.float32)
+            vst = np.zeros(tshape, np.float32)
+            for o, sc in ((0, kst), (D, vst)):
+                sig = np.exp(tok_spread * rng.standard_normal((nb, block_size, Hk, 1)))
+                x = (sig * rng.standard_normal((nb, block_size, Hk, D))).astype(np.float32)
+                amax = np.abs(x).max(axis=-1)                     # [nb, bs, Hk]
+                s_tok = np.maximum(amax / 448.0, 1e-30).astype(np.float32)
+                cache[..., o:o + D] = e4m3_encode(x / s_tok[..., None])
+                sc[...] = s_tok.transpose(0, 2, 1)
+        else:
+            raise ValueError(values)
+        if v_ramp:
+            for b, L in enumerate(seq_lens):
+                t = np.arange(int(L))
+                blk = bt[b, t // block_size]
+                vst[blk, :, t % block_size] *= np.exp2(v_ramp * t / 256.0).astype(
+                    np.float32)[:, None]
+        _tok_scale_poison(kst, bt, seq_lens, used)
+        _tok_scale_poison(vst, bt, seq_lens, used)
+        fmt, k_scale, v_scale = FMT_FP8_E4M3_TOK, 1.0, 1.0
+    elif scales == "tensor":
+        fmt = FMT_FP8_E4M3
+        if values == "uniform_codes":
+            cache = E4M3_FINITE_CODES[rng.integers(0, 254, size=shape, dtype=np.uint8)]
+        elif values == "normal":
+            cache = np.zeros(shape, np.uint8)
+            x = rng.standard_normal((nb, block_size, Hk, 2 * D), dtype=np.float32)
+            cache[..., :2 * D] = e4m3_encode(x)
+        else:
+            raise ValueError(values)
     else:
-        raise ValueError(values)
+        raise ValueError(scales)
     _poison(cache, bt, seq_lens, used)
     q = rng.standard_normal((B * query_len, Hk * qg, D), dtype=np.float32)
     if q_dtype == "bf16":
         q = bf16_round(q)
     P = num_partitions or max(1, -(-int(seq_lens.max()) // TILE_GROUP))
-    return DecodeCase(name, q, q_dtype, cache, bt, seq_lens, Hk, FMT_FP8_E4M3,
+    return DecodeCase(name, q, q_dtype, cache, bt, seq_lens, Hk, fmt,
                       softmax_scale or 1.0 / math.sqrt(D), k_scale, v_scale, P,
-                      query_len=query_len)
+                      query_len=query_len, k_scale_tok=kst, v_scale_tok=vst)
 
 
 def make_fp4_case(name, seed, *, seq_lens, num_kv_heads, qg, head_dim=256, block_size=64,
@@ -278,6 +342,14 @@ def fp8_high() -> DecodeCase:
     return make_fp8_case("fp8_high", 3, seq_lens=fp8_high_seq_lens(), num_kv_heads=8, qg=8,
                          k_scale=0.05, v_scale=0.02, num_partitions=64, spare_blocks=256,
                          max_blocks=1024)
+
+
+def fp8_high_tok() -> DecodeCase:
+    """The high-batch fp8 shape (same lengths and table) with per-token K and V scales:
+    uniform finite e4m3 codes, scales 0.05 (K) and 0.02 (V) times lognormal(0, 0.5)."""
+    return make_fp8_case("fp8_high_tok", 3, seq_lens=fp8_high_seq_lens(), num_kv_heads=8,
+                         qg=8, k_scale=0.05, v_scale=0.02, num_partitions=64,
+                         spare_blocks=256, max_blocks=1024, scales="token")
 
 
 def fp8_high_mtp(query_len=2, qg=4) -> DecodeCase:

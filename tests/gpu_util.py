@@ -84,7 +84,8 @@ def oracle_decode(case, P=0):
                          num_kv_heads=case.num_kv_heads, kv_format=case.kv_format,
                          softmax_scale=case.softmax_scale, k_scale=case.k_scale,
                          v_scale=case.v_scale, rot_signs=case.rot_signs, num_partitions=P,
-                         query_len=case.query_len)
+                         query_len=case.query_len, k_scale_tok=case.k_scale_tok,
+                         v_scale_tok=case.v_scale_tok)
 
 
 def rel_err(got, ref):

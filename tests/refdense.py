@@ -52,6 +52,11 @@ def dense_kv(case, b: int, h: int):
     D = case.D
     if case.kv_format == 0:
         return e4m3_lib(slots[:, :D]), e4m3_lib(slots[:, D:2 * D])
+    if case.kv_format == 3:
+        # per-token scales indexed [physical block, kv head, position in block]
+        ks = case.k_scale_tok[blk, h, t % bs].astype(np.float64)
+        vs = case.v_scale_tok[blk, h, t % bs].astype(np.float64)
+        return e4m3_lib(slots[:, :D]) * ks[:, None], e4m3_lib(slots[:, D:2 * D]) * vs[:, None]
     lay = golden("p1_fp4_slot_layout.txt")
     assert D == lay["head_dim"]
     grp = lay["scale_group_dims"]

@@ -47,10 +47,16 @@ MUTANTS = {
                       "const int64_t qrow = (int64_t)b * QL + (QL - 1 - j);"),
     "mtp_reduce_row_map": ("double* o = out + (((int64_t)b * QL + j) * Hk * QG + h * QG + g) * D;",
                            "double* o = out + (((int64_t)b * QL) * Hk * QG + h * QR + r) * D;"),
+    "tok_scale_layout": ("const int64_t si = (blk * Hk + h) * block_size + t % block_size;",
+                         "const int64_t si = (blk * block_size + t % block_size) * Hk + h;"),
+    "tok_scale_kv_swap": ("const double sk = k_tok[si], sv = v_tok[si];",
+                          "const double sk = v_tok[si], sv = k_tok[si];"),
+    "tok_scale_v_missing": ("V[(size_t)t * D + d] *= sv;", "V[(size_t)t * D + d] *= 1.0;"),
 }
 
 PIN_SUITES = ["tests/test_oracle_codecs.py", "tests/test_oracle_attention.py",
-              "tests/test_oracle_index.py", "tests/test_oracle_mtp.py"]
+              "tests/test_oracle_index.py", "tests/test_oracle_mtp.py",
+              "tests/test_oracle_pertoken.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
