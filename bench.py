@@ -3,7 +3,8 @@
 Default workload (the headline): one decode step = uq_paged_decode + uq_paged_reduce over
 the high-batch fp8 batch (B=128, Hk=8, QG=8, D=128, L ~ U[4096, 16384], block 16, 64
 partitions of 256 tokens, per-tensor e4m3 K/V).  Other workloads (--workload):
-fp8_mid (B=16, L=16384), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions,
+fp8_mid (B=16, L=16384), fp8_high_tok (the high-batch shape with per-token f32 K and V
+scales: 264 algorithmic bytes per (token, head)), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions,
 e2m1 + e4m3 group scales, in-kernel rotation), the same fp8 and FP4 shapes with QL query
 rows per sequence (fp8_high_mtp{QL}_qg{QG}, fp4_d256_mtp{QL}_qg{QG}: each row has its own
 causal window), nvfp4_index_ql{QL}_h{H} (32 requests, L ~ U[1024, 32768]: one
@@ -91,7 +92,8 @@ def cpu_baseline_decode(case, n_seqs: int, min_seconds: float = 10.0):
                               num_kv_heads=sub.num_kv_heads, kv_format=sub.kv_format,
                               softmax_scale=sub.softmax_scale, k_scale=sub.k_scale,
                               v_scale=sub.v_scale, rot_signs=sub.rot_signs,
-                              query_len=sub.query_len), min_seconds)
+                              query_len=sub.query_len, k_scale_tok=sub.k_scale_tok,
+                              v_scale_tok=sub.v_scale_tok), min_seconds)
     return {"value": round(passes * sub.kv_bytes() / dt / 1e9, 4), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {n_seqs} of {case.B} sequences, all {case.num_kv_heads} kv heads "
@@ -122,6 +124,10 @@ def make_case(workload: str):
     if workload == "fp8_high":
         return synth.fp8_high(), ("fp8_high: B=128 Hk=8 QG=8 D=128 L~U[4096,16384] block=16 "
                                   "P=64 per-tensor e4m3 K/V, bf16 Q")
+    if workload == "fp8_high_tok":
+        return synth.fp8_high_tok(), ("fp8_high_tok: B=128 Hk=8 QG=8 D=128 L~U[4096,16384] "
+                                      "block=16 P=64 e4m3 K/V with per-token f32 K and V "
+                                      "scales, bf16 Q")
     if workload.startswith("fp8_high_mtp"):
         ql, qg = (int(x) for x in workload[len("fp8_high_mtp"):].split("_qg"))
         return synth.fp8_high_mtp(ql, qg), (
@@ -158,7 +164,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="fp8_high",
-                    help="fp8_high (default), fp8_mid, fp4_d256_qg{6,8,16}, fp4ue_d256_qg{6,8,16}, "
+                    help="fp8_high (default), fp8_mid, fp8_high_tok, fp4_d256_qg{6,8,16}, "
+                         "fp4ue_d256_qg{6,8,16}, "
                          "fp8_high_mtp{QL}_qg{QG} (QL*QG <= 8), "
                          "fp4[ue]_d256_mtp{QL}_qg{QG} (QL*QG <= 16), "
                          "nvfp4_index_ql{1,2,4,8}_h{1,2,4}")
@@ -221,8 +228,14 @@ def main():
         bt = torch.from_numpy(case.block_table).to(dev)
         sl = torch.from_numpy(case.seq_lens).to(dev)
         is_fp8 = fam == "fp8"
-        ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev) if is_fp8 else None
-        vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev) if is_fp8 else None
+        if case.k_scale_tok is not None:      # per-token scale tensors
+            ks = torch.from_numpy(case.k_scale_tok).to(dev)
+            vs = torch.from_numpy(case.v_scale_tok).to(dev)
+        elif is_fp8:
+            ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev)
+            vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev)
+        else:
+            ks = vs = None
         rot = torch.from_numpy(case.rot_signs).to(dev) if case.rot_signs is not None else None
         po, pm, pl = uq.alloc_partials(B, hk, QL * case.QG, D, P, dev)
         out = torch.empty(B * QL, Hq, D, dtype=qdt, device=dev)

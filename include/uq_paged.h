@@ -54,8 +54,14 @@ enum { UQ_F32 = 0, UQ_BF16 = 1 };
  *                         layout: 0/128/136/264, 272 bytes at D=256).  Supported for
  *                         D = 256.
  *   UQ_KV_FP4_E2M1_UE8M0S same slot with UE8M0 scales 2^(byte-127), byte 0 = 0.0 ([P1]
- *                         STEP F scale words).  Supported for D = 256. */
-enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 };
+ *                         STEP F scale words).  Supported for D = 256.
+ *   UQ_KV_FP8_E4M3_TOKSCALE  the UQ_KV_FP8_E4M3 slot with one f32 K scale and one f32 V
+ *                         scale per (token, kv head) ([P3] per_token_kv mode) held in two
+ *                         tensors [num_blocks, num_kv_heads, block_size] (physical block,
+ *                         head, position in the block) passed as k_scale / v_scale.
+ *                         Supported for D = 128. */
+enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2,
+       UQ_KV_FP8_E4M3_TOKSCALE = 3 };
 
 /* uq_paged_decode -- one decode step of paged attention, split over context partitions.
  *
@@ -75,8 +81,14 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  *                 strides comment).
  *   kv_cache      [num_blocks, block_size, num_kv_heads, slot_bytes] uint8.  block_size in
  *                 {16, 32, 64, 128, 256}; slot_bytes >= slot content and a multiple of 4.
- *   k_scale,      device float[1] per-tensor scales (fp8 format only), or NULL for 1.0
+ *   k_scale,      device float[1] per-tensor scales (UQ_KV_FP8_E4M3), or NULL for 1.0
  *   v_scale       ([P3] scales as 1-element device tensors).  Must be NULL for fp4.
+ *                 With UQ_KV_FP8_E4M3_TOKSCALE both are required: device float
+ *                 [num_blocks, num_kv_heads, block_size], 4-byte aligned; token t of
+ *                 sequence b in head h then decodes as k_t = e4m3(K codes) * k_scale[blk,
+ *                 h, t mod block_size], v_t likewise with v_scale (blk = its physical
+ *                 block), and s_t = softmax_scale * (q' . k_t).  Scales of visible
+ *                 tokens must be finite; those of other slots are never used.
  *   rot_signs     device int8[head_dim] of +-1 for the query rotation, or NULL.
  *                 fp4 formats only; 16-byte aligned.
  *   block_table   [num_seqs, bt_stride] int32 physical block ids.
@@ -98,8 +110,9 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2 }
  * run of consecutive partitions one workgroup streams (its length is chosen by the
  * launcher from the problem size and the device's compute units).
  * With num_partitions = 1 part_* hold exactly the statistics above.
- * Supported: (UQ_KV_FP8_E4M3, D = 128, QG <= 8) and (UQ_KV_FP4_E2M1_E4M3S or
- * UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else returns UQ_ERR_UNSUPPORTED.
+ * Supported: (UQ_KV_FP8_E4M3 or UQ_KV_FP8_E4M3_TOKSCALE, D = 128, QG <= 8) and
+ * (UQ_KV_FP4_E2M1_E4M3S or UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else
+ * returns UQ_ERR_UNSUPPORTED.
  * Device preconditions: 0 <= seq_lens[b] <= max_seq_len (larger values are clamped to
  * max_seq_len); block_table[b][t / block_size] in [0, num_blocks) for every t < L_b;
  * entries past a sequence's last block are never read; slot bytes of tokens t >= L_b are

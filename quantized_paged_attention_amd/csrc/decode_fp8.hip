@@ -31,6 +31,12 @@
 //     e4m3 hi/lo pair in columns 0-7 / 8-15.  PV is a 16x16x32 fp8 MFMA per 8 head dims
 //     with A = V^T: each lane pair loads 16 dims of 4 tokens with 16-byte loads, swaps
 //     halves (DPP) and byte-transposes (v_perm), so V codes go to the MFMA untouched.
+//   * Per-token scales (the PR's per_token_kv mode): each lane loads the K and V scale of
+//     one token of its 4-token quad (a 64-byte line per tile and head) and DPP-broadcasts
+//     them.  The K scale multiplies the score.  The V scale rides in P: P's pair holds
+//     p * v_scale_t / v_ref, with v_ref a running wave maximum of the V scales (raised,
+//     with the accumulators rescaled, only when a larger scale arrives), so the fp8
+//     pair keeps its range; acc * v_ref is the true sum at the end.
 //   * Loads are buffer loads through a descriptor per tile whose record count ends at
 //     the sequence's last visible token (invisible tokens read as zero, no branches);
 //     block ids come from a window preloaded before the stream.  The next tile pair's
@@ -53,7 +59,7 @@ struct VTile {
   i32x4 a, b;  // V bytes [16 (n/2), +16) of tokens 4r + 2 (n&1) and 4r + 2 (n&1) + 1
 };
 
-template <typename QT, int W>
+template <typename QT, int W, bool TOK>
 __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   // staging of the merged partition's bf16 output rows (at most 8 rows of 256 bytes), and
   // the states of waves 1..W-1 handed to wave 0 (per lane: 32 accumulators, m_run,
@@ -154,8 +160,9 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
     E = E < -100 ? -100 : E;
   }
   const float s_q = bits_f((uint32_t)(127 + 7 - E) << 23);
-  const float k_scale = a.k_scale ? *a.k_scale : 1.f;
-  const float v_scale = a.v_scale ? *a.v_scale : 1.f;
+  // per-tensor scales (the per-token ones are applied per token below)
+  const float k_scale = (!TOK && a.k_scale) ? *a.k_scale : 1.f;
+  const float v_scale = (!TOK && a.v_scale) ? *a.v_scale : 1.f;
   const float qk_mul = a.softmax_scale * k_scale * kLog2e / s_q;
 
   i32x8 q_own;  // hi(q s_q) in columns 0-7, lo(q s_q) in columns 8-15
@@ -248,6 +255,30 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
                                              (short)0, __builtin_amdgcn_readfirstlane(nvis * (int)pos),
                                              0x00020000);
   };
+  // Per-token scale descriptor of tile t of work tile-group kk: the tile's 16 scales of
+  // this head are contiguous in the [num_blocks, Hk, block_size] tensor; the record
+  // count ends at the last visible token (the others read as zero).
+  auto srsrc_of = [&](int kk, int t, const float* sbase) {
+    const int idx = (kk & 3) * 16 + t;
+    const int b_lo = __builtin_amdgcn_readlane(win_lo, idx);
+    const int b_hi = __builtin_amdgcn_readlane(win_hi, idx);
+    const int blk = (kk & 7) >= 4 ? b_hi : b_lo;
+    const int tok = (first_tg + kk * step) * kTileGroup + 16 * t;
+    int nvis = L - tok;
+    nvis = kk >= n_tg ? 0 : (nvis < 0 ? 0 : (nvis > 16 ? 16 : nvis));
+    const uint64_t base = (uint64_t)(sbase + ((int64_t)blk * a.Hk + h) * a.block_size +
+                                     (tok & (a.block_size - 1)));
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                             (short)0, __builtin_amdgcn_readfirstlane(nvis * 4),
+                                             0x00020000);
+  };
+  // lane (r, n) loads the scale of token 4 r + (n & 3) of a tile
+  const uint32_t s_off = 4u * (uint32_t)(4 * r + (n & 3));
+  auto load_s = [&](__amdgpu_buffer_rsrc_t rs) {
+    return bits_f((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, s_off, 0, kAuxNT));
+  };
   auto load_k = [&](__amdgpu_buffer_rsrc_t rs, KTile& d) {
     d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kAuxNT);
     d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 64, 0, kAuxNT);
@@ -266,15 +297,29 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   // branches except a rare wave-uniform softmax rescale.
   KTile kp[2][2];  // [pair parity][tile]: K is loaded two pairs ahead
   VTile vp[2];
+  // per-token scales: K scales travel with the K loads, V scales with the V loads (issued
+  // just before them, so waiting for a scale never waits for the V bytes)
+  float ksc[2][2] = {{0.f, 0.f}, {0.f, 0.f}}, vsc[2] = {0.f, 0.f};
+  float v_ref = 0.f, v_inv = 0.f;  // running wave maximum of |V scale| and its inverse
   {
     const auto r0 = rsrc_of(0, 0), r1 = rsrc_of(0, 1);
     load_k(r0, kp[0][0]);
     load_k(r1, kp[0][1]);
+    if constexpr (TOK) {
+      ksc[0][0] = load_s(srsrc_of(0, 0, a.k_scale));
+      ksc[0][1] = load_s(srsrc_of(0, 1, a.k_scale));
+      vsc[0] = load_s(srsrc_of(0, 0, a.v_scale));
+      vsc[1] = load_s(srsrc_of(0, 1, a.v_scale));
+    }
     load_v(r0, vp[0]);
     load_v(r1, vp[1]);
     const auto r2 = rsrc_of(0, 2), r3 = rsrc_of(0, 3);
     load_k(r2, kp[1][0]);
     load_k(r3, kp[1][1]);
+    if constexpr (TOK) {
+      ksc[1][0] = load_s(srsrc_of(0, 2, a.k_scale));
+      ksc[1][1] = load_s(srsrc_of(0, 3, a.k_scale));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -303,9 +348,15 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         const i32x8 kop = {kt.a[0], kt.a[1], kt.a[2], kt.a[3], kt.b[0], kt.b[1], kt.b[2], kt.b[3]};
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own, z, 0, 0, 0, 127, 0, 127);
+        float mul[4] = {qk_mul, qk_mul, qk_mul, qk_mul};
+        if constexpr (TOK) {  // the K scales of this lane's tokens 4r .. 4r+3
+          quad_values(ksc[pr & 1][tt], mul);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mul[j] *= qk_mul;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float v = (z[j] + row_ror8(z[j])) * qk_mul;
+          const float v = (z[j] + row_ror8(z[j])) * mul[j];
           s[tt][j] = pair_start + 16 * tt + 4 * r + j < L_row ? v : -INFINITY;
         }
       }
@@ -317,6 +368,10 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         const auto rk0 = rsrc_of(pk_k, pk_t0), rk1 = rsrc_of(pk_k, pk_t0 + 1);
         load_k(rk0, kp[pr & 1][0]);
         load_k(rk1, kp[pr & 1][1]);
+        if constexpr (TOK) {
+          ksc[pr & 1][0] = load_s(srsrc_of(pk_k, pk_t0, a.k_scale));
+          ksc[pr & 1][1] = load_s(srsrc_of(pk_k, pk_t0 + 1, a.k_scale));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -336,6 +391,26 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         for (int m = 0; m < 8; ++m) acc[m] *= alpha;
         m_run = m_new;
       }
+      // per-token V scales of this lane's tokens; the reference v_ref is raised (and the
+      // accumulators rescaled) when a larger scale arrives, so p v_scale / v_ref <= p
+      float vq[2][4];
+      if constexpr (TOK) {
+        quad_values(vsc[0], vq[0]);
+        quad_values(vsc[1], vq[1]);
+        float vmx = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vmx = fmaxf(vmx, fabsf(vq[tt][j]));
+        vmx = max_across_rows(vmx);  // equal on every lane
+        if (__builtin_amdgcn_ballot_w64(vmx > v_ref)) {  // wave-uniform, rare
+          const float f = v_ref / vmx;  // 0 before the first nonzero scale
+#pragma unroll
+          for (int m = 0; m < 8; ++m) acc[m] *= f;
+          v_ref = vmx;
+          v_inv = 1.f / vmx;
+        }
+      }
       // a row that has seen no token (m_run = -inf) has only -inf scores: weight 0
       const float m8 = m_run == -INFINITY ? 0.f : m_run - 8.f;
       int pw[2];
@@ -346,6 +421,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         for (int j = 0; j < 4; ++j) {
           y[j] = fast_exp2(s[tt][j] - m8);
           l_run += y[j];
+          if constexpr (TOK) y[j] *= vq[tt][j] * v_inv;
         }
         int hw = cvt_pk_e4m3<false>(y[0], y[1], 0);
         hw = cvt_pk_e4m3<true>(y[2], y[3], hw);
@@ -374,6 +450,10 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       {
+        if constexpr (TOK) {
+          vsc[0] = load_s(srsrc_of(pf_k, pf_t0, a.v_scale));
+          vsc[1] = load_s(srsrc_of(pf_k, pf_t0 + 1, a.v_scale));
+        }
         const auto rv0 = rsrc_of(pf_k, pf_t0), rv1 = rsrc_of(pf_k, pf_t0 + 1);
         load_v(rv0, vp[0]);
         load_v(rv1, vp[1]);
@@ -389,6 +469,11 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 
   }
 
+  // per-token V scales: the accumulators hold the sums in units of v_ref
+  if constexpr (TOK) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] *= v_ref;
+  }
   // ---- merge the W wave states into partition part_first: a lane's state belongs to
   //      its column (query head), so the merge is lane-local once the states meet in LDS
   const float l_tot = sum_across_rows(l_run);
@@ -470,7 +555,8 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t stream) {
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales,
+                             hipStream_t stream) {
   constexpr int W = 4;
   const int R = a.run_len > 0 ? a.run_len : 1;
   const int64_t groups = ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
@@ -478,10 +564,16 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t str
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)items);
-  if (q_is_f32)
-    hipLaunchKernelGGL((decode_fp8_kernel<float, W>), grid, dim3(64 * W), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_fp8_kernel<uint16_t, W>), grid, dim3(64 * W), 0, stream, a);
+  if (tok_scales) {
+    if (q_is_f32)
+      hipLaunchKernelGGL((decode_fp8_kernel<float, W, true>), grid, dim3(64 * W), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_fp8_kernel<uint16_t, W, true>), grid, dim3(64 * W), 0, stream, a);
+  } else if (q_is_f32) {
+    hipLaunchKernelGGL((decode_fp8_kernel<float, W, false>), grid, dim3(64 * W), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_fp8_kernel<uint16_t, W, false>), grid, dim3(64 * W), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ bool valid_block_size(int bs) {
 }
 
 int slot_content(int fmt, int D) {
-  if (fmt == UQ_KV_FP8_E4M3) return 2 * D;
+  if (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) return 2 * D;
   if (fmt == UQ_KV_FP4_E2M1_E4M3S || fmt == UQ_KV_FP4_E2M1_UE8M0S)
     return D % 32 ? -1 : 2 * (D / 2 + D / 32);
   return -1;
@@ -162,7 +162,12 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
   if ((int64_t)a.pos_stride * block_size > (int64_t)1 << 31)
     return fail(UQ_ERR_UNSUPPORTED, "a physical block larger than 2 GiB is not supported");
 
-  if (kv_format == UQ_KV_FP8_E4M3) {
+  if (kv_format == UQ_KV_FP8_E4M3 || kv_format == UQ_KV_FP8_E4M3_TOKSCALE) {
+    const bool tok = kv_format == UQ_KV_FP8_E4M3_TOKSCALE;
+    if (tok && num_seqs > 0 && (!k_scale || !v_scale))
+      return fail(UQ_ERR_INVALID_ARG, "per-token scales need both k_scale and v_scale tensors");
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3)
+      return fail(UQ_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
     if (head_dim != 128) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports head_dim 128 only");
     if (query_len * QG > 8)
       return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports query_len x query group up to 8 rows (got %d x %d)",
@@ -170,7 +175,7 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
     if (rot_signs) return fail(UQ_ERR_UNSUPPORTED, "query rotation is supported with fp4 caches only");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache needs slot_bytes a multiple of 16");
     if (num_seqs == 0) return ok();
-    return launch_status(uq::launch_decode_fp8(a, q_dtype == UQ_F32, static_cast<hipStream_t>(stream)),
+    return launch_status(uq::launch_decode_fp8(a, q_dtype == UQ_F32, tok, static_cast<hipStream_t>(stream)),
                          "decode_fp8");
   }
   if (kv_format == UQ_KV_FP4_E2M1_E4M3S || kv_format == UQ_KV_FP4_E2M1_UE8M0S) {

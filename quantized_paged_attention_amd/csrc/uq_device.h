@@ -46,6 +46,16 @@ __device__ __forceinline__ float row_ror8(float v) {
   return bits_f((uint32_t)__builtin_amdgcn_mov_dpp((int)f_bits(v), 0x128, 0xF, 0xF, false));
 }
 
+// The four values of the lane's quad (lanes 4k .. 4k+3), each broadcast to every lane of
+// the quad (DPP quad_perm [j, j, j, j] for j = 0..3).
+__device__ __forceinline__ void quad_values(float v, float out[4]) {
+  const int x = (int)f_bits(v);
+  out[0] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, false));
+  out[1] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, false));
+  out[2] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, false));
+  out[3] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -15,8 +15,8 @@ struct DecodeArgs {
   int64_t blk_stride;          // bytes per physical block = block_size * pos_stride
   int32_t pos_stride;          // bytes per token position = num_kv_heads * slot_bytes
   int32_t slot_bytes;
-  const float* k_scale;        // nullable device scalars
-  const float* v_scale;
+  const float* k_scale;        // nullable device scalars, or per-token scale tensors
+  const float* v_scale;        // [num_blocks, Hk, block_size] (fp8 per-token format)
   const int8_t* rot_signs;     // nullable
   const int32_t* bt;
   int32_t bt_stride;
@@ -58,7 +58,7 @@ struct IndexArgs {
 };
 
 // Each returns the hipError_t of its launch.
-hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, hipStream_t stream);
+hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales, hipStream_t stream);
 hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, bool ue8m0, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, bool out_is_f32, hipStream_t stream);
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream);

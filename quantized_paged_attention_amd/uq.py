@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libuq.so")
 UQ_OK, UQ_ERR_INVALID_ARG, UQ_ERR_UNSUPPORTED, UQ_ERR_LAUNCH = 0, 1, 2, 3
 UQ_F32, UQ_BF16 = 0, 1
 UQ_KV_FP8_E4M3, UQ_KV_FP4_E2M1_E4M3S, UQ_KV_FP4_E2M1_UE8M0S = 0, 1, 2
+UQ_KV_FP8_E4M3_TOKSCALE = 3
 
 EXPORTS = ("uq_paged_decode", "uq_paged_reduce", "uq_paged_decode_mtp", "uq_paged_reduce_mtp",
            "uq_index_score",
@@ -131,7 +132,8 @@ def paged_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch
     """uq_paged_decode (query_len = 1) or uq_paged_decode_mtp on torch tensors: query
     [B*QL, Hq, D] (strided over rows and Hq, D contiguous; row b*QL + j is query j of
     sequence b); kv_cache [num_blocks, block_size, Hk, slot] uint8; partials
-    [B, Hk, P, QL*QG(, D)]."""
+    [B, Hk, P, QL*QG(, D)].  k_scale / v_scale: float32 [1] per-tensor scales, or with
+    kv_format UQ_KV_FP8_E4M3_TOKSCALE the per-token scales [num_blocks, Hk, block_size]."""
     lib = load_library()
     if query.dim() != 3 or query.stride(2) != 1:
         raise ValueError("query must be [B, Hq, D] with a contiguous head dim")
@@ -160,6 +162,10 @@ def paged_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_table: torch
     for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
         if t is not None:
             _need(t, torch.float32, nm)
+            if kv_format == UQ_KV_FP8_E4M3_TOKSCALE and (
+                    tuple(t.shape) != (nb, hk, bs) or not t.is_contiguous()):
+                raise ValueError(f"{nm} must be a contiguous [num_blocks, Hk, block_size] "
+                                 "tensor of per-token scales")
     if rot_signs is not None:
         _need(rot_signs, torch.int8, "rot_signs")
     if seq_lens.shape != (B,) or block_table.shape[0] != B:

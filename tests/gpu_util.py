@@ -49,14 +49,20 @@ def q_tensor(case, strided: bool = False) -> torch.Tensor:
 
 
 def device_case(case):
+    if case.kv_format == synth.FMT_FP8_E4M3:
+        ks = torch.tensor([case.k_scale], dtype=torch.float32, device=DEV)
+        vs = torch.tensor([case.v_scale], dtype=torch.float32, device=DEV)
+    elif case.kv_format == synth.FMT_FP8_E4M3_TOK:
+        ks = torch.from_numpy(case.k_scale_tok).to(DEV)
+        vs = torch.from_numpy(case.v_scale_tok).to(DEV)
+    else:
+        ks = vs = None
     return dict(
         cache=torch.from_numpy(case.cache).to(DEV),
         bt=torch.from_numpy(case.block_table).to(DEV),
         sl=torch.from_numpy(case.seq_lens).to(DEV),
-        ks=(torch.tensor([case.k_scale], dtype=torch.float32, device=DEV)
-            if case.kv_format == synth.FMT_FP8_E4M3 else None),
-        vs=(torch.tensor([case.v_scale], dtype=torch.float32, device=DEV)
-            if case.kv_format == synth.FMT_FP8_E4M3 else None),
+        ks=ks,
+        vs=vs,
         rot=(torch.from_numpy(case.rot_signs).to(DEV) if case.rot_signs is not None else None),
     )
 

@@ -71,6 +71,12 @@ def decode_args(**over):
      uq.UQ_ERR_INVALID_ARG),                              # rotation signs not 16-byte aligned
     (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 8, ks=FAKE), uq.UQ_ERR_INVALID_ARG),
     (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=268, Hq=8 * 8), uq.UQ_ERR_INVALID_ARG),
+    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE), uq.UQ_ERR_INVALID_ARG),        # scales required
+    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE), uq.UQ_ERR_INVALID_ARG),
+    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE + 2), uq.UQ_ERR_INVALID_ARG),
+    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE, D=64, slot=128),
+     uq.UQ_ERR_UNSUPPORTED),
+    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE, Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),
 ])
 def test_decode_validation(lib, over, status):
     st = lib.uq_paged_decode(*decode_args(**over))
