@@ -22,10 +22,15 @@
 //     8-fold merge the partials stay in L2 until the kernel ends and the store cost
 //     vanishes.
 //   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
-//     from HBM (lane = token, 32 head dims per lane: bytes [16r, 16r+16) and
-//     [64+16r, 64+16r+16)) and B = the query group as an e4m3 hi/lo pair -- columns
-//     0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row rotate.  s_q is a per-row
-//     power of two: the pair reproduces a bf16 query exactly.
+//     from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query group as an
+//     e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
+//     rotate.  s_q is a per-row power of two: the pair reproduces a bf16 query exactly.
+//   * K is read in whole 128-byte lines: each of a tile's two K loads covers 8 tokens x
+//     the full K line (lane (r, n): token (n & 7) or 8 + (n & 7), 16-byte chunk 2r or
+//     2r+1), and one DPP swap with lane n ^ 8 gives every lane chunks 2r, 2r+1 of its
+//     own token n.  Measured on MI355X with a load-only kernel in this kernel's order:
+//     loads of 16 tokens x half a line stream at 4.5 TB/s, of 8 tokens x whole lines at
+//     6.2 TB/s.
 //   * Softmax is online in exp2 units against a reference max raised (with 4 units of
 //     headroom) only when a score exceeds it, p = 2^(s - ref + 8) <= 256 split into an
 //     e4m3 hi/lo pair in columns 0-7 / 8-15.  PV is a 16x16x32 fp8 MFMA per 8 head dims
@@ -53,7 +58,8 @@ constexpr int kTiles = 16;     // tiles of 16 tokens per tile-group
 constexpr int kAuxNT = 2;      // KV loads non-temporal (buffer aux bit 1, see below)
 
 struct KTile {
-  i32x4 a, b;  // K bytes [16r, 16r+16) and [64+16r, 64+16r+16) of token n
+  i32x4 a, b;  // a: K chunk 2r + (n >> 3) of token n & 7; b: chunk 2r + 1 - (n >> 3) of token
+               // 8 + (n & 7) (16-byte chunks of the 128-byte K line)
 };
 struct VTile {
   i32x4 a, b;  // V bytes [16 (n/2), +16) of tokens 4r + 2 (n&1) and 4r + 2 (n&1) + 1
@@ -114,8 +120,8 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   const int g = n & 7;
   const bool lo_col = n >= 8;
 
-  // ---- query operands.  Byte j of lane group r holds head dim
-  //      d = j < 16 ? 16 r + j : 64 + 16 r + (j - 16)   (same map as the K loads)
+  // ---- query operands.  Byte j of lane group r holds head dim d = 32 r + j (the K
+  //      operand's map after the chunk exchange)
   float x[32];
   // column g holds unit row g = (query qj, head qh) of QL query rows x QG heads; query qj
   // sees the tokens t < L_row (the causal window of its row)
@@ -126,25 +132,22 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   {
     const QT* qp = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.QL + qj) * a.q_ss +
                    (int64_t)(h * a.QG + qh) * a.q_sh;
+    const QT* src = qp + 32 * r;
+    if constexpr (sizeof(QT) == 4) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const QT* src = qp + half * 64 + 16 * r;
-      if constexpr (sizeof(QT) == 4) {
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * c);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * c);
+        for (int e = 0; e < 4; ++e) x[4 * c + e] = v[e];
+      }
+    } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[half * 16 + 4 * c + e] = v[e];
-        }
-      } else {
+      for (int c = 0; c < 4; ++c) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(src + 8 * c);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const i32x4 v = *reinterpret_cast<const i32x4*>(src + 8 * c);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[half * 16 + 8 * c + 2 * e] = bf16_to_f((uint32_t)v[e] & 0xFFFFu);
-            x[half * 16 + 8 * c + 2 * e + 1] = bf16_to_f((uint32_t)v[e] >> 16);
-          }
+        for (int e = 0; e < 4; ++e) {
+          x[8 * c + 2 * e] = bf16_to_f((uint32_t)v[e] & 0xFFFFu);
+          x[8 * c + 2 * e + 1] = bf16_to_f((uint32_t)v[e] >> 16);
         }
       }
     }
@@ -188,7 +191,11 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t pos = (uint32_t)a.pos_stride;
-  const uint32_t k_off = n * pos + 16 * r;
+  // K loads: a = token n & 7, chunk 2r + (n >> 3); b = token 8 + (n & 7), chunk
+  // 2r + 1 - (n >> 3): each load reads 8 tokens x whole 128-byte K lines
+  const bool hi_n = n >= 8;
+  const uint32_t ka_off = (uint32_t)(n & 7) * pos + 16u * (uint32_t)(2 * r + (hi_n ? 1 : 0));
+  const uint32_t kb_off = (uint32_t)(8 + (n & 7)) * pos + 16u * (uint32_t)(2 * r + (hi_n ? 0 : 1));
   // V: lane pair (2h, 2h+1) fetches dims [16h, 16h+16) of tokens 4r..4r+3 with two
   // 16-byte loads per lane (the even lane tokens 4r, 4r+1, the odd lane 4r+2, 4r+3) and
   // the pair swaps halves, so each lane ends with dims [8n, 8n+8) of all four tokens.
@@ -280,8 +287,8 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
     return bits_f((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, s_off, 0, kAuxNT));
   };
   auto load_k = [&](__amdgpu_buffer_rsrc_t rs, KTile& d) {
-    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off, 0, kAuxNT);
-    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, k_off + 64, 0, kAuxNT);
+    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, ka_off, 0, kAuxNT);
+    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, kb_off, 0, kAuxNT);
   };
   auto load_v = [&](__amdgpu_buffer_rsrc_t rs, VTile& d) {
     d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kAuxNT);
@@ -345,7 +352,15 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const KTile& kt = kp[pr & 1][tt];
-        const i32x8 kop = {kt.a[0], kt.a[1], kt.a[2], kt.a[3], kt.b[0], kt.b[1], kt.b[2], kt.b[3]};
+        // lane n < 8 keeps a (its chunk 2r) and sends b; lane n >= 8 keeps b and sends a;
+        // the chunk received from lane n ^ 8 is chunk 2r + 1 of this lane's token
+        i32x8 kop;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int send = hi_n ? kt.a[e] : kt.b[e];
+          kop[e] = hi_n ? kt.b[e] : kt.a[e];
+          kop[4 + e] = (int)f_bits(row_ror8(bits_f((uint32_t)send)));
+        }
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
         z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own, z, 0, 0, 0, 127, 0, 127);
         float mul[4] = {qk_mul, qk_mul, qk_mul, qk_mul};
