@@ -65,20 +65,25 @@ struct VTile {
   i32x4 a, b;  // V bytes [16 (n/2), +16) of tokens 4r + 2 (n&1) and 4r + 2 (n&1) + 1
 };
 
-template <typename QT, int W, bool TOK>
+template <typename QT, int W, bool TOK, bool HG>
 __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
-  // staging of the merged partition's bf16 output rows (at most 8 rows of 256 bytes), and
-  // the states of waves 1..W-1 handed to wave 0 (per lane: 32 accumulators, m_run,
-  // m_true, l)
-  __shared__ __attribute__((aligned(16))) uint16_t o_stage[8 * kD];
-  __shared__ __attribute__((aligned(16))) float st_acc[W > 1 ? W - 1 : 1][32][64];
-  __shared__ float st_ml[W > 1 ? W - 1 : 1][3][64];
+  // staging of the merged partition's bf16 output rows (at most 8 rows of 256 bytes; one
+  // stage per wave with head groups), and the states of waves 1..W-1 handed to wave 0
+  // (per lane: 32 accumulators, m_run, m_true, l)
+  constexpr bool kMerge = W > 1 && !HG;
+  __shared__ __attribute__((aligned(16))) uint16_t o_stage[(HG ? W : 1) * 8 * kD];
+  __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][32][64];
+  __shared__ float st_ml[kMerge ? W - 1 : 1][3][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t item = blockIdx.x;  // (sequence, kv head, group of W runs)
-  const int h = (int)(item % a.Hk);
-  const int b = (int)((item / a.Hk) % a.B);
-  const int grp = (int)(item / ((int64_t)a.Hk * a.B));
+  // HG: (group of W kv heads, sequence, run): wave w streams kv head W g + w over the
+  // run's partitions, so the W waves read neighbouring slots of the same blocks together.
+  // Otherwise: (kv head, sequence, group of W runs) with the W runs split over the waves.
+  const int64_t item = blockIdx.x;
+  const int nhs = HG ? a.Hk / W : a.Hk;
+  const int h = (int)(item % nhs) * (HG ? W : 1) + (HG ? wave : 0);
+  const int b = (int)((item / nhs) % a.B);
+  const int grp = (int)(item / ((int64_t)nhs * a.B));
 
   int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);  // wave-uniform
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
@@ -93,7 +98,26 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   const int pmax = a.P < ntg ? a.P : ntg;
   const int R = a.run_len > 0 ? a.run_len : 1;
   int part_first, p_end, first_tg, n_tg, step;
-  if (a.run_len > 0) {
+  if (HG && a.run_len > 0) {
+    // this sequence's pmax partitions in G nearly equal runs of at most R; every wave
+    // streams the whole run for its own kv head
+    const int G = (pmax + R - 1) / R;
+    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
+    part_first = (int)((int64_t)grp * pmax / G);
+    p_end = (int)((int64_t)(grp + 1) * pmax / G);
+    first_tg = part_first;
+    n_tg = p_end - part_first;
+    step = 1;
+  } else if (HG) {
+    // partition grp (its strided tile-groups) for each wave's kv head
+    part_first = grp;
+    if (part_first >= pmax) return;  // workgroup-uniform
+    p_end = part_first + 1;
+    first_tg = part_first;
+    n_tg = (ntg - first_tg + a.P - 1) / a.P;
+    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+    step = a.P;
+  } else if (a.run_len > 0) {
     // this sequence's pmax partitions in G nearly equal groups of at most W * R, and a
     // group's m partitions nearly equally over its W waves (no wave idles at the merge
     // for a whole run)
@@ -492,7 +516,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   // ---- merge the W wave states into partition part_first: a lane's state belongs to
   //      its column (query head), so the merge is lane-local once the states meet in LDS
   const float l_tot = sum_across_rows(l_run);
-  if constexpr (W > 1) {
+  if constexpr (kMerge) {
     if (wave > 0) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
@@ -507,22 +531,26 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   }
   // statistics relative to the true maximum M over the workgroup's tokens
   float M = m_true;
+  if constexpr (kMerge) {
 #pragma unroll
-  for (int w = 1; w < W; ++w) M = fmaxf(M, st_ml[w - 1][1][lane]);
+    for (int w = 1; w < W; ++w) M = fmaxf(M, st_ml[w - 1][1][lane]);
+  }
   // 0 for a wave without tokens of this row (m_run = -inf), and for every wave when the
   // row saw no token in the workgroup (M = -inf: an empty state m = -inf, l = 0)
   float f0 = M == -INFINITY ? 0.f : fast_exp2(m_run - 8.f - M);
   float l_all = l_tot * f0;
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc[m] *= f0;
+  if constexpr (kMerge) {
 #pragma unroll
-  for (int w = 1; w < W; ++w) {
-    const float fw = M == -INFINITY ? 0.f : fast_exp2(st_ml[w - 1][0][lane] - 8.f - M);
-    l_all += st_ml[w - 1][2][lane] * fw;
+    for (int w = 1; w < W; ++w) {
+      const float fw = M == -INFINITY ? 0.f : fast_exp2(st_ml[w - 1][0][lane] - 8.f - M);
+      l_all += st_ml[w - 1][2][lane] * fw;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][j] += st_acc[w - 1][4 * m + j][lane] * fw;
+        for (int j = 0; j < 4; ++j) acc[m][j] += st_acc[w - 1][4 * m + j][lane] * fw;
+    }
   }
   {
     const float inv = v_scale / (l_all > 0.f ? l_all : 1.f);
@@ -531,6 +559,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
     // stores: written from registers directly it would be 16-byte pieces at 64-byte
     // stride, and such scattered partial-line writes slow the concurrent KV stream.
     const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * NR;
+    uint16_t* stage = o_stage + (HG ? wave : 0) * 8 * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       i32x4 w;
@@ -540,7 +569,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
         w[e] = (int)pack_bf16x2(o0, o1);
       }
-      if (n < NR) *reinterpret_cast<i32x4*>(o_stage + n * kD + 32 * r + 8 * j) = w;
+      if (n < NR) *reinterpret_cast<i32x4*>(stage + n * kD + 32 * r + 8 * j) = w;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
@@ -551,7 +580,7 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       const int byte = c * 1024 + 16 * lane;
       if (byte < nbytes)
         *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
-            *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(o_stage) + byte);
+            *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) + byte);
     }
     if (n < NR && r == 0) {
       a.part_m[row0 + n] = M * kLn2;
@@ -573,22 +602,32 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales,
                              hipStream_t stream) {
   constexpr int W = 4;
+  const bool hg = a.head_groups != 0;
+  if (hg && a.Hk % W != 0) return hipErrorInvalidValue;
   const int R = a.run_len > 0 ? a.run_len : 1;
-  const int64_t groups = ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
-  const int64_t items = groups * a.B * a.Hk;
+  // HG: one workgroup per (W kv heads, sequence, run); else per (kv head, sequence, W runs)
+  const int64_t groups = hg ? (int64_t)a.runs
+                            : ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
+  const int64_t items = groups * a.B * (hg ? a.Hk / W : a.Hk);
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)items);
-  if (tok_scales) {
-    if (q_is_f32)
-      hipLaunchKernelGGL((decode_fp8_kernel<float, W, true>), grid, dim3(64 * W), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_fp8_kernel<uint16_t, W, true>), grid, dim3(64 * W), 0, stream, a);
-  } else if (q_is_f32) {
-    hipLaunchKernelGGL((decode_fp8_kernel<float, W, false>), grid, dim3(64 * W), 0, stream, a);
+  const dim3 grid((unsigned)items), block(64 * W);
+#define UQ_FP8_LAUNCH(QT, TOK, HG) \
+  hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG>), grid, block, 0, stream, a)
+  if (hg) {
+    if (tok_scales) {
+      if (q_is_f32) UQ_FP8_LAUNCH(float, true, true); else UQ_FP8_LAUNCH(uint16_t, true, true);
+    } else {
+      if (q_is_f32) UQ_FP8_LAUNCH(float, false, true); else UQ_FP8_LAUNCH(uint16_t, false, true);
+    }
   } else {
-    hipLaunchKernelGGL((decode_fp8_kernel<uint16_t, W, false>), grid, dim3(64 * W), 0, stream, a);
+    if (tok_scales) {
+      if (q_is_f32) UQ_FP8_LAUNCH(float, true, false); else UQ_FP8_LAUNCH(uint16_t, true, false);
+    } else {
+      if (q_is_f32) UQ_FP8_LAUNCH(float, false, false); else UQ_FP8_LAUNCH(uint16_t, false, false);
+    }
   }
+#undef UQ_FP8_LAUNCH
   return hipGetLastError();
 }
 

@@ -279,3 +279,30 @@ def test_graph_replay_matches_eager(fmt):
         got = out.float().cpu().numpy().astype(np.float64)
         assert np.array_equal(got, eager), f"replay {i}"
         _ = (q.float() * 2).sum().item()      # eager work between replays
+
+
+@pytest.mark.parametrize("hk", [4, 8])
+@pytest.mark.parametrize("P", [1, 3, 64])
+@pytest.mark.parametrize("q_dtype", ["bf16", "f32"])
+def test_head_group_workgroups(hk, P, q_dtype):
+    """Kv head counts that are multiples of 4 run as head groups (a workgroup's waves take
+    4 neighbouring kv heads of one run of partitions); P = 1 and 3 make partitions own
+    several strided tile-groups."""
+    need_gpu()
+    case = small(hk=hk, qg=8 if hk == 4 else 4, q_dtype=q_dtype, seed=70 + hk + P,
+                 lens=(1, 16, 17, 255, 257, 700, 2049, 4000, 5000))
+    log(f"case fp8 head groups hk={hk} P={P} q={q_dtype}")
+    got, _ = run_decode(case, P=P)
+    assert_decode_close(got, oracle_decode(case), f"head groups hk={hk} P={P} {q_dtype}")
+
+
+def test_head_group_large_batch_runs():
+    """Many sequences with Hk=8 so the launcher picks long runs of partitions per
+    workgroup (the high-batch regime), lengths from 1 to 9000."""
+    need_gpu()
+    rng = np.random.default_rng(75)
+    lens = list(rng.integers(1, 9000, size=96)) + [1, 255, 256, 257]
+    case = small(hk=8, qg=8, lens=tuple(int(x) for x in lens), seed=76)
+    log(f"case fp8 head groups B={case.B} hk=8 P=64")
+    got, _ = run_decode(case, P=64)
+    assert_decode_close(got, oracle_decode(case), "head groups large batch")

@@ -38,6 +38,18 @@ def test_fp8_query_rows(ql, qg, P):
     assert_decode_close(got, oracle_decode(case), f"fp8 mtp ql={ql} qg={qg} P={P}")
 
 
+@pytest.mark.parametrize("ql,qg", [(2, 4), (4, 1)])
+@pytest.mark.parametrize("P", [1, 12])
+def test_fp8_query_rows_head_groups(ql, qg, P):
+    """Query rows with Hk=4 (head-group workgroups)."""
+    need_gpu()
+    case = fp8(ql, qg, seed=260 + 10 * ql + qg + P, hk=4, k_scale=0.05, v_scale=0.02,
+               values="uniform_codes")
+    log(f"case fp8 mtp head groups ql={ql} qg={qg} P={P}")
+    got, _ = run_decode(case, P=P)
+    assert_decode_close(got, oracle_decode(case), f"fp8 mtp hg ql={ql} qg={qg} P={P}")
+
+
 @pytest.mark.parametrize("kind", ["e4m3", "ue8m0"])
 @pytest.mark.parametrize("ql,qg", [(2, 8), (4, 4), (2, 6), (4, 1), (3, 5)])
 def test_fp4_query_rows(ql, qg, kind):

@@ -136,3 +136,13 @@ def test_fp8_high_tok_sampled():
     sub.block_table = case.block_table[pick]
     sub.seq_lens = case.seq_lens[pick]
     assert_decode_close(got[pick], oracle_decode(sub), "fp8_high_tok sample")
+
+
+@pytest.mark.parametrize("P", [1, 64])
+def test_head_groups_per_token(P):
+    """Per-token scales with Hk=8 (head-group workgroups)."""
+    need_gpu()
+    case = tok(69, hk=8, qg=4, lens=(1, 17, 256, 257, 1000, 3000), v_ramp=1.0)
+    log(f"case fp8 per-token head groups P={P}")
+    got, _ = run_decode(case, P=P)
+    assert_decode_close(got, oracle_decode(case), f"per-token head groups P={P}")
