@@ -168,7 +168,7 @@ def main():
     ap.add_argument("--workload", default="fp8_high",
                     help="fp8_high (default), fp8_mid, fp8_high_tok, fp4_d256_qg{6,8,16}, "
                          "fp4ue_d256_qg{6,8,16}, "
-                         "fp8_high_mtp{QL}_qg{QG} (QL*QG <= 8), "
+                         "fp8_high_mtp{QL}_qg{QG} (QL*QG <= 64), "
                          "fp4[ue]_d256_mtp{QL}_qg{QG} (QL*QG <= 16), "
                          "nvfp4_index_ql{1,2,4,8}_h{1,2,4}")
     ap.add_argument("--cpu-seqs", type=int, default=128,

@@ -110,9 +110,11 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2,
  * run of consecutive partitions one workgroup streams (its length is chosen by the
  * launcher from the problem size and the device's compute units).
  * With num_partitions = 1 part_* hold exactly the statistics above.
- * Supported: (UQ_KV_FP8_E4M3 or UQ_KV_FP8_E4M3_TOKSCALE, D = 128, QG <= 8) and
+ * Supported: (UQ_KV_FP8_E4M3 or UQ_KV_FP8_E4M3_TOKSCALE, D = 128, QG <= 64) and
  * (UQ_KV_FP4_E2M1_E4M3S or UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else
- * returns UQ_ERR_UNSUPPORTED.
+ * returns UQ_ERR_UNSUPPORTED ([P3] wide GQA: groups above 16 rows).  The fp8 kernels
+ * carry up to 16 query rows per kv head in one pass over the cache; a wider group runs
+ * one pass per 16 rows.  QG > 64 returns UQ_ERR_INVALID_ARG.
  * Device preconditions: 0 <= seq_lens[b] <= max_seq_len (larger values are clamped to
  * max_seq_len); block_table[b][t / block_size] in [0, num_blocks) for every t < L_b;
  * entries past a sequence's last block are never read; slot bytes of tokens t >= L_b are
@@ -137,7 +139,7 @@ int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq,
  *   out        [num_seqs, num_kv_heads * qg, head_dim] of out_dtype (UQ_F32 or UQ_BF16;
  *              the query dtype, [P3] output dtype follows the query), element strides
  *              o_stride_seq / o_stride_head (head dim contiguous).
- * Supported: head_dim in {128, 256}, 1 <= qg <= 16. */
+ * Supported: head_dim in {128, 256}, 1 <= qg <= 64. */
 int uq_paged_reduce(const void* part_out, const float* part_max, const float* part_sum,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
                     int32_t qg, int32_t head_dim, int32_t num_partitions,
@@ -155,8 +157,9 @@ int uq_paged_reduce(const void* part_out, const float* part_max, const float* pa
  *   part_out      bf16 [num_seqs, num_kv_heads, P, query_len * QG, head_dim]
  *   part_max,     f32  [num_seqs, num_kv_heads, P, query_len * QG]; row j*QG + g holds
  *   part_sum      query j, head h*QG + g (uq_decode_workspace_bytes with qg = query_len*QG)
- * Supported: fp8 with query_len * QG <= 8, fp4 with query_len * QG <= 16; query_len = 1
- * is exactly uq_paged_decode.  query_len < 1 returns UQ_ERR_INVALID_ARG. */
+ * Supported: fp8 with query_len * QG <= 64 (one pass over the cache per 16 rows), fp4
+ * with query_len * QG <= 16; query_len = 1 is exactly uq_paged_decode.  query_len < 1
+ * returns UQ_ERR_INVALID_ARG. */
 int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
                         int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
                         int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
@@ -172,7 +175,7 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
  * row j*qg + g, written to out row b*query_len + j, head h*qg + g.
  *   out        [num_seqs * query_len, num_kv_heads * qg, head_dim]; o_stride_seq is the
  *              stride between query rows.
- * Supported: head_dim in {128, 256}, query_len >= 1, qg >= 1, query_len * qg <= 16. */
+ * Supported: head_dim in {128, 256}, query_len >= 1, qg >= 1, query_len * qg <= 64. */
 int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float* part_sum,
                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
                         int32_t query_len, int32_t qg, int32_t head_dim, int32_t num_partitions,

@@ -65,15 +65,19 @@ struct VTile {
   i32x4 a, b;  // V bytes [16 (n/2), +16) of tokens 4r + 2 (n&1) and 4r + 2 (n&1) + 1
 };
 
-template <typename QT, int W, bool TOK, bool HG>
-__global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
-  // staging of the merged partition's bf16 output rows (at most 8 rows of 256 bytes; one
-  // stage per wave with head groups), and the states of waves 1..W-1 handed to wave 0
-  // (per lane: 32 accumulators, m_run, m_true, l)
+// T: tiles of 8 query rows (QL x QG <= 8 T).  The K/V stream, the K operand and the V^T
+// transpose are shared by the tiles; each tile has its own query operand, softmax state,
+// accumulators, QK MFMA and PV MFMAs (the pages' M-tiles for wide groups).
+template <typename QT, int W, bool TOK, bool HG, int T>
+__global__ __launch_bounds__(64 * W, T == 1 ? 3 : (T == 2 ? 2 : 1)) void decode_fp8_kernel(
+    DecodeArgs a) {
+  // staging of the merged partition's bf16 output rows (8 rows of 256 bytes per tile, one
+  // tile at a time; one stage per wave with head groups), and the states of waves 1..W-1
+  // handed to wave 0 (per lane and tile: 32 accumulators, m_run, m_true, l)
   constexpr bool kMerge = W > 1 && !HG;
   __shared__ __attribute__((aligned(16))) uint16_t o_stage[(HG ? W : 1) * 8 * kD];
-  __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][32][64];
-  __shared__ float st_ml[kMerge ? W - 1 : 1][3][64];
+  __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][T][32][64];
+  __shared__ float st_ml[kMerge ? W - 1 : 1][T][3][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   // HG: (group of W kv heads, sequence, run): wave w streams kv head W g + w over the
@@ -145,15 +149,24 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   const bool lo_col = n >= 8;
 
   // ---- query operands.  Byte j of lane group r holds head dim d = 32 r + j (the K
-  //      operand's map after the chunk exchange)
-  float x[32];
-  // column g holds unit row g = (query qj, head qh) of QL query rows x QG heads; query qj
-  // sees the tokens t < L_row (the causal window of its row)
+  //      operand's map after the chunk exchange).  Column g of tile t holds unit row
+  //      row_base + 8 t + g = (query qj, head qh) of QL query rows x QG heads; query qj
+  //      sees the tokens t < L_row (the causal window of its row)
   const int NR = a.QL * a.QG;
-  const bool qvalid = g < NR;
-  const int qj = qvalid ? g / a.QG : 0, qh = qvalid ? g % a.QG : 0;
-  const int L_row = L - a.QL + 1 + qj;
-  {
+  const int RB = a.row_base;
+  // per-tensor scales (the per-token ones are applied per token below)
+  const float k_scale = (!TOK && a.k_scale) ? *a.k_scale : 1.f;
+  const float v_scale = (!TOK && a.v_scale) ? *a.v_scale : 1.f;
+  i32x8 q_own[T];  // hi(q s_q) in columns 0-7, lo(q s_q) in columns 8-15
+  float qk_mul[T];
+  int L_row[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int urow = RB + 8 * t + g;
+    const bool qvalid = urow < NR;
+    const int qj = qvalid ? urow / a.QG : 0, qh = qvalid ? urow % a.QG : 0;
+    L_row[t] = L - a.QL + 1 + qj;
+    float x[32];
     const QT* qp = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.QL + qj) * a.q_ss +
                    (int64_t)(h * a.QG + qh) * a.q_sh;
     const QT* src = qp + 32 * r;
@@ -175,44 +188,45 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         }
       }
     }
-  }
-  float amax = 0.f;
+    float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = max_across_rows(amax);
-  // s_q = 2^(7 - E) with amax = f 2^E, f in [0.5, 1): amax * s_q in [64, 128)
-  int E = 0;
-  if (amax > 0.f) {
-    E = (int)((f_bits(amax) >> 23) & 0xFF) - 126;
-    E = E < -100 ? -100 : E;
-  }
-  const float s_q = bits_f((uint32_t)(127 + 7 - E) << 23);
-  // per-tensor scales (the per-token ones are applied per token below)
-  const float k_scale = (!TOK && a.k_scale) ? *a.k_scale : 1.f;
-  const float v_scale = (!TOK && a.v_scale) ? *a.v_scale : 1.f;
-  const float qk_mul = a.softmax_scale * k_scale * kLog2e / s_q;
-
-  i32x8 q_own;  // hi(q s_q) in columns 0-7, lo(q s_q) in columns 8-15
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = max_across_rows(amax);
+    // s_q = 2^(7 - E) with amax = f 2^E, f in [0.5, 1): amax * s_q in [64, 128)
+    int E = 0;
+    if (amax > 0.f) {
+      E = (int)((f_bits(amax) >> 23) & 0xFF) - 126;
+      E = E < -100 ? -100 : E;
+    }
+    const float s_q = bits_f((uint32_t)(127 + 7 - E) << 23);
+    qk_mul[t] = a.softmax_scale * k_scale * kLog2e / s_q;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    float y0 = x[4 * w] * s_q, y1 = x[4 * w + 1] * s_q, y2 = x[4 * w + 2] * s_q,
-          y3 = x[4 * w + 3] * s_q;
-    int hw = cvt_pk_e4m3<false>(y0, y1, 0);
-    hw = cvt_pk_e4m3<true>(y2, y3, hw);
-    int lw = cvt_pk_e4m3<false>(y0 - e4m3_to_f<0>(hw), y1 - e4m3_to_f<1>(hw), 0);
-    lw = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hw), y3 - e4m3_to_f<3>(hw), lw);
-    hw = qvalid ? hw : 0;
-    lw = qvalid ? lw : 0;
-    q_own[w] = lo_col ? lw : hw;
+    for (int w = 0; w < 8; ++w) {
+      float y0 = x[4 * w] * s_q, y1 = x[4 * w + 1] * s_q, y2 = x[4 * w + 2] * s_q,
+            y3 = x[4 * w + 3] * s_q;
+      int hw = cvt_pk_e4m3<false>(y0, y1, 0);
+      hw = cvt_pk_e4m3<true>(y2, y3, hw);
+      int lw = cvt_pk_e4m3<false>(y0 - e4m3_to_f<0>(hw), y1 - e4m3_to_f<1>(hw), 0);
+      lw = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hw), y3 - e4m3_to_f<3>(hw), lw);
+      hw = qvalid ? hw : 0;
+      lw = qvalid ? lw : 0;
+      q_own[t][w] = lo_col ? lw : hw;
+    }
   }
 
   // ---- running state across tile-groups
   // base-2 state: m_run is a reference max >= every score seen, m_true the max itself,
   // l_run the sum of 2^(s - m_run + 8)
-  float m_run = -INFINITY, m_true = -INFINITY, l_run = 0.f;
-  f32x4 acc[8];
+  float m_run[T], m_true[T], l_run[T];
+  f32x4 acc[T][8];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < T; ++t) {
+    m_run[t] = -INFINITY;
+    m_true[t] = -INFINITY;
+    l_run[t] = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const uint32_t pos = (uint32_t)a.pos_stride;
   // K loads: a = token n & 7, chunk 2r + (n >> 3); b = token 8 + (n & 7), chunk
@@ -371,8 +385,9 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       // the pair boundary is a scheduling fence: the next pair's QK (and its wait for
       // K loads issued one pair earlier) must not be hoisted above this pair's PV work
       __builtin_amdgcn_sched_barrier(0);
-      // ---- QK: S^T[token][column] of both tiles, hi + lo columns added by DPP
-      float s[2][4];
+      // ---- QK: S^T[token][column] of both tiles for every row tile, hi + lo columns
+      //      added by DPP
+      float s[T][2][4];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const KTile& kt = kp[pr & 1][tt];
@@ -385,18 +400,19 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
           kop[e] = hi_n ? kt.b[e] : kt.a[e];
           kop[4 + e] = (int)f_bits(row_ror8(bits_f((uint32_t)send)));
         }
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own, z, 0, 0, 0, 127, 0, 127);
-        float mul[4] = {qk_mul, qk_mul, qk_mul, qk_mul};
-        if constexpr (TOK) {  // the K scales of this lane's tokens 4r .. 4r+3
-          quad_values(ksc[pr & 1][tt], mul);
+        float ksq[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (TOK) quad_values(ksc[pr & 1][tt], ksq);  // K scales of tokens 4r..4r+3
 #pragma unroll
-          for (int j = 0; j < 4; ++j) mul[j] *= qk_mul;
-        }
+        for (int t = 0; t < T; ++t) {
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own[t], z, 0, 0, 0, 127, 0,
+                                                                127);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float v = (z[j] + row_ror8(z[j])) * mul[j];
-          s[tt][j] = pair_start + 16 * tt + 4 * r + j < L_row ? v : -INFINITY;
+          for (int j = 0; j < 4; ++j) {
+            const float mul = TOK ? ksq[j] * qk_mul[t] : qk_mul[t];
+            const float v = (z[j] + row_ror8(z[j])) * mul;
+            s[t][tt][j] = pair_start + 16 * tt + 4 * r + j < L_row[t] ? v : -INFINITY;
+          }
         }
       }
       // Stage order is fixed: the scheduler must not hoist the prefetch loads above the
@@ -417,18 +433,21 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
       // ---- softmax against a reference max m_run >= every score seen.  It is raised
       // (with 4 units of base-2 headroom, so raises are rare) only when a score exceeds
       // it; then the running sums are rescaled.  p * 256 = 2^(s - m_run + 8) <= 256.
-      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-      mx = max_across_rows(mx);
-      m_true = fmaxf(m_true, mx);
-      if (__builtin_amdgcn_ballot_w64(mx > m_run)) {  // wave-uniform
-        const float m_new = mx > m_run ? mx + 4.f : m_run;
-        // 0 when m_run = -inf; 1 for a row that has seen no token yet (both -inf)
-        const float alpha = m_run == m_new ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) acc[m] *= alpha;
-        m_run = m_new;
+      for (int t = 0; t < T; ++t) {
+        float mx = fmaxf(fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3])),
+                         fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
+        mx = max_across_rows(mx);
+        m_true[t] = fmaxf(m_true[t], mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m_run[t])) {  // wave-uniform
+          const float m_new = mx > m_run[t] ? mx + 4.f : m_run[t];
+          // 0 when m_run = -inf; 1 for a row that has seen no token yet (both -inf)
+          const float alpha = m_run[t] == m_new ? 1.f : fast_exp2(m_run[t] - m_new);
+          l_run[t] *= alpha;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) acc[t][m] *= alpha;
+          m_run[t] = m_new;
+        }
       }
       // per-token V scales of this lane's tokens; the reference v_ref is raised (and the
       // accumulators rescaled) when a larger scale arrives, so p v_scale / v_ref <= p
@@ -445,30 +464,36 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         if (__builtin_amdgcn_ballot_w64(vmx > v_ref)) {  // wave-uniform, rare
           const float f = v_ref / vmx;  // 0 before the first nonzero scale
 #pragma unroll
-          for (int m = 0; m < 8; ++m) acc[m] *= f;
+          for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) acc[t][m] *= f;
           v_ref = vmx;
           v_inv = 1.f / vmx;
         }
       }
-      // a row that has seen no token (m_run = -inf) has only -inf scores: weight 0
-      const float m8 = m_run == -INFINITY ? 0.f : m_run - 8.f;
-      int pw[2];
+      long pop[T];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float y[4];
+      for (int t = 0; t < T; ++t) {
+        // a row that has seen no token (m_run = -inf) has only -inf scores: weight 0
+        const float m8 = m_run[t] == -INFINITY ? 0.f : m_run[t] - 8.f;
+        int pw[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          y[j] = fast_exp2(s[tt][j] - m8);
-          l_run += y[j];
-          if constexpr (TOK) y[j] *= vq[tt][j] * v_inv;
+        for (int tt = 0; tt < 2; ++tt) {
+          float y[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            y[j] = fast_exp2(s[t][tt][j] - m8);
+            l_run[t] += y[j];
+            if constexpr (TOK) y[j] *= vq[tt][j] * v_inv;
+          }
+          int hw = cvt_pk_e4m3<false>(y[0], y[1], 0);
+          hw = cvt_pk_e4m3<true>(y[2], y[3], hw);
+          int lw = cvt_pk_e4m3<false>(y[0] - e4m3_to_f<0>(hw), y[1] - e4m3_to_f<1>(hw), 0);
+          lw = cvt_pk_e4m3<true>(y[2] - e4m3_to_f<2>(hw), y[3] - e4m3_to_f<3>(hw), lw);
+          pw[tt] = lo_col ? lw : hw;
         }
-        int hw = cvt_pk_e4m3<false>(y[0], y[1], 0);
-        hw = cvt_pk_e4m3<true>(y[2], y[3], hw);
-        int lw = cvt_pk_e4m3<false>(y[0] - e4m3_to_f<0>(hw), y[1] - e4m3_to_f<1>(hw), 0);
-        lw = cvt_pk_e4m3<true>(y[2] - e4m3_to_f<2>(hw), y[3] - e4m3_to_f<3>(hw), lw);
-        pw[tt] = lo_col ? lw : hw;
+        pop[t] = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
       }
-      const long pop = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
 
       // ---- V^T: exchange halves with the neighbouring lane, then byte-transpose 8 dims
       //      x 4 tokens per tile
@@ -498,11 +523,13 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         load_v(rv1, vp[1]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- PV: acc[m][j'] holds O^T[d = 32 r' + 8 j' + m][column n']
+      // ---- PV: acc[t][m][j'] holds O^T[d = 32 r' + 8 j' + m][column n'] of row tile t
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const long vop = (long)vtr[0][m] | ((long)vtr[1][m] << 32);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop, acc[m], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop[t], acc[t][m], 0, 0, 0);
       }
     }
 
@@ -511,70 +538,85 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
   // per-token V scales: the accumulators hold the sums in units of v_ref
   if constexpr (TOK) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m] *= v_ref;
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[t][m] *= v_ref;
   }
   // ---- merge the W wave states into partition part_first: a lane's state belongs to
   //      its column (query head), so the merge is lane-local once the states meet in LDS
-  const float l_tot = sum_across_rows(l_run);
+  float l_tot[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) l_tot[t] = sum_across_rows(l_run[t]);
   if constexpr (kMerge) {
     if (wave > 0) {
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int t = 0; t < T; ++t) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st_acc[wave - 1][4 * m + j][lane] = acc[m][j];
-      st_ml[wave - 1][0][lane] = m_run;
-      st_ml[wave - 1][1][lane] = m_true;
-      st_ml[wave - 1][2][lane] = l_tot;
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st_acc[wave - 1][t][4 * m + j][lane] = acc[t][m][j];
+        st_ml[wave - 1][t][0][lane] = m_run[t];
+        st_ml[wave - 1][t][1][lane] = m_true[t];
+        st_ml[wave - 1][t][2][lane] = l_tot[t];
+      }
     }
     __syncthreads();
     if (wave > 0) return;
   }
-  // statistics relative to the true maximum M over the workgroup's tokens
-  float M = m_true;
-  if constexpr (kMerge) {
+  const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * NR;
+  uint16_t* stage = o_stage + (HG ? wave : 0) * 8 * kD;
 #pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, st_ml[w - 1][1][lane]);
-  }
-  // 0 for a wave without tokens of this row (m_run = -inf), and for every wave when the
-  // row saw no token in the workgroup (M = -inf: an empty state m = -inf, l = 0)
-  float f0 = M == -INFINITY ? 0.f : fast_exp2(m_run - 8.f - M);
-  float l_all = l_tot * f0;
+  for (int t = 0; t < T; ++t) {
+    // statistics relative to the true maximum M over the workgroup's tokens
+    float M = m_true[t];
+    if constexpr (kMerge) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] *= f0;
-  if constexpr (kMerge) {
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-      const float fw = M == -INFINITY ? 0.f : fast_exp2(st_ml[w - 1][0][lane] - 8.f - M);
-      l_all += st_ml[w - 1][2][lane] * fw;
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] += st_acc[w - 1][4 * m + j][lane] * fw;
+      for (int w = 1; w < W; ++w) M = fmaxf(M, st_ml[w - 1][t][1][lane]);
     }
-  }
-  {
+    // 0 for a wave without tokens of this row (m_run = -inf), and for every wave when the
+    // row saw no token in the workgroup (M = -inf: an empty state m = -inf, l = 0)
+    const float f0 = M == -INFINITY ? 0.f : fast_exp2(m_run[t] - 8.f - M);
+    float l_all = l_tot[t] * f0;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[t][m] *= f0;
+    if constexpr (kMerge) {
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        const float fw = M == -INFINITY ? 0.f : fast_exp2(st_ml[w - 1][t][0][lane] - 8.f - M);
+        l_all += st_ml[w - 1][t][2][lane] * fw;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[t][m][j] += st_acc[w - 1][t][4 * m + j][lane] * fw;
+      }
+    }
     const float inv = v_scale / (l_all > 0.f ? l_all : 1.f);
+    // rows RB + 8t .. RB + 8t + nrow - 1 of this partition's partial
+    const int nrow = NR - RB - 8 * t < 8 ? NR - RB - 8 * t : 8;
+    if (nrow <= 0) break;  // wave-uniform
     // Every lane joins the DPP exchange (lanes of the lo columns feed the hi columns).
     // The bf16 rows go through LDS so that the partial is written with whole-line
     // stores: written from registers directly it would be 16-byte pieces at 64-byte
     // stride, and such scattered partial-line writes slow the concurrent KV stream.
-    const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * NR;
-    uint16_t* stage = o_stage + (HG ? wave : 0) * 8 * kD;
+    if (t > 0) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the previous tile's stage reads are done
+      __builtin_amdgcn_wave_barrier();
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       i32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float o0 = (acc[2 * e][j] + row_ror8(acc[2 * e][j])) * inv;
-        const float o1 = (acc[2 * e + 1][j] + row_ror8(acc[2 * e + 1][j])) * inv;
+        const float o0 = (acc[t][2 * e][j] + row_ror8(acc[t][2 * e][j])) * inv;
+        const float o1 = (acc[t][2 * e + 1][j] + row_ror8(acc[t][2 * e + 1][j])) * inv;
         w[e] = (int)pack_bf16x2(o0, o1);
       }
-      if (n < NR) *reinterpret_cast<i32x4*>(stage + n * kD + 32 * r + 8 * j) = w;
+      if (n < nrow) *reinterpret_cast<i32x4*>(stage + n * kD + 32 * r + 8 * j) = w;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
-    const int nbytes = NR * kD * 2;  // contiguous partial rows of this partition
-    uint16_t* out = a.part_o + row0 * kD;
+    const int nbytes = nrow * kD * 2;  // contiguous partial rows of this tile
+    uint16_t* out = a.part_o + (row0 + RB + 8 * t) * kD;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int byte = c * 1024 + 16 * lane;
@@ -582,20 +624,22 @@ __global__ __launch_bounds__(64 * W, 3) void decode_fp8_kernel(DecodeArgs a) {
         *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
             *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) + byte);
     }
-    if (n < NR && r == 0) {
-      a.part_m[row0 + n] = M * kLn2;
-      a.part_l[row0 + n] = l_all;
+    if (n < nrow && r == 0) {
+      a.part_m[row0 + RB + 8 * t + n] = M * kLn2;
+      a.part_l[row0 + RB + 8 * t + n] = l_all;
     }
-    // the workgroup's other partitions that hold tokens: empty states
-    for (int pe = part_first + 1 + r; pe < p_end; pe += 4) {
-      if (n < NR) {
-        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + pe) * NR + n;
-        a.part_m[row] = -INFINITY;
-        a.part_l[row] = 0.f;
-      }
+  }
+  // the workgroup's other partitions that hold tokens: empty states
+  for (int pe = part_first + 1 + r; pe < p_end; pe += 4) {
+    const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + pe) * NR;
+    const int u_end = RB + 8 * T < NR ? RB + 8 * T : NR;
+    for (int u = RB + n; u < u_end; u += 16) {
+      a.part_m[prow + u] = -INFINITY;
+      a.part_l[prow + u] = 0.f;
     }
   }
 }
+
 
 }  // namespace
 
@@ -604,6 +648,11 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   constexpr int W = 4;
   const bool hg = a.head_groups != 0;
   if (hg && a.Hk % W != 0) return hipErrorInvalidValue;
+  // row tiles of 8 query rows, 1 or 2 per launch; wider groups run in passes of 16 rows,
+  // each reading the KV stream once (4 tiles per wave would spill)
+  const int rows = a.QL * a.QG;
+  const int T = rows <= 8 ? 1 : 2;
+  if (rows > 64) return hipErrorInvalidValue;
   const int R = a.run_len > 0 ? a.run_len : 1;
   // HG: one workgroup per (W kv heads, sequence, run); else per (kv head, sequence, W runs)
   const int64_t groups = hg ? (int64_t)a.runs
@@ -612,20 +661,31 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)items), block(64 * W);
-#define UQ_FP8_LAUNCH(QT, TOK, HG) \
-  hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG>), grid, block, 0, stream, a)
-  if (hg) {
-    if (tok_scales) {
-      if (q_is_f32) UQ_FP8_LAUNCH(float, true, true); else UQ_FP8_LAUNCH(uint16_t, true, true);
+#define UQ_FP8_LAUNCH(QT, TOK, HG)                                                         \
+  do {                                                                                    \
+    if (T == 1)                                                                           \
+      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 1>), grid, block, 0, stream, p); \
+    else                                                                                  \
+      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 2>), grid, block, 0, stream, p); \
+  } while (0)
+  for (int rb = 0; rb < rows; rb += 16) {
+    DecodeArgs p = a;
+    p.row_base = rb;
+    if (hg) {
+      if (tok_scales) {
+        if (q_is_f32) UQ_FP8_LAUNCH(float, true, true); else UQ_FP8_LAUNCH(uint16_t, true, true);
+      } else {
+        if (q_is_f32) UQ_FP8_LAUNCH(float, false, true); else UQ_FP8_LAUNCH(uint16_t, false, true);
+      }
     } else {
-      if (q_is_f32) UQ_FP8_LAUNCH(float, false, true); else UQ_FP8_LAUNCH(uint16_t, false, true);
+      if (tok_scales) {
+        if (q_is_f32) UQ_FP8_LAUNCH(float, true, false); else UQ_FP8_LAUNCH(uint16_t, true, false);
+      } else {
+        if (q_is_f32) UQ_FP8_LAUNCH(float, false, false); else UQ_FP8_LAUNCH(uint16_t, false, false);
+      }
     }
-  } else {
-    if (tok_scales) {
-      if (q_is_f32) UQ_FP8_LAUNCH(float, true, false); else UQ_FP8_LAUNCH(uint16_t, true, false);
-    } else {
-      if (q_is_f32) UQ_FP8_LAUNCH(float, false, false); else UQ_FP8_LAUNCH(uint16_t, false, false);
-    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
 #undef UQ_FP8_LAUNCH
   return hipGetLastError();

@@ -88,7 +88,7 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
     return fail(UQ_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, num_kv_heads);
   const int QG = num_q_heads / num_kv_heads;
-  if (QG > 16) return fail(UQ_ERR_INVALID_ARG, "query group %d exceeds 16", QG);
+  if (QG > 64) return fail(UQ_ERR_INVALID_ARG, "query group %d exceeds 64", QG);
   if (q_dtype != UQ_F32 && q_dtype != UQ_BF16)
     return fail(UQ_ERR_INVALID_ARG, "q_dtype must be UQ_F32 or UQ_BF16 (got %d)", q_dtype);
   if (q_stride_seq <= 0 || q_stride_head <= 0)
@@ -169,8 +169,8 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
     if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3)
       return fail(UQ_ERR_INVALID_ARG, "k_scale and v_scale must be 4-byte aligned");
     if (head_dim != 128) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports head_dim 128 only");
-    if (query_len * QG > 8)
-      return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports query_len x query group up to 8 rows (got %d x %d)",
+    if (query_len * QG > 64)
+      return fail(UQ_ERR_UNSUPPORTED, "fp8 cache supports query_len x query group up to 64 rows (got %d x %d)",
                   query_len, QG);
     if (rot_signs) return fail(UQ_ERR_UNSUPPORTED, "query rotation is supported with fp4 caches only");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache needs slot_bytes a multiple of 16");
@@ -265,7 +265,7 @@ int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float
                         int32_t max_seq_len, void* out, int out_dtype, int64_t o_stride_seq,
                         int64_t o_stride_head, void* stream) {
   if (query_len < 1) return fail(UQ_ERR_INVALID_ARG, "query_len must be >= 1 (got %d)", query_len);
-  if (num_seqs < 0 || num_kv_heads <= 0 || qg < 1 || query_len * qg > 16)
+  if (num_seqs < 0 || num_kv_heads <= 0 || qg < 1 || query_len * qg > 64)
     return fail(UQ_ERR_INVALID_ARG, "bad sizes: num_seqs %d, num_kv_heads %d, query_len %d x qg %d",
                 num_seqs, num_kv_heads, query_len, qg);
   if (head_dim != 128 && head_dim != 256)

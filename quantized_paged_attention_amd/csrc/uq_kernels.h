@@ -27,6 +27,8 @@ struct DecodeArgs {
   int32_t runs;     // work items per (sequence, kv head)
   int32_t run_len;  // partitions per work item when each partition is one tile-group, else 0
   int32_t head_groups;  // fp8: 1 = a workgroup's waves are consecutive kv heads of one run
+  int32_t row_base;     // fp8: first unit row of this launch (wide groups run in passes of
+                        // 16 rows; set by the launcher)
   float softmax_scale;
   uint16_t* part_o;            // bf16 [B, Hk, P, QL*QG, D]
   float* part_m;               // [B, Hk, P, QL*QG]

@@ -48,7 +48,9 @@ def decode_args(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(Hq=60), uq.UQ_ERR_INVALID_ARG),                 # Hq not a multiple of Hk
-    (dict(Hq=8 * 17), uq.UQ_ERR_INVALID_ARG),             # QG > 16
+    (dict(Hq=8 * 65), uq.UQ_ERR_INVALID_ARG),             # QG > 64
+    (dict(Hq=8 * 17, fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272),
+     uq.UQ_ERR_UNSUPPORTED),                              # fp4 QG up to 16
     (dict(q_dtype=7), uq.UQ_ERR_INVALID_ARG),
     (dict(bs=24), uq.UQ_ERR_INVALID_ARG),
     (dict(bs=512), uq.UQ_ERR_INVALID_ARG),
@@ -63,7 +65,7 @@ def decode_args(**over):
     (dict(q_sh=129), uq.UQ_ERR_INVALID_ARG),              # stride not 16-byte aligned
     (dict(fmt=9), uq.UQ_ERR_INVALID_ARG),
     (dict(D=64, slot=128), uq.UQ_ERR_UNSUPPORTED),        # fp8 supports D=128 only
-    (dict(Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),             # fp8 QG up to 8
+    (dict(Hq=8 * 64, D=64, slot=128), uq.UQ_ERR_UNSUPPORTED),  # fp8 needs D = 128
     (dict(rot=FAKE), uq.UQ_ERR_UNSUPPORTED),              # rotation needs an fp4 cache
     (dict(fmt=uq.UQ_KV_FP4_E2M1_UE8M0S, D=128, slot=144, Hq=8 * 8), uq.UQ_ERR_UNSUPPORTED),
     (dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=128, slot=144, Hq=8 * 4), uq.UQ_ERR_UNSUPPORTED),
@@ -76,7 +78,7 @@ def decode_args(**over):
     (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE + 2), uq.UQ_ERR_INVALID_ARG),
     (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE, D=64, slot=128),
      uq.UQ_ERR_UNSUPPORTED),
-    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE, Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),
+    (dict(fmt=uq.UQ_KV_FP8_E4M3_TOKSCALE, ks=FAKE, vs=FAKE, Hq=8 * 65), uq.UQ_ERR_INVALID_ARG),
 ])
 def test_decode_validation(lib, over, status):
     st = lib.uq_paged_decode(*decode_args(**over))
@@ -98,8 +100,8 @@ def decode_mtp_args(QL=2, **over):
 @pytest.mark.parametrize("QL,over,status", [
     (0, dict(), uq.UQ_ERR_INVALID_ARG),                    # query_len < 1
     (-3, dict(), uq.UQ_ERR_INVALID_ARG),
-    (2, dict(), uq.UQ_ERR_UNSUPPORTED),                    # fp8: 2 x 8 rows > 8
-    (3, dict(Hq=8 * 3), uq.UQ_ERR_UNSUPPORTED),            # fp8: 3 x 3 rows > 8
+    (9, dict(), uq.UQ_ERR_UNSUPPORTED),                    # fp8: 9 x 8 rows > 64
+    (3, dict(Hq=8 * 22), uq.UQ_ERR_UNSUPPORTED),           # fp8: 3 x 22 rows > 64
     (2, dict(fmt=uq.UQ_KV_FP4_E2M1_E4M3S, D=256, slot=272, Hq=8 * 16), uq.UQ_ERR_UNSUPPORTED),
     (5, dict(fmt=uq.UQ_KV_FP4_E2M1_UE8M0S, D=256, slot=272, Hq=8 * 4), uq.UQ_ERR_UNSUPPORTED),
     (2, dict(Hq=60), uq.UQ_ERR_INVALID_ARG),               # checks of uq_paged_decode apply
@@ -123,7 +125,7 @@ def reduce_args(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(qg=0), uq.UQ_ERR_INVALID_ARG), (dict(qg=17), uq.UQ_ERR_INVALID_ARG),
+    (dict(qg=0), uq.UQ_ERR_INVALID_ARG), (dict(qg=65), uq.UQ_ERR_INVALID_ARG),
     (dict(D=64), uq.UQ_ERR_UNSUPPORTED), (dict(P=0), uq.UQ_ERR_INVALID_ARG),
     (dict(dt=5), uq.UQ_ERR_INVALID_ARG), (dict(out=None), uq.UQ_ERR_INVALID_ARG),
     (dict(o_sh=4), uq.UQ_ERR_INVALID_ARG), (dict(max_len=-5), uq.UQ_ERR_INVALID_ARG),
@@ -133,7 +135,7 @@ def test_reduce_validation(lib, over, status):
 
 
 @pytest.mark.parametrize("QL,qg,status", [
-    (0, 8, uq.UQ_ERR_INVALID_ARG), (2, 16, uq.UQ_ERR_INVALID_ARG), (5, 4, uq.UQ_ERR_INVALID_ARG),
+    (0, 8, uq.UQ_ERR_INVALID_ARG), (2, 33, uq.UQ_ERR_INVALID_ARG), (5, 13, uq.UQ_ERR_INVALID_ARG),
     (3, 0, uq.UQ_ERR_INVALID_ARG),
 ])
 def test_reduce_mtp_validation(lib, QL, qg, status):

@@ -306,3 +306,17 @@ def test_head_group_large_batch_runs():
     log(f"case fp8 head groups B={case.B} hk=8 P=64")
     got, _ = run_decode(case, P=64)
     assert_decode_close(got, oracle_decode(case), "head groups large batch")
+
+
+@pytest.mark.parametrize("qg", [12, 16, 24, 32, 64])
+@pytest.mark.parametrize("hk", [2, 4])
+def test_wide_query_groups(qg, hk):
+    """Query groups above 8 rows: two row tiles of 8 share one pass over the cache, and
+    groups above 16 rows run one pass per 16 rows (the pages' wide-GQA case)."""
+    need_gpu()
+    case = small(hk=hk, qg=qg, seed=80 + qg + hk, q_dtype="f32" if qg == 12 else "bf16",
+                 lens=(1, 17, 256, 257, 1000, 2500))
+    log(f"case fp8 wide group qg={qg} hk={hk}")
+    for P in (1, 3):
+        got, _ = run_decode(case, P=P)
+        assert_decode_close(got, oracle_decode(case), f"wide qg={qg} hk={hk} P={P}")

@@ -148,3 +148,14 @@ def test_fp4_d256_mtp_full(kind):
     log(f"case fp4_d256_mtp2_qg8 scales={kind}")
     got, _ = run_decode(case)
     assert_decode_close(got, oracle_decode(case), f"fp4_d256_mtp {kind}")
+
+
+@pytest.mark.parametrize("ql,qg,hk", [(2, 8, 2), (3, 5, 4), (4, 8, 4), (2, 16, 2)])
+def test_fp8_query_rows_wide(ql, qg, hk):
+    """Query rows x heads above 8 (two row tiles; 32 rows run two passes)."""
+    need_gpu()
+    case = fp8(ql, qg, seed=280 + 10 * ql + qg + hk, hk=hk, k_scale=0.05, v_scale=0.02,
+               values="uniform_codes", lens=(1, 2, 3, 7, 255, 256, 257, 1000))
+    log(f"case fp8 mtp wide ql={ql} qg={qg} hk={hk}")
+    got, _ = run_decode(case, P=3)
+    assert_decode_close(got, oracle_decode(case), f"fp8 mtp wide ql={ql} qg={qg} hk={hk}")

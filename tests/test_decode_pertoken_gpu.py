@@ -146,3 +146,13 @@ def test_head_groups_per_token(P):
     log(f"case fp8 per-token head groups P={P}")
     got, _ = run_decode(case, P=P)
     assert_decode_close(got, oracle_decode(case), f"per-token head groups P={P}")
+
+
+@pytest.mark.parametrize("qg,hk", [(16, 2), (16, 8), (32, 4)])
+def test_wide_groups_per_token(qg, hk):
+    """Per-token scales with query groups of 16 and 32 rows."""
+    need_gpu()
+    case = tok(90 + qg + hk, hk=hk, qg=qg, lens=(1, 17, 256, 257, 1500), v_ramp=1.0)
+    log(f"case fp8 per-token wide qg={qg} hk={hk}")
+    got, _ = run_decode(case, P=3)
+    assert_decode_close(got, oracle_decode(case), f"per-token wide qg={qg} hk={hk}")
