@@ -246,14 +246,22 @@ def test_reduce_skips_empty_partitions(D, P):
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "fp8_tok_hg", "fp8_wide"])
 def test_graph_replay_matches_eager(fmt):
     """decode + reduce captured in a HIP graph (torch.cuda.graph on the current stream):
     every one of several replays, with eager work and synchronisations in between, gives
-    the eager result bit for bit (no memset nodes; all state lives in the partials)."""
+    the eager result bit for bit (no memset nodes; all state lives in the partials).
+    fp8_tok_hg: per-token scales with head-group workgroups; fp8_wide: a 32-row query
+    group, two decode launches per step."""
     need_gpu()
     if fmt == "fp8":
         case = small(lens=(40, 700, 2049, 5000), seed=59, hk=2)
+    elif fmt == "fp8_tok_hg":
+        case = synth.make_fp8_case("tok_graph", 96, seq_lens=[40, 700, 2049, 5000],
+                                   num_kv_heads=8, qg=4, spare_blocks=3, scales="token",
+                                   values="normal")
+    elif fmt == "fp8_wide":
+        case = small(lens=(40, 700, 2049), seed=97, hk=4, qg=32)
     else:
         case = synth.make_fp4_case("fp4_graph", 95, seq_lens=[300, 1000, 3000], num_kv_heads=2,
                                    qg=8, head_dim=256, block_size=64, rotate=True, spare_blocks=3)
