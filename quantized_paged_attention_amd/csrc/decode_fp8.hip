@@ -1,26 +1,30 @@
-// decode_fp8.hip -- paged decode over a per-tensor-scaled OCP e4m3 cache, D = 128,
-// GQA groups of up to 8 query heads, for gfx950.
+// decode_fp8.hip -- paged decode over an OCP e4m3 cache (per-tensor or per-token K/V
+// scales), D = 128, query groups of up to 64 rows (query rows x heads), for gfx950.
 //
 // What is computed (ROCm/FlyDSL PR #825 "pa_decode_tile": per-tensor fp8 K/V decode with
-// a cross-workgroup partition split; vLLM "ultraquant_decode_hd256" page: strided
-// partition -> 256-token tile-group map, softmax statistics of STEP F, epilogue of
-// STEP G): for a work unit (sequence b, kv head h, partition p) the softmax statistics
-// (m, l, o = v_scale * sum exp(s - m) v / l) of the tokens of tile-groups p, p+P, ...
+// a cross-workgroup partition split, per_token_kv mode, query rows and wide groups; vLLM
+// "ultraquant_decode_hd256" page: strided partition -> 256-token tile-group map, softmax
+// statistics of STEP F, epilogue of STEP G): for a work unit (sequence b, kv head h,
+// partition p) the softmax statistics (m, l, o = v_scale * sum exp(s - m) v / l) of the
+// tokens of tile-groups p, p+P, ...
 //
-// Design (a workgroup of W = 4 waves per group of consecutive partitions of one
-// (sequence, kv head); KV streamed once):
-//   * Wave w streams R consecutive partitions (R = 2 for large batches, else 1; a
-//     partition that owns several strided tile-groups when P is small) as one online
-//     softmax.  The W wave states meet in LDS at the end and are merged into the
-//     statistics of the group's first partition; the group's other partitions are
-//     written as empty (m = -inf, l = 0), which the flash-combine reduce treats as
-//     absent.  The partial rows written to HBM shrink W * R times (11 MB instead of
-//     88 MB at B = 128, ctx 16k).
+// Design (a workgroup of W = 4 waves; KV streamed once per 16 query rows):
+//   * Head groups (Hk a multiple of 4): the 4 waves take 4 neighbouring kv heads of one
+//     (sequence, run of consecutive partitions), so they read the neighbouring head slots
+//     of the same blocks together; each wave streams the run as one online softmax and
+//     merges it into the statistics of the run's first partition.  Otherwise the 4 waves
+//     split a group of one head's partitions and their states meet in LDS.  Either way
+//     the run's other partitions are written as empty (m = -inf, l = 0), which the
+//     flash-combine reduce treats as absent, and the partial rows written to HBM shrink
+//     by the run length.
 //   * Measured on MI355X: partial-row write-backs interleaved with the KV read stream
 //     cost far more than their bytes (88 MB of partials: +90 us on a 480 us stream);
-//     the same stores kept L2-resident cost ~4 us.  With non-temporal KV loads and the
-//     8-fold merge the partials stay in L2 until the kernel ends and the store cost
-//     vanishes.
+//     the same stores kept L2-resident cost ~4 us.  With non-temporal KV loads and whole
+//     runs merged into one partial, the partials stay in L2 until the kernel ends.
+//   * Query rows are carried as T tiles of 8 MFMA columns (T = 1 or 2); the K/V loads,
+//     the K operand and the V^T transpose are shared by the tiles, each tile has its own
+//     query operand, softmax state and accumulators.  Wider groups run one launch per
+//     16 rows.
 //   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
 //     from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query group as an
 //     e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
