@@ -107,9 +107,9 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2,
  * partitions into the first of them (m, l, o of their union) and write the others of the
  * set as empty (m = -inf, l = 0, o rows left unwritten).  Combining all written states
  * with uq_paged_reduce gives the attention output either way.  The kernels merge the
- * run of consecutive partitions that one workgroup (fp4) or one wave (fp8) streams for a
- * kv head; the run length is chosen by the launcher from the problem size and the
- * device's compute units.
+ * run of consecutive partitions streamed for one kv head by one wave (fp8 with
+ * num_kv_heads a multiple of 4) or by one workgroup (otherwise); the run length is
+ * chosen by the launcher from the problem size and the device's compute units.
  * With num_partitions = 1 part_* hold exactly the statistics above.
  * Supported: (UQ_KV_FP8_E4M3 or UQ_KV_FP8_E4M3_TOKSCALE, D = 128, QG <= 64) and
  * (UQ_KV_FP4_E2M1_E4M3S or UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else
