@@ -156,3 +156,13 @@ def test_wide_groups_per_token(qg, hk):
     log(f"case fp8 per-token wide qg={qg} hk={hk}")
     got, _ = run_decode(case, P=3)
     assert_decode_close(got, oracle_decode(case), f"per-token wide qg={qg} hk={hk}")
+
+
+@pytest.mark.parametrize("hk,bs", [(3, 16), (1, 16), (3, 32)])
+def test_odd_head_counts(hk, bs):
+    """Odd kv head counts (runs of one head, no head groups) at block sizes 16 and 32."""
+    need_gpu()
+    case = tok(95 + hk + bs, hk=hk, qg=4, bs=bs, lens=(1, 15, 16, 17, 255, 257, 1000))
+    log(f"case fp8 per-token odd hk={hk} bs={bs}")
+    got, _ = run_decode(case, P=3)
+    assert_decode_close(got, oracle_decode(case), f"per-token hk={hk} bs={bs}")
