@@ -110,7 +110,7 @@ def cpu_baseline_index(case, min_seconds: float = 10.0):
         lambda: oracle.index_score(case.q, case.pages, case.block_table, case.seq_lens,
                                    query_len=case.query_len, scores_init=case.scores_init()),
         min_seconds)
-    return {"value": round(passes * case.page_bytes() / dt / 1e9, 4), "unit": "GB/s",
+    return {"value": round(passes * case.unique_page_bytes() / dt / 1e9, 4), "unit": "GB/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"all {case.num_reqs} requests ({case.page_bytes() / 1e6:.1f} MB of "
                       f"pages) x {passes} passes, fp64, {dt:.2f} s wall"}
@@ -152,6 +152,12 @@ def make_case(workload: str):
             f"{workload}: B=4 Hk=2 QG={qg} D=256 L=75000 block=64 P=512 e2m1 K/V with "
             f"{'UE8M0' if ue else 'e4m3'} group-of-32 scales, 272-byte slot, rotated keys, "
             "bf16 Q")
+    if workload.startswith("nvfp4_index_shared_ql"):
+        ql, h = workload[len("nvfp4_index_shared_ql"):].split("_h")
+        case = synth.nvfp4_index_shared(int(ql), int(h))
+        return case, (f"{workload}: 32 requests QL={ql} H={h} D=128 L~U[9216,32768] sharing "
+                      "their first 64 nvfp4 pages (a prompt prefix), 9216-byte pages, e4m3 Q; "
+                      "bytes = distinct pages read once")
     if workload.startswith("nvfp4_index_ql"):
         ql, h = workload[len("nvfp4_index_ql"):].split("_h")
         case = synth.nvfp4_index(int(ql), int(h))
@@ -170,7 +176,7 @@ def main():
                          "fp4ue_d256_qg{6,8,16}, "
                          "fp8_high_mtp{QL}_qg{QG} (QL*QG <= 64), "
                          "fp4[ue]_d256_mtp{QL}_qg{QG} (QL*QG <= 16), "
-                         "nvfp4_index_ql{1,2,4,8}_h{1,2,4}")
+                         "nvfp4_index_ql{1,2,4,8}_h{1,2,4}, nvfp4_index_shared_ql{QL}_h{H}")
     ap.add_argument("--cpu-seqs", type=int, default=128,
                     help="sequences of a decode workload the CPU oracle baseline runs")
     ap.add_argument("--no-cpu", action="store_true")
@@ -217,7 +223,7 @@ def main():
 
         def kernels(pages):
             uq.index_score(q, pages, bt, sl, scores, query_len=case.query_len, stream=stream)
-        algo_bytes = case.page_bytes()
+        algo_bytes = case.unique_page_bytes()   # = page_bytes() when no page is shared
         names = ("index_score",)
         dtype = "f16"
     else:

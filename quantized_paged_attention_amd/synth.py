@@ -405,6 +405,17 @@ class IndexCase:
         s.fill(SCORE_POISON_BITS)
         return s.view(np.float32)
 
+    def unique_page_bytes(self) -> int:
+        """Algorithmic bytes when pages that several requests map to are read once: per
+        distinct page, its visible tokens (the most any referencing request sees) x 72."""
+        vis = {}
+        for r, L in enumerate(self.seq_lens):
+            L = int(L)
+            for b in range(-(-L // INDEX_PAGE)):
+                pid = int(self.block_table[r, b])
+                vis[pid] = max(vis.get(pid, 0), min(INDEX_PAGE, L - b * INDEX_PAGE))
+        return sum(vis.values()) * (self.D // 2 + self.D // 16)
+
     def page_bytes(self) -> int:
         """Algorithmic bytes: every visible token's 72 bytes (codes + scales), once."""
         return int(self.seq_lens.astype(np.int64).sum()) * (self.D // 2 + self.D // 16)
@@ -441,6 +452,28 @@ def make_index_case(name, seed, *, seq_lens, query_len, heads, head_dim=128, pag
     q = e4m3_encode(rng.standard_normal((R * query_len, heads, D), dtype=np.float32))
     S = max_pages or bt.shape[1]
     return IndexCase(name, q, pages, bt, seq_lens, query_len, heads, S)
+
+
+def index_shared_prefix(case: IndexCase, prefix_pages: int) -> IndexCase:
+    """The same requests, but every request's first prefix_pages table entries point at
+    request 0's pages (a shared prompt prefix, as a prefix cache lays out).  Requires
+    every request to be longer than the prefix; the pages other requests held there are
+    left unreferenced."""
+    c = dataclasses.replace(case, block_table=case.block_table.copy())
+    assert int(c.seq_lens.min()) > prefix_pages * INDEX_PAGE
+    c.block_table[:, :prefix_pages] = c.block_table[0, :prefix_pages]
+    c.name = f"{case.name}_shared{prefix_pages}"
+    return c
+
+
+def nvfp4_index_shared(query_len=8, heads=4, prefix_pages=64, seed=6) -> IndexCase:
+    """32 requests, L ~ U[prefix + 1024, 32768], sharing their first prefix_pages pages
+    (8192 tokens at 64)."""
+    lo = prefix_pages * INDEX_PAGE + 1024
+    lens = np.random.default_rng(seed + 1000).integers(lo, 32769, size=32).astype(np.int32)
+    base = make_index_case(f"nvfp4_index_ql{query_len}_h{heads}", seed, seq_lens=lens,
+                           query_len=query_len, heads=heads, page_stride=9216)
+    return index_shared_prefix(base, prefix_pages)
 
 
 def nvfp4_index(query_len=8, heads=4, seed=5) -> IndexCase:

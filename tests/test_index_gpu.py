@@ -108,3 +108,54 @@ def test_page_permutation_bit_identical():
                               -1).astype(np.int32)
     got = run_gpu(c2)
     assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+
+
+@pytest.mark.parametrize("ql,h", [(1, 1), (4, 2), (8, 4)])
+def test_shared_prefix_pages(ql, h):
+    """Requests whose first 64 pages are the same physical pages (a shared prefix): the
+    result matches the oracle and is bit-identical to the same table pointing at private
+    copies of those pages."""
+    need_gpu()
+    base = synth.make_index_case("shared", 77 + ql + h,
+                                 seq_lens=np.random.default_rng(ql * 10 + h).integers(
+                                     64 * 128 + 1, 20000, size=40).astype(np.int32),
+                                 query_len=ql, heads=h, page_stride=9216)
+    case = synth.index_shared_prefix(base, 64)
+    log(f"case nvfp4_index shared prefix ql={ql} h={h} reqs={case.num_reqs}")
+    got = run_gpu(case)
+    assert_index_match(got, run_oracle(case), case.scores_init(), f"shared ql={ql} h={h}")
+    # private copies: every request's prefix entries point at its own copy of the pages
+    priv = copy.deepcopy(case)
+    nref = case.pages.shape[0]
+    extra = []
+    for r in range(1, case.num_reqs):
+        ids = case.block_table[r, :64]
+        new_ids = nref + len(extra) + np.arange(64)
+        extra.extend(case.pages[i] for i in ids)
+        priv.block_table[r, :64] = new_ids
+    priv.pages = np.concatenate([case.pages, np.stack(extra)], axis=0)
+    got_priv = run_gpu(priv)
+    assert np.array_equal(got.view(np.uint32), got_priv.view(np.uint32))
+
+
+def test_shared_pages_across_windows_and_partial():
+    """70 requests (two 64-request windows) sharing pages in irregular places: some
+    requests share a page only at one block index, the shared last page of a request is
+    partly visible, and requests in different windows share pages too."""
+    need_gpu()
+    rng = np.random.default_rng(123)
+    lens = rng.integers(300, 3000, size=70).astype(np.int32)
+    case = synth.make_index_case("shared_irreg", 124, seq_lens=lens, query_len=2, heads=2,
+                                 page_stride=9216)
+    bt = case.block_table
+    for r in range(1, 70):
+        if r % 3 == 0:           # share block 0 with the previous request
+            bt[r, 0] = bt[r - 1, 0]
+        if r % 5 == 0 and lens[r] > 128 and lens[r - 5] > 128:   # share block 1 with r - 5
+            bt[r, 1] = bt[r - 5, 1]
+    # request 69 maps request 1's pages at its first blocks (different windows)
+    n = min(-(-int(lens[1]) // 128), -(-int(lens[69]) // 128)) - 1
+    bt[69, :n] = bt[1, :n]
+    log("case nvfp4_index irregular sharing, 70 requests")
+    got = run_gpu(case)
+    assert_index_match(got, run_oracle(case), case.scores_init(), "irregular sharing")
