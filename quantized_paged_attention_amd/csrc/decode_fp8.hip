@@ -72,9 +72,16 @@ struct VTile {
 // T: tiles of 8 query rows (QL x QG <= 8 T).  The K/V stream, the K operand and the V^T
 // transpose are shared by the tiles; each tile has its own query operand, softmax state,
 // accumulators, QK MFMA and PV MFMAs (the pages' M-tiles for wide groups).
+// One work unit of a wave: kv head h of sequence b (length L, already clamped), the
+// tile-groups first_tg, first_tg + step, ... (n_tg of them) of the partitions
+// [part_first, p_end) it merges; writes the merged statistics to partition part_first and
+// marks the others of [part_first, p_end) empty.
 template <typename QT, int W, bool TOK, bool HG, int T>
-__global__ __launch_bounds__(64 * W, T == 1 ? 3 : (T == 2 ? 2 : 1)) void decode_fp8_kernel(
-    DecodeArgs a) {
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane, const int wave,
+                                            const int b, const int h, const int L,
+                                            const int part_first, const int p_end,
+                                            const int first_tg, const int n_tg,
+                                            const int step) {
   // staging of the merged partition's bf16 output rows (8 rows of 256 bytes per tile, one
   // tile at a time; one stage per wave with head groups), and the states of waves 1..W-1
   // handed to wave 0 (per lane and tile: 32 accumulators, m_run, m_true, l)
@@ -82,72 +89,6 @@ __global__ __launch_bounds__(64 * W, T == 1 ? 3 : (T == 2 ? 2 : 1)) void decode_
   __shared__ __attribute__((aligned(16))) uint16_t o_stage[(HG ? W : 1) * 8 * kD];
   __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][T][32][64];
   __shared__ float st_ml[kMerge ? W - 1 : 1][T][3][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // HG: (group of W kv heads, sequence, run): wave w streams kv head W g + w over the
-  // run's partitions, so the W waves read neighbouring slots of the same blocks together.
-  // Otherwise: (kv head, sequence, group of W runs) with the W runs split over the waves.
-  const int64_t item = blockIdx.x;
-  const int nhs = HG ? a.Hk / W : a.Hk;
-  const int h = (int)(item % nhs) * (HG ? W : 1) + (HG ? wave : 0);
-  const int b = (int)((item / nhs) % a.B);
-  const int grp = (int)(item / ((int64_t)nhs * a.B));
-
-  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);  // wave-uniform
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int ntg = (L + kTileGroup - 1) / kTileGroup;
-  // Partitions that hold tokens: p < pmax.  The workgroup owns partitions
-  // [part_first, p_end): with one tile-group per partition a run of consecutive ones per
-  // wave (up to R = run_len), else one partition (with its strided tile-groups) per wave.
-  // The W wave states are merged into the statistics of partition part_first and the
-  // workgroup's other partitions are written as empty (m = -inf, l = 0).  The
-  // flash-combine of the reduce gives the same result as for separate partitions, and
-  // the partial rows written to HBM shrink up to W * R times.
-  const int pmax = a.P < ntg ? a.P : ntg;
-  const int R = a.run_len > 0 ? a.run_len : 1;
-  int part_first, p_end, first_tg, n_tg, step;
-  if (HG && a.run_len > 0) {
-    // this sequence's pmax partitions in G nearly equal runs of at most R; every wave
-    // streams the whole run for its own kv head
-    const int G = (pmax + R - 1) / R;
-    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
-    part_first = (int)((int64_t)grp * pmax / G);
-    p_end = (int)((int64_t)(grp + 1) * pmax / G);
-    first_tg = part_first;
-    n_tg = p_end - part_first;
-    step = 1;
-  } else if (HG) {
-    // partition grp (its strided tile-groups) for each wave's kv head
-    part_first = grp;
-    if (part_first >= pmax) return;  // workgroup-uniform
-    p_end = part_first + 1;
-    first_tg = part_first;
-    n_tg = (ntg - first_tg + a.P - 1) / a.P;
-    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
-    step = a.P;
-  } else if (a.run_len > 0) {
-    // this sequence's pmax partitions in G nearly equal groups of at most W * R, and a
-    // group's m partitions nearly equally over its W waves (no wave idles at the merge
-    // for a whole run)
-    const int G = (pmax + W * R - 1) / (W * R);
-    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
-    part_first = (int)((int64_t)grp * pmax / G);
-    p_end = (int)((int64_t)(grp + 1) * pmax / G);
-    const int m = p_end - part_first;
-    first_tg = part_first + wave * m / W;
-    n_tg = part_first + (wave + 1) * m / W - first_tg;
-    step = 1;
-  } else {
-    part_first = grp * W;
-    if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
-    p_end = part_first + W < pmax ? part_first + W : pmax;
-    // partition part_first + wave owns the strided tile-groups p, p + P, ...
-    first_tg = part_first + wave;
-    n_tg = first_tg < pmax ? (ntg - first_tg + a.P - 1) / a.P : 0;
-    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
-    step = a.P;
-  }
-
   const int r = lane >> 4, n = lane & 15;
   const int g = n & 7;
   const bool lo_col = n >= 8;
@@ -645,6 +586,140 @@ __global__ __launch_bounds__(64 * W, T == 1 ? 3 : (T == 2 ? 2 : 1)) void decode_
 }
 
 
+
+template <typename QT, int W, bool TOK, bool HG, int T, bool BAL>
+__global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8_kernel(
+    DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // HG: (group of W kv heads, sequence, run): wave w streams kv head W g + w over the
+  // run's partitions, so the W waves read neighbouring slots of the same blocks together.
+  // Otherwise: (kv head, sequence, group of W runs) with the W runs split over the waves.
+  const int64_t item = blockIdx.x;
+  const int nhs = HG ? a.Hk / W : a.Hk;
+  if constexpr (BAL) {
+    {
+      // Balanced slices: the partitions of all sequences, in sequence order, form one list
+      // of Tt entries; slice s of N takes entries [s Tt / N, (s + 1) Tt / N), so every
+      // workgroup streams the same number of partitions however ragged the lengths are.
+      // A slice that crosses a sequence boundary is streamed as one unit per sequence.
+      const int hh = (int)(item % nhs) * W + wave;
+      const int64_t slice = item / nhs, N = a.balanced_items;
+      auto parts_of = [&](int bb) {  // partitions of sequence bb that hold tokens
+        int Lb = a.seq_lens[bb];
+        Lb = Lb < 0 ? 0 : (Lb > a.max_seq_len ? a.max_seq_len : Lb);
+        const int ntb = (Lb + kTileGroup - 1) / kTileGroup;
+        return a.P < ntb ? a.P : ntb;
+      };
+      int64_t Tt = 0;
+      for (int c = 0; c < a.B; c += 64) {
+        int v = c + lane < a.B ? parts_of(c + lane) : 0;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+        Tt += __builtin_amdgcn_readfirstlane(v);
+      }
+      const int64_t s0 = slice * Tt / N, s1 = (slice + 1) * Tt / N;
+      if (s0 >= s1) return;  // workgroup-uniform
+      // the sequence holding entry s0, and s0's partition index in it
+      int bb = 0;
+      int64_t off = s0;
+      for (int c = 0; c < a.B; c += 64) {
+        const int v = c + lane < a.B ? parts_of(c + lane) : 0;
+        int incl = v;  // inclusive prefix sum over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int u = __shfl_up(incl, d, 64);
+          incl += lane >= d ? u : 0;
+        }
+        const int tot = __builtin_amdgcn_readlane(incl, 63);
+        if (off < tot) {
+          const uint64_t past = __builtin_amdgcn_ballot_w64((int64_t)incl <= off);
+          const int i = __builtin_popcountll(past);  // first lane whose prefix passes off
+          off -= i > 0 ? __builtin_amdgcn_readlane(incl, i - 1) : 0;
+          bb = c + i;
+          break;
+        }
+        off -= tot;
+      }
+      int64_t left = s1 - s0;
+      int p_lo = (int)off;
+      for (; left > 0 && bb < a.B; ++bb, p_lo = 0) {
+        int Lb = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
+        Lb = Lb < 0 ? 0 : (Lb > a.max_seq_len ? a.max_seq_len : Lb);
+        const int ntb = (Lb + kTileGroup - 1) / kTileGroup;
+        const int pm = a.P < ntb ? a.P : ntb;
+        const int take = (int)(left < pm - p_lo ? left : pm - p_lo);
+        if (take <= 0) continue;
+        decode_unit<QT, W, TOK, HG, T>(a, lane, wave, bb, hh, Lb, p_lo, p_lo + take, p_lo, take,
+                                       1);
+        left -= take;
+      }
+      return;
+    }
+  }
+  const int h = (int)(item % nhs) * (HG ? W : 1) + (HG ? wave : 0);
+  const int b = (int)((item / nhs) % a.B);
+  const int grp = (int)(item / ((int64_t)nhs * a.B));
+
+  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);  // wave-uniform
+  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int ntg = (L + kTileGroup - 1) / kTileGroup;
+  // Partitions that hold tokens: p < pmax.  The workgroup owns partitions
+  // [part_first, p_end): with one tile-group per partition a run of consecutive ones per
+  // wave (up to R = run_len), else one partition (with its strided tile-groups) per wave.
+  // The W wave states are merged into the statistics of partition part_first and the
+  // workgroup's other partitions are written as empty (m = -inf, l = 0).  The
+  // flash-combine of the reduce gives the same result as for separate partitions, and
+  // the partial rows written to HBM shrink up to W * R times.
+  const int pmax = a.P < ntg ? a.P : ntg;
+  const int R = a.run_len > 0 ? a.run_len : 1;
+  int part_first, p_end, first_tg, n_tg, step;
+  if (HG && a.run_len > 0) {
+    // this sequence's pmax partitions in G nearly equal runs of at most R; every wave
+    // streams the whole run for its own kv head
+    const int G = (pmax + R - 1) / R;
+    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
+    part_first = (int)((int64_t)grp * pmax / G);
+    p_end = (int)((int64_t)(grp + 1) * pmax / G);
+    first_tg = part_first;
+    n_tg = p_end - part_first;
+    step = 1;
+  } else if (HG) {
+    // partition grp (its strided tile-groups) for each wave's kv head
+    part_first = grp;
+    if (part_first >= pmax) return;  // workgroup-uniform
+    p_end = part_first + 1;
+    first_tg = part_first;
+    n_tg = (ntg - first_tg + a.P - 1) / a.P;
+    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+    step = a.P;
+  } else if (a.run_len > 0) {
+    // this sequence's pmax partitions in G nearly equal groups of at most W * R, and a
+    // group's m partitions nearly equally over its W waves (no wave idles at the merge
+    // for a whole run)
+    const int G = (pmax + W * R - 1) / (W * R);
+    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
+    part_first = (int)((int64_t)grp * pmax / G);
+    p_end = (int)((int64_t)(grp + 1) * pmax / G);
+    const int m = p_end - part_first;
+    first_tg = part_first + wave * m / W;
+    n_tg = part_first + (wave + 1) * m / W - first_tg;
+    step = 1;
+  } else {
+    part_first = grp * W;
+    if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
+    p_end = part_first + W < pmax ? part_first + W : pmax;
+    // partition part_first + wave owns the strided tile-groups p, p + P, ...
+    first_tg = part_first + wave;
+    n_tg = first_tg < pmax ? (ntg - first_tg + a.P - 1) / a.P : 0;
+    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+    step = a.P;
+  }
+
+  decode_unit<QT, W, TOK, HG, T>(a, lane, wave, b, h, L, part_first, p_end, first_tg, n_tg,
+                                 step);
+}
+
 }  // namespace
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales,
@@ -661,31 +736,39 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   // HG: one workgroup per (W kv heads, sequence, run); else per (kv head, sequence, W runs)
   const int64_t groups = hg ? (int64_t)a.runs
                             : ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
-  const int64_t items = groups * a.B * (hg ? a.Hk / W : a.Hk);
+  const int64_t items = a.balanced_items > 0 ? (int64_t)a.balanced_items * (a.Hk / W)
+                                             : groups * a.B * (hg ? a.Hk / W : a.Hk);
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)items), block(64 * W);
-#define UQ_FP8_LAUNCH(QT, TOK, HG)                                                         \
-  do {                                                                                    \
-    if (T == 1)                                                                           \
-      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 1>), grid, block, 0, stream, p); \
-    else                                                                                  \
-      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 2>), grid, block, 0, stream, p); \
+#define UQ_FP8_LAUNCH(QT, TOK, HG, BAL)                                                        \
+  do {                                                                                         \
+    if (T == 1)                                                                                \
+      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 1, BAL>), grid, block, 0, stream, p); \
+    else                                                                                       \
+      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 2, BAL>), grid, block, 0, stream, p); \
   } while (0)
+  const bool bal = hg && a.balanced_items > 0;
   for (int rb = 0; rb < rows; rb += 16) {
     DecodeArgs p = a;
     p.row_base = rb;
-    if (hg) {
+    if (bal) {
       if (tok_scales) {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, true, true); else UQ_FP8_LAUNCH(uint16_t, true, true);
+        if (q_is_f32) UQ_FP8_LAUNCH(float, true, true, true); else UQ_FP8_LAUNCH(uint16_t, true, true, true);
       } else {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, false, true); else UQ_FP8_LAUNCH(uint16_t, false, true);
+        if (q_is_f32) UQ_FP8_LAUNCH(float, false, true, true); else UQ_FP8_LAUNCH(uint16_t, false, true, true);
+      }
+    } else if (hg) {
+      if (tok_scales) {
+        if (q_is_f32) UQ_FP8_LAUNCH(float, true, true, false); else UQ_FP8_LAUNCH(uint16_t, true, true, false);
+      } else {
+        if (q_is_f32) UQ_FP8_LAUNCH(float, false, true, false); else UQ_FP8_LAUNCH(uint16_t, false, true, false);
       }
     } else {
       if (tok_scales) {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, true, false); else UQ_FP8_LAUNCH(uint16_t, true, false);
+        if (q_is_f32) UQ_FP8_LAUNCH(float, true, false, false); else UQ_FP8_LAUNCH(uint16_t, true, false, false);
       } else {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, false, false); else UQ_FP8_LAUNCH(uint16_t, false, false);
+        if (q_is_f32) UQ_FP8_LAUNCH(float, false, false, false); else UQ_FP8_LAUNCH(uint16_t, false, false, false);
       }
     }
     const hipError_t e = hipGetLastError();

@@ -29,6 +29,8 @@ struct DecodeArgs {
   int32_t head_groups;  // fp8: 1 = a workgroup's waves are consecutive kv heads of one run
   int32_t row_base;     // fp8: first unit row of this launch (wide groups run in passes of
                         // 16 rows; set by the launcher)
+  int32_t balanced_items;  // fp8 head groups: > 0 = the partitions of all sequences are
+                           // split on the device into this many equal slices per head group
   float softmax_scale;
   uint16_t* part_o;            // bf16 [B, Hk, P, QL*QG, D]
   float* part_m;               // [B, Hk, P, QL*QG]
