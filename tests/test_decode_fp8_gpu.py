@@ -328,3 +328,48 @@ def test_wide_query_groups(qg, hk):
     for P in (1, 3):
         got, _ = run_decode(case, P=P)
         assert_decode_close(got, oracle_decode(case), f"wide qg={qg} hk={hk} P={P}")
+
+
+def _bal_lens(rng, B, zeros, lo, hi, long_len):
+    lens = rng.integers(lo, hi, size=B)
+    lens[rng.choice(B, zeros, replace=False)] = 0
+    lens[0] = long_len
+    return tuple(int(x) for x in lens)
+
+
+@pytest.mark.parametrize("qg,hk", [(8, 4), (4, 8)])
+def test_balanced_slices_sparse_batch(qg, hk):
+    """Enough work for balanced slices (one workgroup per CU, each an equal share of all
+    sequences' partitions) but mostly empty or tiny sequences, so fewer partitions than
+    slices: empty slices, slices that start on empty sequences, units split at
+    sequence boundaries."""
+    need_gpu()
+    rng = np.random.default_rng(90 + qg)
+    lens = _bal_lens(rng, 300, 60, 1, 300, 16000)
+    case = small(hk=hk, qg=qg, lens=lens, seed=91 + hk)
+    log(f"case fp8 balanced sparse B={case.B} hk={hk} qg={qg}")
+    got, _ = run_decode(case, P=64)
+    assert_decode_close(got, oracle_decode(case), f"balanced sparse hk={hk}")
+
+
+def test_balanced_slices_one_long_sequence():
+    """A batch dominated by one 60000-token sequence: its partitions are split over many
+    slices (one unit each), the other sequences share the rest."""
+    need_gpu()
+    rng = np.random.default_rng(93)
+    lens = _bal_lens(rng, 120, 10, 1000, 3000, 60000)
+    case = small(hk=8, qg=2, lens=lens, seed=94)
+    log(f"case fp8 balanced long B={case.B}")
+    got, _ = run_decode(case, P=256)
+    assert_decode_close(got, oracle_decode(case), "balanced one long")
+
+
+def test_balanced_slices_wide_group():
+    """Balanced slices with a 24-row query group (two launches: rows 0-15, 16-23)."""
+    need_gpu()
+    rng = np.random.default_rng(95)
+    lens = _bal_lens(rng, 200, 5, 100, 8000, 8000)
+    case = small(hk=4, qg=24, lens=lens, seed=96)
+    log(f"case fp8 balanced wide B={case.B} qg=24")
+    got, _ = run_decode(case, P=64)
+    assert_decode_close(got, oracle_decode(case), "balanced wide qg=24")
