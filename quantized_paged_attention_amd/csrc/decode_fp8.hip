@@ -17,6 +17,9 @@
 //     the run's other partitions are written as empty (m = -inf, l = 0), which the
 //     flash-combine reduce treats as absent, and the partial rows written to HBM shrink
 //     by the run length.
+//   * Balanced slices (head groups with much work): one workgroup per CU, each taking an
+//     equal share of all sequences' partitions, split on the device from the lengths, so
+//     ragged lengths leave no tail (B=128, L ~ U[4k, 16k] on MI355X: 469 -> 409 us).
 //   * Measured on MI355X: partial-row write-backs interleaved with the KV read stream
 //     cost far more than their bytes (88 MB of partials: +90 us on a 480 us stream);
 //     the same stores kept L2-resident cost ~4 us.  With non-temporal KV loads and whole
@@ -587,14 +590,22 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 
 
 
+// The decode kernel: which units a workgroup's waves stream.
+//   BAL (balanced slices, head groups only): workgroup = (group of W kv heads, slice s of
+//     N); the slice is an equal share of all sequences' partitions, streamed as one unit
+//     per sequence it touches.  One workgroup per CU, so the kernel is compiled for one
+//     wave per SIMD (AGPRs available, no spills).
+//   HG: workgroup = (group of W kv heads, sequence, run); wave w streams kv head W g + w
+//     over the run's partitions, so the W waves read neighbouring slots of the same
+//     blocks together.
+//   Otherwise: workgroup = (kv head, sequence, group of W runs) with the W runs split over
+//     the waves and merged in LDS.
 template <typename QT, int W, bool TOK, bool HG, int T, bool BAL>
 __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8_kernel(
     DecodeArgs a) {
+  static_assert(!BAL || HG, "balanced slices are built on head groups");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // HG: (group of W kv heads, sequence, run): wave w streams kv head W g + w over the
-  // run's partitions, so the W waves read neighbouring slots of the same blocks together.
-  // Otherwise: (kv head, sequence, group of W runs) with the W runs split over the waves.
   const int64_t item = blockIdx.x;
   const int nhs = HG ? a.Hk / W : a.Hk;
   if constexpr (BAL) {
@@ -733,7 +744,8 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   const int T = rows <= 8 ? 1 : 2;
   if (rows > 64) return hipErrorInvalidValue;
   const int R = a.run_len > 0 ? a.run_len : 1;
-  // HG: one workgroup per (W kv heads, sequence, run); else per (kv head, sequence, W runs)
+  // BAL: one workgroup per (W kv heads, slice); HG: per (W kv heads, sequence, run); else
+  // per (kv head, sequence, W runs)
   const int64_t groups = hg ? (int64_t)a.runs
                             : ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
   const int64_t items = a.balanced_items > 0 ? (int64_t)a.balanced_items * (a.Hk / W)
