@@ -622,35 +622,41 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
         const int ntb = (Lb + kTileGroup - 1) / kTileGroup;
         return a.P < ntb ? a.P : ntb;
       };
-      int64_t Tt = 0;
-      for (int c = 0; c < a.B; c += 64) {
-        int v = c + lane < a.B ? parts_of(c + lane) : 0;
+      // Lane l holds sequences [l per, (l + 1) per) (per <= 16: the launcher takes this
+      // path for B <= 1024 only); all their lengths are loaded at once, so finding the
+      // slice costs one memory round trip.
+      const int per = (a.B + 63) >> 6;
+      int pm[16];
+      int lsum = 0;
 #pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-        Tt += __builtin_amdgcn_readfirstlane(v);
+      for (int i = 0; i < 16; ++i) {
+        const int q = lane * per + i;
+        pm[i] = i < per && q < a.B ? parts_of(q) : 0;
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lsum += pm[i];
+      int incl = lsum;  // inclusive prefix sum over the lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d, 64);
+        incl += lane >= d ? u : 0;
+      }
+      const int64_t Tt = __builtin_amdgcn_readlane(incl, 63);
       const int64_t s0 = slice * Tt / N, s1 = (slice + 1) * Tt / N;
       if (s0 >= s1) return;  // workgroup-uniform
-      // the sequence holding entry s0, and s0's partition index in it
-      int bb = 0;
-      int64_t off = s0;
-      for (int c = 0; c < a.B; c += 64) {
-        const int v = c + lane < a.B ? parts_of(c + lane) : 0;
-        int incl = v;  // inclusive prefix sum over the lanes
+      // the lane, then the sequence within it, holding entry s0, and s0's partition index
+      const int ln = __builtin_popcountll(__builtin_amdgcn_ballot_w64((int64_t)incl <= s0));
+      int64_t off = s0 - (__builtin_amdgcn_readlane(incl, ln) - __builtin_amdgcn_readlane(lsum, ln));
+      int bb = ln * per;
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int u = __shfl_up(incl, d, 64);
-          incl += lane >= d ? u : 0;
-        }
-        const int tot = __builtin_amdgcn_readlane(incl, 63);
-        if (off < tot) {
-          const uint64_t past = __builtin_amdgcn_ballot_w64((int64_t)incl <= off);
-          const int i = __builtin_popcountll(past);  // first lane whose prefix passes off
-          off -= i > 0 ? __builtin_amdgcn_readlane(incl, i - 1) : 0;
-          bb = c + i;
+      for (int i = 0; i < 16; ++i) {
+        const int v = __builtin_amdgcn_readlane(pm[i], ln);
+        if (i < per && off >= v && bb + 1 < a.B) {
+          off -= v;
+          ++bb;
+        } else {
           break;
         }
-        off -= tot;
       }
       int64_t left = s1 - s0;
       int p_lo = (int)off;
@@ -738,6 +744,8 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   constexpr int W = 4;
   const bool hg = a.head_groups != 0;
   if (hg && a.Hk % W != 0) return hipErrorInvalidValue;
+  // balanced slices hold up to 16 sequence lengths per lane
+  if (a.balanced_items > 0 && (!hg || a.B > 1024)) return hipErrorInvalidValue;
   // row tiles of 8 query rows, 1 or 2 per launch; wider groups run in passes of 16 rows,
   // each reading the KV stream once (4 tiles per wave would spill)
   const int rows = a.QL * a.QG;

@@ -201,11 +201,14 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
         a.runs = (pmax + a.run_len - 1) / a.run_len;
         // With much work, balanced slices instead: one workgroup per compute unit, each
         // taking an equal share of all sequences' partitions (split on the device from
-        // the lengths), so ragged lengths leave no tail.  Measured on MI355X (B=128,
-        // L ~ U[4k, 16k]): decode 469 -> 421 us; two or three workgroups per unit 439 /
-        // 453 us.  With little work the runs above already fill one round (B=16, L=16k:
-        // 88 us, balanced 91 us).
-        if (units * pmax > 16 * cus) a.balanced_items = (int)(cus / (num_kv_heads / 4) > 0 ? cus / (num_kv_heads / 4) : 1);
+        // the lengths, up to 16 per lane: B <= 1024), so ragged lengths leave no tail.
+        // Measured on MI355X (B=128, L ~ U[4k, 16k]): decode 469 -> 409 us; two or three
+        // workgroups per unit 439 / 453 us.  With little work the runs above already fill
+        // one round (B=16, L=16k: 88 us either way).
+        if (units * pmax > 16 * cus && num_seqs <= 1024) {
+          const int64_t per_hg = cus / (num_kv_heads / 4);
+          a.balanced_items = (int)(per_hg > 0 ? per_hg : 1);
+        }
       }
     }
     return launch_status(uq::launch_decode_fp8(a, q_dtype == UQ_F32, tok, static_cast<hipStream_t>(stream)),

@@ -373,3 +373,16 @@ def test_balanced_slices_wide_group():
     log(f"case fp8 balanced wide B={case.B} qg=24")
     got, _ = run_decode(case, P=64)
     assert_decode_close(got, oracle_decode(case), "balanced wide qg=24")
+
+
+def test_balanced_slices_many_sequences():
+    """1000 sequences (16 lengths per lane of the slice lookup), lengths 0..900 with a few
+    long ones: balanced slices start in the middle of lanes' runs of sequences."""
+    need_gpu()
+    rng = np.random.default_rng(97)
+    lens = rng.integers(0, 900, size=1000)
+    lens[rng.choice(1000, 20, replace=False)] = rng.integers(4000, 9000, size=20)
+    case = small(hk=4, qg=2, lens=tuple(int(x) for x in lens), seed=98)
+    log(f"case fp8 balanced B={case.B}")
+    got, _ = run_decode(case, P=64)
+    assert_decode_close(got, oracle_decode(case), "balanced 1000 sequences")
