@@ -1,24 +1,30 @@
 """Benchmark of the quantized paged-attention hot path on one MI355X.
 
-Default workload (the headline): one decode step = uq_paged_decode + uq_paged_reduce over
-the high-batch fp8 batch (B=128, Hk=8, QG=8, D=128, L ~ U[4096, 16384], block 16, 64
-partitions of 256 tokens, per-tensor e4m3 K/V).  Other workloads (--workload):
-fp8_mid (B=16, L=16384), fp8_high_tok (the high-batch shape with per-token f32 K and V
-scales: 264 algorithmic bytes per (token, head)), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions,
-e2m1 + e4m3 group scales, in-kernel rotation), the same fp8 and FP4 shapes with QL query
-rows per sequence (fp8_high_mtp{QL}_qg{QG}, fp4_d256_mtp{QL}_qg{QG}: each row has its own
-causal window), nvfp4_index_ql{QL}_h{H} (32 requests, L ~ U[1024, 32768]: one
-uq_index_score call is a step).  Inputs are generated once,
-copied to HBM, and are resident before the timed region starts.  The KV cache (or the
-index pages) is held in as many copies as make at least 1 GiB, and step i reads copy
-i mod n: no step finds its bytes in L2 or the 256 MB MALL left there by the step before,
-as after a >= 1 GiB cache flush, while the timed steps still run back to back.
+Default workload (the headline): one decode step = uq_paged_attention (decode and
+flash-combine; one launch for the fp8 head-group kernels) over the high-batch fp8 batch
+(B=128, Hk=8, QG=8, D=128, L ~ U[4096, 16384], block 16, 64 partitions of 256 tokens,
+per-tensor e4m3 K/V).  Other workloads (--workload): fp8_mid (B=16, L=16384),
+fp8_high_tok (the high-batch shape with per-token f32 K and V scales: 264 algorithmic bytes
+per (token, head)), fp4_d256_qg{6,8,16} (B=4, Hk=2, D=256, L=75000, 512 partitions, e2m1 +
+e4m3 group scales, in-kernel rotation; decode + reduce), the same fp8 and FP4 shapes with
+QL query rows per sequence (fp8_high_mtp{QL}_qg{QG}, fp4_d256_mtp{QL}_qg{QG}: each row has
+its own causal window), nvfp4_index_ql{QL}_h{H} (32 requests, L ~ U[1024, 32768]: one
+uq_index_score call is a step).  Inputs are generated once, copied to HBM, and are
+resident before the timed region starts.  The KV cache (or the index pages) is held in as
+many copies as make at least 1 GiB, and step i reads copy i mod n: no step finds its bytes
+in L2 or the 256 MB MALL left there by the step before, as after a >= 1 GiB cache flush,
+while the timed steps still run back to back.
+
+Order of the passes, each of K steps: W warm-up steps; an instrumented pass with a HIP
+event before each step and after each kernel (per-kernel means and percentiles, the
+step's median / p10 / p90); the timed bare pass (`value`, `ms_per_step`: K steps back to
+back between two synchronisations); a HIP-graph pass (one captured step per input copy,
+K replays back to back).
 
 Prints ONE JSON line: value = effective KV-stream GB/s (algorithmic bytes of every visible
-(token, head) / step wall time over K steps run back to back), with the dominant kernel's
-roofline (HIP events on the launch stream, from a second pass of the same K steps with an
-event around every kernel) and the fp64 CPU oracle timed on a bounded sample of the same
-workload.
+(token, head) / step wall time of the bare pass), with the dominant kernel's roofline (HIP
+events of the instrumented pass) and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -72,6 +78,16 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _timed_passes(fn, min_seconds: float, max_passes: int = 8):
     passes, t0 = 0, time.perf_counter()
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
@@ -97,7 +113,7 @@ def cpu_baseline_decode(case, n_seqs: int, min_seconds: float = 10.0):
                               query_len=sub.query_len, k_scale_tok=sub.k_scale_tok,
                               v_scale_tok=sub.v_scale_tok), min_seconds)
     return {"value": round(passes * sub.kv_bytes() / dt / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {n_seqs} of {case.B} sequences, all {case.num_kv_heads} kv heads "
                       f"({sub.kv_bytes() / 1e6:.1f} MB of KV) x {passes} passes, fp64, "
                       f"{dt:.2f} s wall"}
@@ -111,7 +127,7 @@ def cpu_baseline_index(case, min_seconds: float = 10.0):
                                    query_len=case.query_len, scores_init=case.scores_init()),
         min_seconds)
     return {"value": round(passes * case.unique_page_bytes() / dt / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"all {case.num_reqs} requests ({case.page_bytes() / 1e6:.1f} MB of "
                       f"pages) x {passes} passes, fp64, {dt:.2f} s wall"}
 
@@ -221,8 +237,9 @@ def main():
         sl = torch.from_numpy(case.seq_lens).to(dev)
         scores = torch.from_numpy(case.scores_init().copy()).to(dev)
 
-        def kernels(pages):
-            uq.index_score(q, pages, bt, sl, scores, query_len=case.query_len, stream=stream)
+        def step(pages, st):
+            uq.index_score(q, pages, bt, sl, scores, query_len=case.query_len, stream=st)
+        kernel_calls = [step]       # one kernel per step
         algo_bytes = case.unique_page_bytes()   # = page_bytes() when no page is shared
         names = ("index_score",)
         dtype = "f16"
@@ -245,68 +262,92 @@ def main():
         else:
             ks = vs = None
         rot = torch.from_numpy(case.rot_signs).to(dev) if case.rot_signs is not None else None
-        po, pm, pl = uq.alloc_partials(B, hk, QL * case.QG, D, P, dev)
-        out = torch.empty(B * QL, Hq, D, dtype=qdt, device=dev)
         max_len = case.max_seq_len
+        ws = uq.alloc_workspace(B, hk, QL, case.QG, D, P, max_len, case.kv_format, dev)
+        out = torch.empty(B * QL, Hq, D, dtype=qdt, device=dev)
+        # one launch per step when the decode finishes the flash-combine itself (fp8 head
+        # groups), else decode + reduce inside the same call
+        fused = is_fp8 and hk % 4 == 0
+        kw = dict(kv_format=case.kv_format, max_seq_len=max_len, num_partitions=P,
+                  softmax_scale=case.softmax_scale, k_scale=ks, v_scale=vs, rot_signs=rot,
+                  query_len=QL)
 
-        def decode(cache):
-            uq.paged_decode(q, cache, bt, sl, kv_format=case.kv_format, max_seq_len=max_len,
-                            num_partitions=P, part_out=po, part_max=pm, part_sum=pl,
-                            softmax_scale=case.softmax_scale, k_scale=ks, v_scale=vs,
-                            rot_signs=rot, query_len=QL, stream=stream)
+        def step(cache, st):
+            uq.paged_attention(q, cache, bt, sl, out=out, workspace=ws, stream=st, **kw)
 
-        def reduce():
-            uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, query_len=QL,
-                            stream=stream)
+        if fused:
+            kernel_calls = [step]
+            names = ("decode_fp8_fused",)
+        else:
+            # the same two kernels uq_paged_attention launches, called one at a time so
+            # that an event can sit between them
+            po, pm, pl = uq.alloc_partials(B, hk, QL * case.QG, D, P, dev)
 
-        def kernels(cache):
-            decode(cache)
-            reduce()
+            def dec(cache, st):
+                uq.paged_decode(q, cache, bt, sl, part_out=po, part_max=pm, part_sum=pl,
+                                stream=st, **kw)
+
+            def red(cache, st):
+                uq.paged_reduce(po, pm, pl, sl, out, max_seq_len=max_len, query_len=QL,
+                                stream=st)
+            kernel_calls = [dec, red]
+            names = (f"decode_{fam}", "reduce")
         algo_bytes = case.kv_bytes()
-        names = (f"decode_{fam}", "reduce")
         dtype = "fp8" if is_fp8 else "f16"
 
     n_in = len(inputs)
-    for i in range(args.warmup):
-        kernels(inputs[i % n_in])
-    torch.cuda.synchronize()
-
-    # Timed region: K steps back to back with nothing else on the stream.  A HIP event
-    # record between kernels costs the stream about 4 us on MI355X (B=128 fp8: 480 us per
-    # step bare, 486 with one event per step, 490 with three), so the per-kernel events
-    # run in a second, instrumented pass of the same K steps right after.
     K = args.steps
+    for i in range(args.warmup):
+        step(inputs[i % n_in], stream)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        kernels(inputs[i % n_in])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
-    # instrumented pass: an event before each step and one after each kernel, on the
-    # launch stream
-    nk = len(names)
+    # Instrumented pass (untimed for `value`): an event before each step and after each
+    # kernel, on the launch stream, gives per-kernel times and the spread of the step.
+    nk = len(kernel_calls)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
-        if fam == "index":
-            kernels(inputs[i % n_in])
-            ev[i][1].record(stream)
-        else:
-            decode(inputs[i % n_in])
-            ev[i][1].record(stream)
-            reduce()
-            ev[i][2].record(stream)
+        for j, call in enumerate(kernel_calls):
+            call(inputs[i % n_in], stream)
+            ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t1
-
     k_ms = [np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)]) for j in range(nk)]
+    step_ev_ms = np.array([ev[i][0].elapsed_time(ev[i][nk]) for i in range(K)])
+
+    # Timed region: K steps back to back with nothing else on the stream.  A HIP event
+    # record between kernels costs the stream about 4 us on MI355X, so the events live in
+    # the pass above and this one is bare.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(inputs[i % n_in], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # HIP-graph replay: one captured step per input copy (no launch overhead on the host
+    # side), K replays back to back.
+    graphs = []
+    cap = torch.cuda.Stream()
+    for c in range(n_in):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(inputs[c], cap)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(K):
+        graphs[i % n_in].replay()
+    torch.cuda.synchronize()
+    wall_graph = time.perf_counter() - t2
+
     step_ms = wall * 1e3 / K
     value = algo_bytes / (step_ms * 1e-3) / 1e9
     dom_avg = float(k_ms[0].mean())          # the dominant kernel: decode, or the scorer
     achieved = algo_bytes / (dom_avg * 1e-3) / 1e9
+    pct = lambda a, p: round(float(np.percentile(a, p)) * 1e3, 2)
 
     res = {
         "metric": (METRIC if workload == "fp8_high" else
@@ -320,6 +361,9 @@ def main():
         "ms_per_step": round(step_ms, 5),
         "us_per_step": round(step_ms * 1e3, 2),
         "us_per_step_instrumented": round(wall_ev * 1e6 / K, 2),
+        "us_per_step_graph": round(wall_graph * 1e6 / K, 2),
+        "step_us_events": {"median": pct(step_ev_ms, 50), "p10": pct(step_ev_ms, 10),
+                           "p90": pct(step_ev_ms, 90)},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -334,7 +378,9 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(workload)},
     }
-    res["kernels_us"][f"{names[0]}_median"] = round(float(np.median(k_ms[0])) * 1e3, 2)
+    res["kernels_us"][f"{names[0]}_median"] = pct(k_ms[0], 50)
+    res["kernels_us"][f"{names[0]}_p10"] = pct(k_ms[0], 10)
+    res["kernels_us"][f"{names[0]}_p90"] = pct(k_ms[0], 90)
     if fam != "index":
         res["config"].update(global_batch=case.B, seq_len_max=case.max_seq_len,
                              query_len=case.query_len)

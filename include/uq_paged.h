@@ -183,6 +183,40 @@ int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float
                         int32_t max_seq_len, void* out, int out_dtype, int64_t o_stride_seq,
                         int64_t o_stride_head, void* stream);
 
+/* uq_paged_attention -- one whole decode step: uq_paged_decode_mtp and the flash-combine
+ * of uq_paged_reduce_mtp ([P3] partition split + parallel reduce) in one call, writing
+ * the attention output directly.  The result is that of the two calls in sequence:
+ *   out[b*query_len + j, h*QG + g, :] = v_scale * sum_t exp(s_t - M) v_t / sum_t exp(s_t - M)
+ * over the tokens t the query row sees (0 when it sees none), in the query dtype.
+ * Arguments as uq_paged_decode_mtp, except that the partial buffers are replaced by:
+ *   workspace       device buffer of workspace_bytes >= uq_attention_workspace_bytes(...)
+ *                   for the same sizes, 256-byte aligned.  It must be zero-filled once
+ *                   before its first use (e.g. hipMemset after allocating it); every
+ *                   call that completes leaves it fit for the next call of any sizes
+ *                   that fit it (the arrival counters it holds return to zero), so it can
+ *                   be reused across calls and graph replays.  Calls that overlap in time
+ *                   on one workspace race.
+ *   out             [num_seqs * query_len, num_q_heads, head_dim] of q_dtype, element
+ *                   strides o_stride_seq / o_stride_head (> 0, 16-byte multiples; the head
+ *                   dim is contiguous, out 16-byte aligned).
+ * How it runs: with the fp8 formats and num_kv_heads a multiple of 4 one launch; every work
+ * unit of a (sequence, kv head) that does not cover the whole sequence leaves its softmax
+ * state in the workspace and counts its partitions with a device-scope atomic, and the
+ * unit that completes the count merges the states and writes the output rows.  Other
+ * formats and head counts run the decode into partials held in the workspace, then the
+ * reduce (two launches).  Errors as uq_paged_decode_mtp, plus UQ_ERR_INVALID_ARG for a
+ * NULL, misaligned or too small workspace or output. */
+int uq_paged_attention(const void* query, int q_dtype, int64_t q_stride_seq,
+                       int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
+                       int kv_format, const float* k_scale, const float* v_scale,
+                       const int8_t* rot_signs, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                       int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                       float softmax_scale, int32_t num_partitions, void* workspace,
+                       size_t workspace_bytes, void* out, int64_t o_stride_seq,
+                       int64_t o_stride_head, void* stream);
+
 /* uq_index_score -- nvfp4 index scores ([P2] compile_score_decode).  For request r,
  * query row j < query_len, index head h and page b < ceil(L_r / 128):
  *   scores[h, r*QL + j, b] = max over tokens t of page b with t <= L_r - QL + j of
@@ -197,7 +231,10 @@ int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float
  *   block_table [num_reqs, bt_stride] int32 page ids; seq_lens [num_reqs] int32.
  *   scores   fp32 [heads, num_reqs*query_len, max_blocks], element strides s_stride_head,
  *            s_stride_row (page index contiguous).  Cells with b >= ceil(L_r/128) (or
- *            b >= max_blocks) are not written.
+ *            b >= max_blocks) are not written.  s_stride_row >= max_blocks, and with
+ *            heads > 1 the heads' planes may not overlap: s_stride_head >=
+ *            (num_reqs*query_len - 1) * s_stride_row + max_blocks (else
+ *            UQ_ERR_INVALID_ARG).
  *   init_blocks, local_blocks: sentinel block counts of [P2] block_sentinels; their
  *            semantics are not given on the page, so both must be 0.
  * Supported: head_dim 128, heads in {1, 2, 4}, 1 <= heads*query_len <= 32.
@@ -215,6 +252,12 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
  * part_sum), each rounded up to 256 bytes; 0 on invalid sizes.  Host-only. */
 size_t uq_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t qg,
                                  int32_t head_dim, int32_t num_partitions);
+
+/* Bytes of the uq_paged_attention workspace for these sizes on the current device (the
+ * work decomposition depends on its compute-unit count); 0 on invalid sizes.  Host-only. */
+size_t uq_attention_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t query_len,
+                                    int32_t qg, int32_t head_dim, int32_t num_partitions,
+                                    int32_t max_seq_len, int kv_format);
 
 /* Text describing the last non-OK return on the calling thread ("" if none).  The
  * string is owned by the library and valid until the next call on this thread. */

@@ -31,7 +31,10 @@
 //   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
 //     from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query group as an
 //     e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
-//     rotate.  s_q is a per-row power of two: the pair reproduces a bf16 query exactly.
+//     rotate.  s_q is a per-row power of two putting the row's largest magnitude in
+//     [64, 128): the pair reproduces every bf16 element of magnitude >= 2^-2 / s_q (about
+//     amax / 512 to amax / 256) exactly; smaller elements land on the e4m3 subnormal grid
+//     of the lo term, an error of at most 2^-10 / s_q <= 2^-16 amax per element.
 //   * K is read in whole 128-byte lines: each of a tile's two K loads covers 8 tokens x
 //     the full K line (lane (r, n): token (n & 7) or 8 + (n & 7), 16-byte chunk 2r or
 //     2r+1), and one DPP swap with lane n ^ 8 gives every lane chunks 2r, 2r+1 of its
@@ -54,6 +57,8 @@
 //     block ids come from a window preloaded before the stream.  The next tile pair's
 //     K and V loads are issued while the current pair is computed; sched_barrier fences
 //     keep that order (vector loads retire in order: a misplaced wait drains them all).
+#include <type_traits>
+
 #include "uq_device.h"
 #include "uq_kernels.h"
 
@@ -72,24 +77,60 @@ struct VTile {
   i32x4 a, b;  // V bytes [16 (n/2), +16) of tokens 4r + 2 (n&1) and 4r + 2 (n&1) + 1
 };
 
+// A work unit's place in the fused flash-combine of its (sequence, kv head): it streams
+// `take` of the sequence's `pm` partitions that hold tokens.  When take < pm its state
+// goes to slot `slot`; the sequence's units use slots lo..hi.  With balanced slices slot k
+// belongs to slice k - b and is unused when that slice is empty (its share of the Tt
+// partitions over N slices is nothing); Tt = 0 marks every slot of the range used.
+struct FuseUnit {
+  int take, pm;
+  int64_t slot, lo, hi;
+  int64_t Tt, N;
+};
+
+// Output rows of unit rows RB .. RB + 8 T - 1 (those below NR) of sequence b, kv head h
+// set to zero: the flash-combine of a sequence without tokens.
+template <typename QT, int T>
+__device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int lane, const int b,
+                                                 const int h) {
+  const int NR = a.QL * a.QG;
+  constexpr int kLanesPerRow = kD * (int)sizeof(QT) / 16;
+  constexpr int kRowsPerPass = 64 / kLanesPerRow;
+  const int u_end = a.row_base + 8 * T < NR ? a.row_base + 8 * T : NR;
+  for (int u0 = a.row_base; u0 < u_end; u0 += kRowsPerPass) {
+    const int u = u0 + lane / kLanesPerRow;
+    if (u < u_end) {
+      QT* dst = reinterpret_cast<QT*>(a.out) + ((int64_t)b * a.QL + u / a.QG) * a.o_ss +
+                (int64_t)(h * a.QG + u % a.QG) * a.o_sh;
+      *reinterpret_cast<i32x4*>(dst + (lane % kLanesPerRow) * (16 / (int)sizeof(QT))) =
+          i32x4{0, 0, 0, 0};
+    }
+  }
+}
+
 // T: tiles of 8 query rows (QL x QG <= 8 T).  The K/V stream, the K operand and the V^T
 // transpose are shared by the tiles; each tile has its own query operand, softmax state,
 // accumulators, QK MFMA and PV MFMAs (the pages' M-tiles for wide groups).
 // One work unit of a wave: kv head h of sequence b (length L, already clamped), the
 // tile-groups first_tg, first_tg + step, ... (n_tg of them) of the partitions
-// [part_first, p_end) it merges; writes the merged statistics to partition part_first and
-// marks the others of [part_first, p_end) empty.
-template <typename QT, int W, bool TOK, bool HG, int T>
+// [part_first, p_end) it merges.  Without FUSE it writes the merged statistics to
+// partition part_first and marks the others of [part_first, p_end) empty; with FUSE it
+// takes part in the flash-combine of the sequence (FuseUnit) and, as the last of the
+// sequence's units, writes the output rows.
+template <typename QT, int W, bool TOK, bool HG, int T, bool FUSE = false>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane, const int wave,
                                             const int b, const int h, const int L,
                                             const int part_first, const int p_end,
                                             const int first_tg, const int n_tg,
-                                            const int step) {
+                                            const int step, const FuseUnit fz = FuseUnit{}) {
+  static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
   // staging of the merged partition's bf16 output rows (8 rows of 256 bytes per tile, one
-  // tile at a time; one stage per wave with head groups), and the states of waves 1..W-1
-  // handed to wave 0 (per lane and tile: 32 accumulators, m_run, m_true, l)
+  // tile at a time; one stage per wave with head groups; fused: rows of the query dtype),
+  // and the states of waves 1..W-1 handed to wave 0 (per lane and tile: 32 accumulators,
+  // m_run, m_true, l)
   constexpr bool kMerge = W > 1 && !HG;
-  __shared__ __attribute__((aligned(16))) uint16_t o_stage[(HG ? W : 1) * 8 * kD];
+  constexpr int kStageElems = (FUSE ? (int)sizeof(QT) / 2 : 1) * 8 * kD;  // 16-bit units
+  __shared__ __attribute__((aligned(16))) uint16_t o_stage[(HG ? W : 1) * kStageElems];
   __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][T][32][64];
   __shared__ float st_ml[kMerge ? W - 1 : 1][T][3][64];
   const int r = lane >> 4, n = lane & 15;
@@ -490,6 +531,147 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
       for (int m = 0; m < 8; ++m) acc[t][m] *= v_ref;
   }
+
+  if constexpr (FUSE) {
+    // ---- fused flash-combine.  A unit's state is (r, l, acc) per lane: the accumulators
+    //      and the sum l hold sums of 2^(s - r) (exp2 units) with r = m_run - 8, and
+    //      r = -inf (l = 0, acc = 0) for a column that saw no token.
+    float ref[T], lsum[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      ref[t] = m_run[t] == -INFINITY ? -INFINITY : m_run[t] - 8.f;
+      lsum[t] = sum_across_rows(l_run[t]);
+    }
+    if (fz.take < fz.pm) {
+      // Leave the state in this unit's slot, publish it (release at device scope: every
+      // XCD's L2 sees it before the count does), then count the unit's partitions.  The
+      // unit whose count completes the sequence merges; the others are done.
+      auto state_at = [&](int64_t k) {
+        return a.states + ((k * a.Hk + h) * a.state_tiles) * (int64_t)kStateBytes;
+      };
+      uint8_t* st = state_at(fz.slot);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        f32x4* sa = reinterpret_cast<f32x4*>(st + t * kStateBytes);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) sa[m * 64 + lane] = acc[t][m];
+        float* sm = reinterpret_cast<float*>(st + t * kStateBytes + 8 * 64 * 16);
+        sm[lane] = ref[t];
+        sm[64 + lane] = lsum[t];
+      }
+      int32_t* cnt = a.counters + (int64_t)b * a.Hk + h;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      int old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(cnt, fz.take, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __builtin_amdgcn_readfirstlane(old);
+      if (old + fz.take != fz.pm) return;  // wave-uniform: another unit finishes the sequence
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // the next used slot of the range at or after k, other than this unit's own
+      auto next_used = [&](int64_t k) {
+        for (; k <= fz.hi; ++k) {
+          if (k == fz.slot) continue;
+          if (fz.Tt > 0) {
+            const int64_t sl = k - b;
+            if (sl * fz.Tt / fz.N >= (sl + 1) * fz.Tt / fz.N) continue;  // empty slice
+          }
+          break;
+        }
+        return k;
+      };
+      auto merge = [&](int t, const f32x4* x, float rk, float lk) {
+        const float M = fmaxf(ref[t], rk);
+        const float fa = ref[t] == -INFINITY ? 0.f : fast_exp2(ref[t] - M);
+        const float fb = rk == -INFINITY ? 0.f : fast_exp2(rk - M);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[t][m] = acc[t][m] * fa + x[m] * fb;
+        lsum[t] = lsum[t] * fa + lk * fb;
+        ref[t] = M;
+      };
+      // states two at a time (one tile) or one at a time (two tiles), all their loads
+      // issued before the first use
+      constexpr int U = T == 1 ? 2 : 1;
+      for (int64_t k0 = next_used(fz.lo); k0 <= fz.hi;) {
+        int64_t ks[U];
+        ks[0] = k0;
+#pragma unroll
+        for (int u = 1; u < U; ++u) ks[u] = ks[u - 1] <= fz.hi ? next_used(ks[u - 1] + 1) : fz.hi + 1;
+        f32x4 x[U][T][8];
+        float rk[U][T], lk[U][T];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (ks[u] <= fz.hi) {
+            const uint8_t* sk = state_at(ks[u]);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+              const f32x4* sa = reinterpret_cast<const f32x4*>(sk + t * kStateBytes);
+#pragma unroll
+              for (int m = 0; m < 8; ++m) x[u][t][m] = sa[m * 64 + lane];
+              const float* sm = reinterpret_cast<const float*>(sk + t * kStateBytes + 8 * 64 * 16);
+              rk[u][t] = sm[lane];
+              lk[u][t] = sm[64 + lane];
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (ks[u] <= fz.hi)
+#pragma unroll
+            for (int t = 0; t < T; ++t) merge(t, x[u][t], rk[u][t], lk[u][t]);
+        k0 = ks[U - 1] <= fz.hi ? next_used(ks[U - 1] + 1) : fz.hi + 1;
+      }
+      if (lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // ---- output rows: o = v_scale acc / l (0 without tokens), hi and lo columns added;
+    //      the rows go through this wave's LDS stage so that each is written whole
+    uint16_t* stage = o_stage + wave * kStageElems;
+    constexpr int kRowBytes = kD * (int)sizeof(QT);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int nrow = NR - RB - 8 * t < 8 ? NR - RB - 8 * t : 8;
+      if (nrow <= 0) break;  // wave-uniform
+      const float inv = v_scale / (lsum[t] > 0.f ? lsum[t] : 1.f);
+      if (t > 0) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // the previous tile's stage reads are done
+        __builtin_amdgcn_wave_barrier();
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float o[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] = (acc[t][m][j] + row_ror8(acc[t][m][j])) * inv;
+        uint8_t* row = reinterpret_cast<uint8_t*>(stage) + n * kRowBytes;
+        if (n < nrow) {
+          if constexpr (sizeof(QT) == 4) {
+            *reinterpret_cast<f32x4*>(row + 4 * (32 * r + 8 * j)) = f32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<f32x4*>(row + 4 * (32 * r + 8 * j + 4)) = f32x4{o[4], o[5], o[6], o[7]};
+          } else {
+            *reinterpret_cast<i32x4*>(row + 2 * (32 * r + 8 * j)) =
+                i32x4{(int)pack_bf16x2(o[0], o[1]), (int)pack_bf16x2(o[2], o[3]),
+                      (int)pack_bf16x2(o[4], o[5]), (int)pack_bf16x2(o[6], o[7])};
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
+      __builtin_amdgcn_wave_barrier();
+      constexpr int kLanesPerRow = kRowBytes / 16;
+      constexpr int kRowsPerPass = 64 / kLanesPerRow;
+#pragma unroll
+      for (int c = 0; c < 8 / kRowsPerPass; ++c) {
+        const int i = c * kRowsPerPass + lane / kLanesPerRow;  // stage row
+        if (i < nrow) {
+          const int urow = RB + 8 * t + i;
+          QT* dst = reinterpret_cast<QT*>(a.out) + ((int64_t)b * a.QL + urow / a.QG) * a.o_ss +
+                    (int64_t)(h * a.QG + urow % a.QG) * a.o_sh;
+          const int chunk = lane % kLanesPerRow;
+          *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(dst) + 16 * chunk) =
+              *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) +
+                                              i * kRowBytes + 16 * chunk);
+        }
+      }
+    }
+    return;
+  }
   // ---- merge the W wave states into partition part_first: a lane's state belongs to
   //      its column (query head), so the merge is lane-local once the states meet in LDS
   float l_tot[T];
@@ -600,10 +782,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 //     blocks together.
 //   Otherwise: workgroup = (kv head, sequence, group of W runs) with the W runs split over
 //     the waves and merged in LDS.
-template <typename QT, int W, bool TOK, bool HG, int T, bool BAL>
+template <typename QT, int W, bool TOK, bool HG, int T, bool BAL, bool FUSE>
 __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8_kernel(
     DecodeArgs a) {
   static_assert(!BAL || HG, "balanced slices are built on head groups");
+  static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t item = blockIdx.x;
@@ -643,7 +826,18 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
       }
       const int64_t Tt = __builtin_amdgcn_readlane(incl, 63);
       const int64_t s0 = slice * Tt / N, s1 = (slice + 1) * Tt / N;
-      if (s0 >= s1) return;  // workgroup-uniform
+      // fused: the sequences without tokens b = slice, slice + N, ... get zero output rows
+      // from this slice (after its stream, or at once when the slice is empty)
+      auto zero_empty = [&]() {
+        if constexpr (FUSE) {
+          for (int64_t bz = slice; bz < a.B; bz += N)
+            if (parts_of((int)bz) == 0) zero_output_rows<QT, T>(a, lane, (int)bz, hh);
+        }
+      };
+      if (s0 >= s1) {  // workgroup-uniform
+        zero_empty();
+        return;
+      }
       // the lane, then the sequence within it, holding entry s0, and s0's partition index
       const int ln = __builtin_popcountll(__builtin_amdgcn_ballot_w64((int64_t)incl <= s0));
       int64_t off = s0 - (__builtin_amdgcn_readlane(incl, ln) - __builtin_amdgcn_readlane(lsum, ln));
@@ -660,6 +854,7 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
       }
       int64_t left = s1 - s0;
       int p_lo = (int)off;
+      int64_t e = s0;  // list entry of (bb, p_lo)
       for (; left > 0 && bb < a.B; ++bb, p_lo = 0) {
         int Lb = __builtin_amdgcn_readfirstlane(a.seq_lens[bb]);
         Lb = Lb < 0 ? 0 : (Lb > a.max_seq_len ? a.max_seq_len : Lb);
@@ -667,10 +862,26 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
         const int pm = a.P < ntb ? a.P : ntb;
         const int take = (int)(left < pm - p_lo ? left : pm - p_lo);
         if (take <= 0) continue;
-        decode_unit<QT, W, TOK, HG, T>(a, lane, wave, bb, hh, Lb, p_lo, p_lo + take, p_lo, take,
-                                       1);
+        FuseUnit fz{};
+        if constexpr (FUSE) {
+          // the slices holding the sequence's first and last entries: owner(x) =
+          // ceil((x + 1) N / Tt) - 1; unit (bb, slice) keeps its state in slot slice + bb
+          // (one-to-one: a later slice never holds an earlier sequence)
+          const int64_t first = e - p_lo, last = first + pm - 1;
+          fz.take = take;
+          fz.pm = pm;
+          fz.slot = slice + bb;
+          fz.lo = ((first + 1) * N + Tt - 1) / Tt - 1 + bb;
+          fz.hi = ((last + 1) * N + Tt - 1) / Tt - 1 + bb;
+          fz.Tt = Tt;
+          fz.N = N;
+        }
+        decode_unit<QT, W, TOK, HG, T, FUSE>(a, lane, wave, bb, hh, Lb, p_lo, p_lo + take, p_lo,
+                                             take, 1, fz);
         left -= take;
+        e += take;
       }
+      zero_empty();
       return;
     }
   }
@@ -690,6 +901,13 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
   // the partial rows written to HBM shrink up to W * R times.
   const int pmax = a.P < ntg ? a.P : ntg;
   const int R = a.run_len > 0 ? a.run_len : 1;
+  if constexpr (FUSE) {
+    // a sequence without tokens: zero output rows from the first workgroup of its heads
+    if (pmax == 0) {
+      if (grp == 0) zero_output_rows<QT, T>(a, lane, b, h);
+      return;
+    }
+  }
   int part_first, p_end, first_tg, n_tg, step;
   if (HG && a.run_len > 0) {
     // this sequence's pmax partitions in G nearly equal runs of at most R; every wave
@@ -733,8 +951,21 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
     step = a.P;
   }
 
-  decode_unit<QT, W, TOK, HG, T>(a, lane, wave, b, h, L, part_first, p_end, first_tg, n_tg,
-                                 step);
+  FuseUnit fz{};
+  if constexpr (FUSE) {
+    // units (b, grp) keep their states in slots b * runs + grp, grp < the sequence's count
+    // of workgroups (runs of partitions, or single partitions with strided tile-groups)
+    const int G = a.run_len > 0 ? (pmax + R - 1) / R : pmax;
+    fz.take = p_end - part_first;
+    fz.pm = pmax;
+    fz.slot = (int64_t)b * a.runs + grp;
+    fz.lo = (int64_t)b * a.runs;
+    fz.hi = fz.lo + G - 1;
+    fz.Tt = 0;
+    fz.N = 1;
+  }
+  decode_unit<QT, W, TOK, HG, T, FUSE>(a, lane, wave, b, h, L, part_first, p_end, first_tg,
+                                       n_tg, step, fz);
 }
 
 }  // namespace
@@ -751,6 +982,9 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   const int rows = a.QL * a.QG;
   const int T = rows <= 8 ? 1 : 2;
   if (rows > 64) return hipErrorInvalidValue;
+  const bool fuse = a.fused != 0;
+  if (fuse && (!hg || !a.out || !a.counters || !a.states || a.state_tiles != T))
+    return hipErrorInvalidValue;
   const int R = a.run_len > 0 ? a.run_len : 1;
   // BAL: one workgroup per (W kv heads, slice); HG: per (W kv heads, sequence, run); else
   // per (kv head, sequence, W runs)
@@ -761,40 +995,46 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)items), block(64 * W);
-#define UQ_FP8_LAUNCH(QT, TOK, HG, BAL)                                                        \
-  do {                                                                                         \
-    if (T == 1)                                                                                \
-      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 1, BAL>), grid, block, 0, stream, p); \
-    else                                                                                       \
-      hipLaunchKernelGGL((decode_fp8_kernel<QT, W, TOK, HG, 2, BAL>), grid, block, 0, stream, p); \
-  } while (0)
   const bool bal = hg && a.balanced_items > 0;
+  auto go = [&](auto kernel, const DecodeArgs& p) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+  };
+  // one instantiation per (query type, per-token scales, order, row tiles, fused)
+  auto pick = [&](auto qt, auto tok, const DecodeArgs& p) {
+    using QT = decltype(qt);
+    constexpr bool TOK = decltype(tok)::value;
+    if (bal) {
+      if (fuse) {
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, true>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true>, p);
+      } else {
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false>, p);
+      }
+    } else if (hg) {
+      if (fuse) {
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, true>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true>, p);
+      } else {
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false>, p);
+      }
+    } else {
+      if (T == 1) go(decode_fp8_kernel<QT, W, TOK, false, 1, false, false>, p);
+      else go(decode_fp8_kernel<QT, W, TOK, false, 2, false, false>, p);
+    }
+  };
   for (int rb = 0; rb < rows; rb += 16) {
     DecodeArgs p = a;
     p.row_base = rb;
-    if (bal) {
-      if (tok_scales) {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, true, true, true); else UQ_FP8_LAUNCH(uint16_t, true, true, true);
-      } else {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, false, true, true); else UQ_FP8_LAUNCH(uint16_t, false, true, true);
-      }
-    } else if (hg) {
-      if (tok_scales) {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, true, true, false); else UQ_FP8_LAUNCH(uint16_t, true, true, false);
-      } else {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, false, true, false); else UQ_FP8_LAUNCH(uint16_t, false, true, false);
-      }
+    if (tok_scales) {
+      if (q_is_f32) pick(float{}, std::true_type{}, p); else pick(uint16_t{}, std::true_type{}, p);
     } else {
-      if (tok_scales) {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, true, false, false); else UQ_FP8_LAUNCH(uint16_t, true, false, false);
-      } else {
-        if (q_is_f32) UQ_FP8_LAUNCH(float, false, false, false); else UQ_FP8_LAUNCH(uint16_t, false, false, false);
-      }
+      if (q_is_f32) pick(float{}, std::false_type{}, p); else pick(uint16_t{}, std::false_type{}, p);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-#undef UQ_FP8_LAUNCH
   return hipGetLastError();
 }
 

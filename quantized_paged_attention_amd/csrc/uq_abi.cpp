@@ -51,6 +51,8 @@ bool valid_block_size(int bs) {
   return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
 }
 
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 int slot_content(int fmt, int D) {
   if (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) return 2 * D;
   if (fmt == UQ_KV_FP4_E2M1_E4M3S || fmt == UQ_KV_FP4_E2M1_UE8M0S)
@@ -68,20 +70,170 @@ size_t uq_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t
                                  int32_t head_dim, int32_t num_partitions) {
   if (num_seqs < 0 || num_kv_heads <= 0 || qg <= 0 || head_dim <= 0 || num_partitions <= 0)
     return 0;
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)num_seqs * num_kv_heads * num_partitions * qg;
-  return up(rows * head_dim * 2) + 2 * up(rows * 4);
+  return up256(rows * head_dim * 2) + 2 * up256(rows * 4);
 }
 
-int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
-                        int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
-                        int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
-                        int kv_format, const float* k_scale, const float* v_scale,
-                        const int8_t* rot_signs, const int32_t* block_table, int32_t bt_stride,
-                        const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
-                        int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
-                        float softmax_scale, int32_t num_partitions, void* part_out,
-                        float* part_max, float* part_sum, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Work decomposition of a decode launch, from sizes alone (the launches and the workspace
+// size of uq_paged_attention share it).
+struct Plan {
+  int TGPP;            // tile-groups per partition
+  int run_len, runs;   // partitions per work item (0: one partition, strided tile-groups)
+  int head_groups;     // fp8: workgroups of 4 neighbouring kv heads
+  int balanced_items;  // fp8 head groups: slices per head group (0: runs per sequence)
+};
+
+Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len) {
+  Plan p{};
+  const int ntg = (max_seq_len + uq::kTileGroup - 1) / uq::kTileGroup;
+  p.TGPP = ntg == 0 ? 1 : (ntg + P - 1) / P;
+  const int pmax = P < ntg ? P : (ntg > 0 ? ntg : 1);
+  // Work items: with one tile-group per partition a wave streams a run of consecutive
+  // partitions of one (sequence, kv head), so the per-item start-up chain (length ->
+  // block table -> first KV loads) is paid once per run and fewer partial rows are
+  // written.  Measured on MI355X (B=16 / B=128, ctx up to 16k, 64 partitions): runs of
+  // three pay off from 128 partitions per compute unit, runs of two from 16 (shorter
+  // grids would leave compute units idle at the end).
+  if (p.TGPP == 1) {
+    const int64_t work = (int64_t)B * Hk * pmax;
+    p.run_len = work >= 128 * 256 ? 3 : (work >= 16 * 256 ? 2 : 1);
+    p.runs = (pmax + p.run_len - 1) / p.run_len;
+  } else {
+    p.run_len = 0;
+    p.runs = P;
+  }
+  if (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) {
+    // Head groups: with Hk a multiple of 4 a workgroup's 4 waves stream 4 neighbouring kv
+    // heads of one (sequence, run of partitions), so they read the neighbouring slots of
+    // the same blocks together (a load-only kernel measured 6.2 -> 6.6 TB/s for this
+    // order), and each wave writes its own merged partial.  The run length sets how the
+    // workgroups pack onto the compute units.  With little work per compute unit, about
+    // one workgroup per unit with equal runs; with much, enough runs for two rounds of the
+    // three resident workgroups per unit, so that the dispatcher evens out ragged
+    // lengths.  Measured on MI355X (fp8, Hk=8, 64 partitions): B=16, L=16k: run 8
+    // (256 workgroups) 86 us, runs 4 / 6 / 16: 89 / 102 / 129 us; B=128, L ~ U[4k, 16k]:
+    // run 11 472 us, runs 8 / 16 / 22: 482 / 494 / 506 us.
+    if (Hk % 4 == 0) {
+      p.head_groups = 1;
+      if (p.TGPP == 1 && B > 0) {
+        const int64_t units = (int64_t)B * (Hk / 4);
+        const int64_t cus = device_cus();
+        int64_t G;  // runs per (sequence, head group)
+        if (units * pmax <= 16 * cus)
+          G = (cus + units - 1) / units;
+        else
+          G = (6 * cus + units - 1) / units;
+        G = G < 1 ? 1 : (G > pmax ? pmax : G);
+        p.run_len = (int)((pmax + G - 1) / G);
+        p.runs = (pmax + p.run_len - 1) / p.run_len;
+        // With much work, balanced slices instead: one workgroup per compute unit, each
+        // taking an equal share of all sequences' partitions (split on the device from
+        // the lengths, up to 16 per lane: B <= 1024), so ragged lengths leave no tail.
+        // Measured on MI355X (B=128, L ~ U[4k, 16k]): decode 469 -> 409 us; two or three
+        // workgroups per unit 439 / 453 us.  With little work the runs above already fill
+        // one round (B=16, L=16k: 88 us either way).
+        if (units * pmax > 16 * cus && B <= 1024) {
+          const int64_t per_hg = cus / (Hk / 4);
+          p.balanced_items = (int)(per_hg > 0 ? per_hg : 1);
+        }
+      }
+    }
+  } else if (p.TGPP == 1) {
+    // FP4: one workgroup streams a run of R partitions (one query rotation, one merged
+    // partial).  Two workgroups fit a compute unit, and the time goes as (rounds of
+    // resident workgroups) x (R + about one partition of fixed cost per workgroup:
+    // rotation, start-up, merge), so R in [1, 8] minimises ceil(groups / slots) * (R + 1)
+    // (ties: the shorter run).  Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions,
+    // 512 slots, 20 launches back to back): R = 5 (472 groups, one round) 38.6 us;
+    // R = 3, 4, 6, 8: 51.7, 48.9, 42.3, 50.9 us.
+    const int64_t slots = 2LL * device_cus();
+    int best_r = 1;
+    int64_t best_cost = -1;
+    for (int r = 1; r <= 8; ++r) {
+      const int64_t groups = (int64_t)B * Hk * ((pmax + r - 1) / r);
+      const int64_t cost = (groups + slots - 1) / slots * (r + 1);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_r = r;
+      }
+    }
+    p.run_len = best_r;
+    p.runs = (pmax + p.run_len - 1) / p.run_len;
+  }
+  return p;
+}
+
+// Workspace of uq_paged_attention: the [B, Hk] arrival counters, then either the fused
+// states (fp8 head groups: one slot per work unit of a sequence, kStateBytes per kv head
+// and row tile) or the three decode partial buffers.
+struct AttnLayout {
+  bool fused;
+  int tiles;              // row tiles per fused state
+  int64_t slots;          // fused state slots
+  size_t counter_bytes, body_bytes;
+};
+
+AttnLayout attn_layout(int fmt, int B, int Hk, int QL, int QG, int D, int P, int max_seq_len) {
+  AttnLayout l{};
+  const Plan p = plan_decode(fmt, B, Hk, P, max_seq_len);
+  const int rows = QL * QG;
+  l.counter_bytes = up256((size_t)B * Hk * 4);
+  l.fused = (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) && p.head_groups;
+  if (l.fused) {
+    l.tiles = rows <= 8 ? 1 : 2;
+    // balanced slices: unit (b, slice s) uses slot s + b; runs: unit (b, run g) slot
+    // b * runs + g
+    l.slots = p.balanced_items > 0 ? (int64_t)p.balanced_items + B - 1 : (int64_t)B * p.runs;
+    if (l.slots < 1) l.slots = 1;
+    l.body_bytes = up256((size_t)l.slots * Hk * l.tiles * uq::kStateBytes);
+  } else {
+    l.body_bytes = uq_decode_workspace_bytes(B, Hk, rows, D, P);
+  }
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t uq_attention_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t query_len,
+                                    int32_t qg, int32_t head_dim, int32_t num_partitions,
+                                    int32_t max_seq_len, int kv_format) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || query_len < 1 || qg <= 0 || head_dim <= 0 ||
+      num_partitions <= 0 || max_seq_len < 0 || slot_content(kv_format, head_dim) < 0)
+    return 0;
+  const AttnLayout l = attn_layout(kv_format, num_seqs, num_kv_heads, query_len, qg, head_dim,
+                                   num_partitions, max_seq_len);
+  return l.counter_bytes + l.body_bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of the decode kernels.  Without `fused` the partial buffers are
+// the outputs; with it the fp8 head-group kernels finish the flash-combine themselves
+// and write `fused->out` (the caller has checked that the layout is fused).
+struct FusedTarget {
+  void* out;
+  int64_t o_ss, o_sh;
+  int32_t* counters;
+  uint8_t* states;
+  int tiles;
+};
+
+int decode_impl(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_stride_head,
+                const uint8_t* kv_cache, int64_t num_blocks, int32_t block_size,
+                int32_t num_kv_heads, int32_t slot_bytes, int kv_format, const float* k_scale,
+                const float* v_scale, const int8_t* rot_signs, const int32_t* block_table,
+                int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                int32_t query_len, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                float softmax_scale, int32_t num_partitions, void* part_out, float* part_max,
+                float* part_sum, const FusedTarget* fused, void* stream) {
   if (num_seqs < 0) return fail(UQ_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (query_len < 1) return fail(UQ_ERR_INVALID_ARG, "query_len must be >= 1 (got %d)", query_len);
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
@@ -106,8 +258,9 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
     return fail(UQ_ERR_INVALID_ARG, "bt_stride %d cannot hold max_seq_len %d at block size %d",
                 bt_stride, max_seq_len, block_size);
   if (!std::isfinite(softmax_scale)) return fail(UQ_ERR_INVALID_ARG, "softmax_scale is not finite");
-  if (num_seqs > 0 && (!query || !kv_cache || !block_table || !seq_lens || !part_out || !part_max ||
-                       !part_sum))
+  if (num_seqs > 0 && (!query || !kv_cache || !block_table || !seq_lens))
+    return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!fused && num_seqs > 0 && (!part_out || !part_max || !part_sum))
     return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
   if ((reinterpret_cast<uintptr_t>(query) | reinterpret_cast<uintptr_t>(part_out)) & 15)
     return fail(UQ_ERR_INVALID_ARG, "query and part_out must be 16-byte aligned");
@@ -117,6 +270,7 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
   if (reinterpret_cast<uintptr_t>(kv_cache) & 15)
     return fail(UQ_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
 
+  const Plan plan = plan_decode(kv_format, num_seqs, num_kv_heads, num_partitions, max_seq_len);
   uq::DecodeArgs a{};
   a.q = query;
   a.q_ss = q_stride_seq;
@@ -136,29 +290,26 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
   a.QG = QG;
   a.QL = query_len;
   a.P = num_partitions;
-  const int ntg = (max_seq_len + uq::kTileGroup - 1) / uq::kTileGroup;
-  a.TGPP = ntg == 0 ? 1 : (ntg + num_partitions - 1) / num_partitions;
+  a.TGPP = plan.TGPP;
   a.max_seq_len = max_seq_len;
   a.block_size = block_size;
-  // Work items: with one tile-group per partition a wave streams a run of consecutive
-  // partitions of one (sequence, kv head), so the per-item start-up chain (length ->
-  // block table -> first KV loads) is paid once per run and fewer partial rows are
-  // written.  Measured on MI355X (B=16 / B=128, ctx up to 16k, 64 partitions): runs of
-  // three pay off from 128 partitions per compute unit, runs of two from 16 (shorter
-  // grids would leave compute units idle at the end).
-  if (a.TGPP == 1) {
-    const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
-    const int64_t work = (int64_t)num_seqs * num_kv_heads * pmax;
-    a.run_len = work >= 128 * 256 ? 3 : (work >= 16 * 256 ? 2 : 1);
-    a.runs = (pmax + a.run_len - 1) / a.run_len;
-  } else {
-    a.run_len = 0;
-    a.runs = num_partitions;
-  }
+  a.run_len = plan.run_len;
+  a.runs = plan.runs;
+  a.head_groups = plan.head_groups;
+  a.balanced_items = plan.balanced_items;
   a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.part_o = static_cast<uint16_t*>(part_out);
   a.part_m = part_max;
   a.part_l = part_sum;
+  if (fused) {
+    a.fused = 1;
+    a.out = fused->out;
+    a.o_ss = fused->o_ss;
+    a.o_sh = fused->o_sh;
+    a.counters = fused->counters;
+    a.states = fused->states;
+    a.state_tiles = fused->tiles;
+  }
   if ((int64_t)a.pos_stride * block_size > (int64_t)1 << 31)
     return fail(UQ_ERR_UNSUPPORTED, "a physical block larger than 2 GiB is not supported");
 
@@ -175,42 +326,6 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
     if (rot_signs) return fail(UQ_ERR_UNSUPPORTED, "query rotation is supported with fp4 caches only");
     if (slot_bytes % 16) return fail(UQ_ERR_UNSUPPORTED, "fp8 cache needs slot_bytes a multiple of 16");
     if (num_seqs == 0) return ok();
-    // Head groups: with Hk a multiple of 4 a workgroup's 4 waves stream 4 neighbouring kv
-    // heads of one (sequence, run of partitions), so they read the neighbouring slots of
-    // the same blocks together (a load-only kernel measured 6.2 -> 6.6 TB/s for this
-    // order), and each wave writes its own merged partial.  The run length sets how the
-    // workgroups pack onto the compute units.  With little work per compute unit, about
-    // one workgroup per unit with equal runs; with much, enough runs for two rounds of the
-    // three resident workgroups per unit, so that the dispatcher evens out ragged
-    // lengths.  Measured on MI355X (fp8, Hk=8, 64 partitions): B=16, L=16k: run 8
-    // (256 workgroups) 86 us, runs 4 / 6 / 16: 89 / 102 / 129 us; B=128, L ~ U[4k, 16k]:
-    // run 11 472 us, runs 8 / 16 / 22: 482 / 494 / 506 us.
-    if (num_kv_heads % 4 == 0) {
-      a.head_groups = 1;
-      if (a.TGPP == 1) {
-        const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
-        const int64_t units = (int64_t)num_seqs * (num_kv_heads / 4);
-        const int64_t cus = device_cus();
-        int64_t G;  // runs per (sequence, head group)
-        if (units * pmax <= 16 * cus)
-          G = (cus + units - 1) / units;
-        else
-          G = (6 * cus + units - 1) / units;
-        G = G < 1 ? 1 : (G > pmax ? pmax : G);
-        a.run_len = (int)((pmax + G - 1) / G);
-        a.runs = (pmax + a.run_len - 1) / a.run_len;
-        // With much work, balanced slices instead: one workgroup per compute unit, each
-        // taking an equal share of all sequences' partitions (split on the device from
-        // the lengths, up to 16 per lane: B <= 1024), so ragged lengths leave no tail.
-        // Measured on MI355X (B=128, L ~ U[4k, 16k]): decode 469 -> 409 us; two or three
-        // workgroups per unit 439 / 453 us.  With little work the runs above already fill
-        // one round (B=16, L=16k: 88 us either way).
-        if (units * pmax > 16 * cus && num_seqs <= 1024) {
-          const int64_t per_hg = cus / (num_kv_heads / 4);
-          a.balanced_items = (int)(per_hg > 0 ? per_hg : 1);
-        }
-      }
-    }
     return launch_status(uq::launch_decode_fp8(a, q_dtype == UQ_F32, tok, static_cast<hipStream_t>(stream)),
                          "decode_fp8");
   }
@@ -223,35 +338,33 @@ int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
     if (query_len * QG > 16)
       return fail(UQ_ERR_UNSUPPORTED, "fp4 cache supports query_len x query group up to 16 rows (got %d x %d)",
                   query_len, QG);
+    if (fused) return fail(UQ_ERR_UNSUPPORTED, "the fused flash-combine covers fp8 head groups only");
     if (num_seqs == 0) return ok();
-    // One workgroup streams a run of R partitions (one query rotation, one merged
-    // partial).  Two workgroups fit a compute unit, and the time goes as (rounds of
-    // resident workgroups) x (R + about one partition of fixed cost per workgroup:
-    // rotation, start-up, merge), so R in [1, 8] minimises ceil(groups / slots) * (R + 1)
-    // (ties: the shorter run).  Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions,
-    // 512 slots, 20 launches back to back): R = 5 (472 groups, one round) 38.6 us;
-    // R = 3, 4, 6, 8: 51.7, 48.9, 42.3, 50.9 us.
-    if (a.TGPP == 1) {
-      const int pmax = num_partitions < ntg ? num_partitions : (ntg > 0 ? ntg : 1);
-      const int64_t slots = 2LL * device_cus();
-      int best_r = 1;
-      int64_t best_cost = -1;
-      for (int r = 1; r <= 8; ++r) {
-        const int64_t groups = (int64_t)num_seqs * num_kv_heads * ((pmax + r - 1) / r);
-        const int64_t cost = (groups + slots - 1) / slots * (r + 1);
-        if (best_cost < 0 || cost < best_cost) {
-          best_cost = cost;
-          best_r = r;
-        }
-      }
-      a.run_len = best_r;
-      a.runs = (pmax + a.run_len - 1) / a.run_len;
-    }
     return launch_status(uq::launch_decode_fp4(a, q_dtype == UQ_F32, kv_format == UQ_KV_FP4_E2M1_UE8M0S,
                                                static_cast<hipStream_t>(stream)),
                          "decode_fp4");
   }
   return fail(UQ_ERR_UNSUPPORTED, "kv_format %d is not implemented", kv_format);
+}
+
+}  // namespace
+
+extern "C" {
+
+int uq_paged_decode_mtp(const void* query, int q_dtype, int64_t q_stride_seq,
+                        int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
+                        int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
+                        int kv_format, const float* k_scale, const float* v_scale,
+                        const int8_t* rot_signs, const int32_t* block_table, int32_t bt_stride,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                        int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                        float softmax_scale, int32_t num_partitions, void* part_out,
+                        float* part_max, float* part_sum, void* stream) {
+  return decode_impl(query, q_dtype, q_stride_seq, q_stride_head, kv_cache, num_blocks,
+                     block_size, num_kv_heads, slot_bytes, kv_format, k_scale, v_scale, rot_signs,
+                     block_table, bt_stride, seq_lens, num_seqs, query_len, num_q_heads, head_dim,
+                     max_seq_len, softmax_scale, num_partitions, part_out, part_max, part_sum,
+                     nullptr, stream);
 }
 
 int uq_paged_decode(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_stride_head,
@@ -321,6 +434,69 @@ int uq_paged_reduce(const void* part_out, const float* part_max, const float* pa
                              o_stride_head, stream);
 }
 
+int uq_paged_attention(const void* query, int q_dtype, int64_t q_stride_seq,
+                       int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
+                       int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
+                       int kv_format, const float* k_scale, const float* v_scale,
+                       const int8_t* rot_signs, const int32_t* block_table, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                       int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                       float softmax_scale, int32_t num_partitions, void* workspace,
+                       size_t workspace_bytes, void* out, int64_t o_stride_seq,
+                       int64_t o_stride_head, void* stream) {
+  if (num_seqs < 0) return fail(UQ_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (query_len < 1) return fail(UQ_ERR_INVALID_ARG, "query_len must be >= 1 (got %d)", query_len);
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(UQ_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  if (q_dtype != UQ_F32 && q_dtype != UQ_BF16)
+    return fail(UQ_ERR_INVALID_ARG, "q_dtype must be UQ_F32 or UQ_BF16 (got %d)", q_dtype);
+  if (num_partitions < 1) return fail(UQ_ERR_INVALID_ARG, "num_partitions must be >= 1");
+  if (max_seq_len < 0) return fail(UQ_ERR_INVALID_ARG, "max_seq_len must be >= 0");
+  if (slot_content(kv_format, head_dim) < 0)
+    return fail(UQ_ERR_INVALID_ARG, "unknown kv_format %d or head_dim %d", kv_format, head_dim);
+  if (o_stride_seq <= 0 || o_stride_head <= 0)
+    return fail(UQ_ERR_INVALID_ARG, "output strides must be positive");
+  const int esz = q_dtype == UQ_F32 ? 4 : 2;
+  if (num_seqs > 0 && (!out || !workspace))
+    return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((reinterpret_cast<uintptr_t>(out) & 15) || ((o_stride_seq * esz) | (o_stride_head * esz)) % 16)
+    return fail(UQ_ERR_INVALID_ARG, "out and the output strides must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(UQ_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int QG = num_q_heads / num_kv_heads;
+  const AttnLayout l = attn_layout(kv_format, num_seqs, num_kv_heads, query_len, QG, head_dim,
+                                   num_partitions, max_seq_len);
+  if (workspace_bytes < l.counter_bytes + l.body_bytes)
+    return fail(UQ_ERR_INVALID_ARG, "workspace of %zu bytes is below the %zu this call needs",
+                workspace_bytes, l.counter_bytes + l.body_bytes);
+  if (num_seqs == 0) return ok();
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (l.fused) {
+    FusedTarget ft{out, o_stride_seq, o_stride_head, reinterpret_cast<int32_t*>(ws),
+                   ws + l.counter_bytes, l.tiles};
+    return decode_impl(query, q_dtype, q_stride_seq, q_stride_head, kv_cache, num_blocks,
+                       block_size, num_kv_heads, slot_bytes, kv_format, k_scale, v_scale,
+                       rot_signs, block_table, bt_stride, seq_lens, num_seqs, query_len,
+                       num_q_heads, head_dim, max_seq_len, softmax_scale, num_partitions,
+                       nullptr, nullptr, nullptr, &ft, stream);
+  }
+  // decode into partials carved from the workspace, then the flash-combine launch
+  const size_t rows = (size_t)num_seqs * num_kv_heads * num_partitions * query_len * QG;
+  uint8_t* po = ws + l.counter_bytes;
+  float* pm = reinterpret_cast<float*>(po + up256(rows * head_dim * 2));
+  float* pl = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(pm) + up256(rows * 4));
+  int st = decode_impl(query, q_dtype, q_stride_seq, q_stride_head, kv_cache, num_blocks,
+                       block_size, num_kv_heads, slot_bytes, kv_format, k_scale, v_scale,
+                       rot_signs, block_table, bt_stride, seq_lens, num_seqs, query_len,
+                       num_q_heads, head_dim, max_seq_len, softmax_scale, num_partitions, po, pm,
+                       pl, nullptr, stream);
+  if (st != UQ_OK) return st;
+  return uq_paged_reduce_mtp(po, pm, pl, seq_lens, num_seqs, num_kv_heads, query_len, QG,
+                             head_dim, num_partitions, max_seq_len, out, q_dtype, o_stride_seq,
+                             o_stride_head, stream);
+}
+
 int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head,
                    const uint8_t* k_pages, int64_t page_stride, int64_t num_pages,
                    const int32_t* block_table, int32_t bt_stride, const int32_t* seq_lens,
@@ -347,6 +523,14 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
     return fail(UQ_ERR_INVALID_ARG, "num_pages, bt_stride and max_blocks must be positive");
   if (s_stride_head <= 0 || s_stride_row <= 0)
     return fail(UQ_ERR_INVALID_ARG, "score strides must be positive");
+  // rows of max_blocks cells must not overlap, nor the [rows, max_blocks] planes of heads
+  if (s_stride_row < max_blocks)
+    return fail(UQ_ERR_INVALID_ARG, "s_stride_row %lld is below max_blocks %d",
+                (long long)s_stride_row, max_blocks);
+  if (heads > 1 && num_reqs > 0 &&
+      s_stride_head < ((int64_t)num_reqs * query_len - 1) * s_stride_row + max_blocks)
+    return fail(UQ_ERR_INVALID_ARG, "s_stride_head %lld makes the heads' score planes overlap",
+                (long long)s_stride_head);
   if (num_reqs > 0 && (!q || !k_pages || !block_table || !seq_lens || !scores))
     return fail(UQ_ERR_INVALID_ARG, "a required pointer is NULL");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pages)) & 15)

@@ -35,7 +35,22 @@ struct DecodeArgs {
   uint16_t* part_o;            // bf16 [B, Hk, P, QL*QG, D]
   float* part_m;               // [B, Hk, P, QL*QG]
   float* part_l;
+  // Fused flash-combine (fp8 head groups, uq_paged_attention): every work unit of a
+  // (sequence, kv head) that does not cover the whole sequence leaves its softmax state
+  // in a slot and counts its partitions into counters[b * Hk + h]; the unit that brings
+  // the count to the sequence's partition count merges the states and writes the output
+  // rows (query dtype) itself, then resets the counter to zero.
+  int32_t fused;               // 1: the above; 0: write partials
+  void* out;                   // [B*QL, Hq, D] of the query dtype, element strides o_ss, o_sh
+  int64_t o_ss, o_sh;
+  int32_t* counters;           // [B * Hk], zero between calls
+  uint8_t* states;             // kStateBytes per (slot, kv head, row tile)
+  int32_t state_tiles;         // row tiles per state (1 or 2)
 };
+
+// One fused state: per lane of the wave, 32 fp32 accumulators (8 x f32x4, lane-major)
+// and the (reference, sum) pair of its column.
+constexpr int kStateBytes = 8 * 64 * 16 + 2 * 64 * 4;
 
 struct ReduceArgs {
   const uint16_t* part_o;

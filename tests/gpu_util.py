@@ -18,7 +18,21 @@ except Exception:  # pragma: no cover
     uq = None
 
 DEV = "cuda"
-TOL_DECODE = 1e-2      # max|gpu - ref| <= 1e-2 max|ref|  (fp8 tolerance of the pa_decode_tile PR)
+_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_value(name: str, key: str) -> float:
+    """The number after `key` in tests/golden/<name> (lines starting with # are comments)."""
+    with open(os.path.join(_GOLDEN, name)) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 2 and parts[0] == key:
+                return float(parts[1])
+    raise KeyError(f"{key} not in {name}")
+
+
+# max|gpu - ref| <= TOL_DECODE max|ref|: the fp8 tolerance of the pa_decode_tile PR
+TOL_DECODE = _golden_value("p3_fp8_tolerance.txt", "rel_to_max_abs_out")
 TOL_INDEX = 1e-4       # relative to max|ref| over finite cells
 
 
@@ -67,19 +81,28 @@ def device_case(case):
     )
 
 
-def run_decode(case, P=None, strided=False, dev=None, q=None, partials=None, out=None):
-    """HIP decode + reduce; returns (out float64 numpy, (po, pm, pl) torch tensors)."""
+def run_decode(case, P=None, strided=False, dev=None, q=None, partials=None, out=None,
+               mode=None, workspace=None):
+    """HIP decode step; returns (out float64 numpy, partials or None).  mode "fused":
+    uq_paged_attention (decode and flash-combine in one call, the default); "split":
+    uq_paged_decode then uq_paged_reduce through partials (the default when partials are
+    passed)."""
     dev = dev or device_case(case)
     P = P or case.num_partitions
     q = q if q is not None else q_tensor(case, strided)
     _, Hq, D = q.shape
     hk = case.num_kv_heads
     QL = case.query_len
-    partials = partials or uq.alloc_partials(case.B, hk, QL * (Hq // hk), D, P)
-    out = uq.paged_attention(q, dev["cache"], dev["bt"], dev["sl"], kv_format=case.kv_format,
-                             max_seq_len=case.max_seq_len, num_partitions=P, partials=partials,
-                             out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"],
-                             v_scale=dev["vs"], rot_signs=dev["rot"], query_len=QL)
+    mode = mode or ("split" if partials is not None else "fused")
+    kw = dict(kv_format=case.kv_format, max_seq_len=case.max_seq_len, num_partitions=P,
+              out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"], v_scale=dev["vs"],
+              rot_signs=dev["rot"], query_len=QL)
+    if mode == "split":
+        partials = partials or uq.alloc_partials(case.B, hk, QL * (Hq // hk), D, P)
+        out = uq.paged_decode_reduce(q, dev["cache"], dev["bt"], dev["sl"], partials=partials,
+                                     **kw)
+    else:
+        out = uq.paged_attention(q, dev["cache"], dev["bt"], dev["sl"], workspace=workspace, **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), partials
 

@@ -163,6 +163,8 @@ def index_args(**over):
     (dict(pstride=9200), uq.UQ_ERR_INVALID_ARG), (dict(pstride=9224), uq.UQ_ERR_INVALID_ARG),
     (dict(q_st=100), uq.UQ_ERR_INVALID_ARG), (dict(scores=None), uq.UQ_ERR_INVALID_ARG),
     (dict(npages=0), uq.UQ_ERR_INVALID_ARG),
+    (dict(s_st=255), uq.UQ_ERR_INVALID_ARG),              # score rows overlap
+    (dict(s_sh=63 * 256 + 255), uq.UQ_ERR_INVALID_ARG),   # heads' score planes overlap
 ])
 def test_index_validation(lib, over, status):
     assert lib.uq_index_score(*index_args(**over)) == status
@@ -184,3 +186,70 @@ def test_binding_rejects_cpu_tensors(lib):
                         kv_format=0, max_seq_len=1, num_partitions=1,
                         part_out=torch.zeros(1, 1, 1, 8, 128, dtype=torch.bfloat16),
                         part_max=torch.zeros(1, 1, 1, 8), part_sum=torch.zeros(1, 1, 1, 8))
+
+
+def test_binding_rejects_column_sliced_tables(lib):
+    """A column slice of a wider block table keeps the wide row stride, which is all the C
+    ABI sees; the binding checks the view's own width."""
+    import torch
+    wide = torch.zeros(1, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="columns"):
+        uq.paged_decode(torch.zeros(1, 8, 128, dtype=torch.bfloat16),
+                        torch.zeros(8, 16, 1, 256, dtype=torch.uint8), wide[:, :2],
+                        torch.ones(1, dtype=torch.int32), kv_format=0, max_seq_len=100,
+                        num_partitions=1,
+                        part_out=torch.zeros(1, 1, 1, 8, 128, dtype=torch.bfloat16),
+                        part_max=torch.zeros(1, 1, 1, 8), part_sum=torch.zeros(1, 1, 1, 8))
+    with pytest.raises(ValueError, match="columns"):
+        uq.index_score(torch.zeros(1, 1, 128, dtype=torch.uint8),
+                       torch.zeros(2, 9216, dtype=torch.uint8), wide[:, :2],
+                       torch.ones(1, dtype=torch.int32), torch.zeros(1, 1, 4),
+                       query_len=1)
+
+
+def attention_args(ws_bytes=1 << 30, **over):
+    """uq_paged_attention arguments: decode_mtp_args without the partials, then the
+    workspace and the output."""
+    a = dict(ws=FAKE * 16, ws_bytes=ws_bytes, out=FAKE, o_ss=64 * 128, o_sh=128, stream=None)
+    d = {k: v for k, v in over.items() if k not in a}
+    a.update({k: v for k, v in over.items() if k in a})
+    base = decode_mtp_args(QL=1, **d)[:-4]          # drop part_out, part_max, part_sum, stream
+    return base + list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ws=None), uq.UQ_ERR_INVALID_ARG),
+    (dict(ws=FAKE * 16 + 16), uq.UQ_ERR_INVALID_ARG),   # workspace not 256-byte aligned
+    (dict(ws_bytes=4096), uq.UQ_ERR_INVALID_ARG),       # below what the call needs
+    (dict(out=None), uq.UQ_ERR_INVALID_ARG),
+    (dict(out=FAKE + 8), uq.UQ_ERR_INVALID_ARG),
+    (dict(o_sh=100), uq.UQ_ERR_INVALID_ARG),
+    (dict(o_ss=0), uq.UQ_ERR_INVALID_ARG),
+    (dict(Hq=60), uq.UQ_ERR_INVALID_ARG),
+    (dict(fmt=9), uq.UQ_ERR_INVALID_ARG),
+    (dict(P=0), uq.UQ_ERR_INVALID_ARG),
+    (dict(bs=24), uq.UQ_ERR_INVALID_ARG),               # decode checks still apply
+    (dict(D=64, slot=128), uq.UQ_ERR_UNSUPPORTED),
+])
+def test_attention_validation(lib, over, status):
+    st = lib.uq_paged_attention(*attention_args(**over))
+    assert st == status, lib.uq_last_error()
+    assert lib.uq_last_error().decode()
+
+
+def test_attention_zero_sequences_is_a_no_op(lib):
+    assert lib.uq_paged_attention(*attention_args(B=0, ws=None, out=None)) == uq.UQ_OK
+
+
+def test_attention_workspace_bytes(lib):
+    """Counters [B, Hk] then the fused states (fp8 head groups) or the decode partials.
+    With no GPU the planner assumes 256 compute units: the fp8 high-batch shape takes
+    balanced slices, 128 per head group, so 128 + 127 state slots of one row tile."""
+    up = lambda x: (x + 255) // 256 * 256
+    n = uq.attention_workspace_bytes(128, 8, 1, 8, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
+    assert n == up(128 * 8 * 4) + up(255 * 8 * 1 * (8 * 64 * 16 + 2 * 64 * 4))
+    # fp8 with an odd head count and fp4: decode partials after the counters
+    for fmt, hk, D in ((uq.UQ_KV_FP8_E4M3, 3, 128), (uq.UQ_KV_FP4_E2M1_E4M3S, 2, 256)):
+        n = uq.attention_workspace_bytes(4, hk, 2, 8, D, 512, 75000, fmt)
+        assert n == up(4 * hk * 4) + uq.decode_workspace_bytes(4, hk, 16, D, 512)
+    assert uq.attention_workspace_bytes(4, 2, 0, 8, 256, 512, 75000, 1) == 0

@@ -63,7 +63,7 @@ def test_partition_statistics():
     need_gpu()
     case = small(lens=(300, 1000), qg=6, seed=90)
     P = 3
-    _, (po, pm, pl) = run_decode(case, P=P)
+    _, (po, pm, pl) = run_decode(case, P=P, mode="split")
     _, (rm, rl, ro) = oracle_decode(case, P)
     pm, pl, po = pm.cpu().numpy(), pl.cpu().numpy(), po.float().cpu().numpy()
     live = np.isfinite(rm)

@@ -28,7 +28,7 @@ def test_tiny_config():
     need_gpu()
     case = synth.tiny_fp8()
     log(f"case tiny_fp8 seq_lens={case.seq_lens.tolist()}")
-    got, (po, pm, pl) = run_decode(case)
+    got, (po, pm, pl) = run_decode(case, mode="split")
     ref, (rm, rl, ro) = oracle_decode(case, case.num_partitions)
     assert_decode_close(got, ref, "tiny_fp8 out")
     # partition statistics themselves
@@ -166,31 +166,28 @@ def test_reduce_against_oracle_partials():
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6 * np.abs(want).max())
 
 
-def test_mid_config_full():
-    """B=16, Hk=8, QG=8, L=16384, bf16 Q, 64 partitions, k/v scales 0.05/0.02."""
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_mid_config_full(mode):
+    """B=16, Hk=8, QG=8, L=16384, bf16 Q, 64 partitions, k/v scales 0.05/0.02 (head-group
+    runs: every sequence split into runs of partitions)."""
     need_gpu()
     case = synth.fp8_mid()
-    log("case fp8_mid (full)")
-    got, _ = run_decode(case)
-    assert_decode_close(got, oracle_decode(case), "fp8_mid")
+    log(f"case fp8_mid {mode} (full)")
+    got, _ = run_decode(case, mode=mode)
+    assert_decode_close(got, oracle_decode(case), f"fp8_mid {mode}")
 
 
-def test_high_config_sampled():
-    """B=128 with L ~ U[4096, 16384] at full size on the GPU; the oracle checks a sample
-    of 12 sequences (all their heads), including the shortest and longest."""
+@pytest.mark.parametrize("mode", ["fused", "split"])
+def test_high_config_full(mode):
+    """B=128 with L ~ U[4096, 16384] at full size, in the benchmark's launch configuration
+    (balanced slices: almost every sequence is split at some slice edge); every output row
+    of all 128 sequences and 64 query heads is compared with the oracle.  fused: the one
+    launch of uq_paged_attention; split: decode then reduce through partials."""
     need_gpu()
     case = synth.fp8_high()
-    log(f"case fp8_high (full GPU run, sampled oracle) kv_bytes={case.kv_bytes()}")
-    got, _ = run_decode(case)
-    order = np.argsort(case.seq_lens)
-    pick = sorted(set([int(order[0]), int(order[-1])] +
-                      list(np.random.default_rng(0).choice(case.B, 10, replace=False))))
-    sub = copy.copy(case)
-    sub.q = case.q[pick]
-    sub.block_table = case.block_table[pick]
-    sub.seq_lens = case.seq_lens[pick]
-    ref = oracle_decode(sub)
-    assert_decode_close(got[pick], ref, "fp8_high sample")
+    log(f"case fp8_high {mode} (full GPU run, full oracle) kv_bytes={case.kv_bytes()}")
+    got, _ = run_decode(case, mode=mode)
+    assert_decode_close(got, oracle_decode(case), f"fp8_high {mode}")
 
 
 @pytest.mark.parametrize("B,run", [(32, 2), (128, 3)])
@@ -275,10 +272,10 @@ def test_graph_replay_matches_eager(fmt):
     out.fill_(float("nan"))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        uq.paged_attention(q, dev["cache"], dev["bt"], dev["sl"], kv_format=case.kv_format,
-                           max_seq_len=case.max_seq_len, num_partitions=P, partials=partials,
-                           out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"],
-                           v_scale=dev["vs"], rot_signs=dev["rot"])
+        uq.paged_decode_reduce(q, dev["cache"], dev["bt"], dev["sl"], kv_format=case.kv_format,
+                               max_seq_len=case.max_seq_len, num_partitions=P, partials=partials,
+                               out=out, softmax_scale=case.softmax_scale, k_scale=dev["ks"],
+                               v_scale=dev["vs"], rot_signs=dev["rot"])
     for i in range(4):
         out.fill_(float("nan"))
         partials[0].fill_(0)

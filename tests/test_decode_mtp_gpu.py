@@ -120,23 +120,15 @@ def test_masked_bytes_bit_identical(fmt):
     assert np.array_equal(got, base)
 
 
-def test_fp8_high_mtp_sampled():
+def test_fp8_high_mtp_full():
     """The high-batch fp8 shape (B=128, L ~ U[4096, 16384], Hk=8) with 2 query rows x 4
-    heads per kv head, at full size on the GPU in the benchmark's launch configuration;
-    the oracle checks 12 sequences (all rows and heads), shortest and longest included."""
+    heads per kv head, at full size in the benchmark's launch configuration; every output
+    row (both query rows of all 128 sequences) is compared with the oracle."""
     need_gpu()
     case = synth.fp8_high_mtp(2, 4)
-    log(f"case fp8_high_mtp2_qg4 (full GPU run, sampled oracle) kv_bytes={case.kv_bytes()}")
+    log(f"case fp8_high_mtp2_qg4 (full GPU run, full oracle) kv_bytes={case.kv_bytes()}")
     got, _ = run_decode(case)
-    order = np.argsort(case.seq_lens)
-    pick = sorted(set([int(order[0]), int(order[-1])] +
-                      list(np.random.default_rng(0).choice(case.B, 10, replace=False))))
-    rows = [b * 2 + j for b in pick for j in range(2)]
-    sub = copy.copy(case)
-    sub.q = case.q[rows]
-    sub.block_table = case.block_table[pick]
-    sub.seq_lens = case.seq_lens[pick]
-    assert_decode_close(got[rows], oracle_decode(sub), "fp8_high_mtp sample")
+    assert_decode_close(got, oracle_decode(case), "fp8_high_mtp")
 
 
 @pytest.mark.parametrize("kind", ["e4m3", "ue8m0"])

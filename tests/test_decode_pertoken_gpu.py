@@ -120,22 +120,15 @@ def test_masked_scales_bit_identical():
     assert np.array_equal(got, base)
 
 
-def test_fp8_high_tok_sampled():
+def test_fp8_high_tok_full():
     """The high-batch fp8 shape (B=128, L ~ U[4096, 16384], Hk=8, QG=8, 64 partitions)
-    with per-token scales, at full size in the benchmark's launch configuration; the
-    oracle checks 12 sequences (all heads), shortest and longest included."""
+    with per-token scales, at full size in the benchmark's launch configuration; every
+    output row is compared with the oracle."""
     need_gpu()
     case = synth.fp8_high_tok()
-    log(f"case fp8_high_tok (full GPU run, sampled oracle) kv_bytes={case.kv_bytes()}")
+    log(f"case fp8_high_tok (full GPU run, full oracle) kv_bytes={case.kv_bytes()}")
     got, _ = run_decode(case)
-    order = np.argsort(case.seq_lens)
-    pick = sorted(set([int(order[0]), int(order[-1])] +
-                      list(np.random.default_rng(0).choice(case.B, 10, replace=False))))
-    sub = copy.copy(case)
-    sub.q = case.q[pick]
-    sub.block_table = case.block_table[pick]
-    sub.seq_lens = case.seq_lens[pick]
-    assert_decode_close(got[pick], oracle_decode(sub), "fp8_high_tok sample")
+    assert_decode_close(got, oracle_decode(case), "fp8_high_tok")
 
 
 @pytest.mark.parametrize("P", [1, 64])
