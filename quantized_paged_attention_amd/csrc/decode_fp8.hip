@@ -68,6 +68,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kTiles = 16;     // tiles of 16 tokens per tile-group
 constexpr int kAuxNT = 2;      // KV loads non-temporal (buffer aux bit 1, see below)
+constexpr int kAuxDevice = 16;  // device-scope coherent access (buffer aux bit 4: sc1)
 
 struct KTile {
   i32x4 a, b;  // a: K chunk 2r + (n >> 3) of token n & 7; b: chunk 2r + 1 - (n >> 3) of token
@@ -543,30 +544,45 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       lsum[t] = sum_across_rows(l_run[t]);
     }
     if (fz.take < fz.pm) {
-      // Leave the state in this unit's slot, publish it (release at device scope: every
-      // XCD's L2 sees it before the count does), then count the unit's partitions.  The
-      // unit whose count completes the sequence merges; the others are done.
-      auto state_at = [&](int64_t k) {
-        return a.states + ((k * a.Hk + h) * a.state_tiles) * (int64_t)kStateBytes;
+      // Leave the state in this unit's slot with device-scope stores (written through to
+      // the point where every XCD's L2 sees them), wait for them to complete, then count
+      // the unit's partitions.  The unit whose count completes the sequence merges, reading
+      // the states with device-scope loads; the others are done.  (A release / acquire
+      // fence pair would also write back and invalidate the whole L2 of the XCD at every
+      // unit end: measured on MI355X, B=128 ctx <= 16k, that costs ~110 us per step.)
+      auto state_rsrc = [&](int64_t k) {
+        const uint64_t base = (uint64_t)(a.states + ((k * a.Hk + h) * a.state_tiles) *
+                                                        (int64_t)kStateBytes);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+        return __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, T * kStateBytes,
+            0x00020000);
       };
-      uint8_t* st = state_at(fz.slot);
+      constexpr int kML = 8 * 64 * 16;  // byte offset of (r, l) in a tile's state
+      {
+        const auto rs = state_rsrc(fz.slot);
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        f32x4* sa = reinterpret_cast<f32x4*>(st + t * kStateBytes);
+        for (int t = 0; t < T; ++t) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) sa[m * 64 + lane] = acc[t][m];
-        float* sm = reinterpret_cast<float*>(st + t * kStateBytes + 8 * 64 * 16);
-        sm[lane] = ref[t];
-        sm[64 + lane] = lsum[t];
+          for (int m = 0; m < 8; ++m)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, acc[t][m]), rs,
+                                                   t * kStateBytes + (m * 64 + lane) * 16, 0,
+                                                   kAuxDevice);
+          __builtin_amdgcn_raw_buffer_store_b32(f_bits(ref[t]), rs,
+                                                t * kStateBytes + kML + 4 * lane, 0, kAuxDevice);
+          __builtin_amdgcn_raw_buffer_store_b32(f_bits(lsum[t]), rs,
+                                                t * kStateBytes + kML + 256 + 4 * lane, 0,
+                                                kAuxDevice);
+        }
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state stores have completed
       int32_t* cnt = a.counters + (int64_t)b * a.Hk + h;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       int old = 0;
       if (lane == 0)
         old = __hip_atomic_fetch_add(cnt, fz.take, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       old = __builtin_amdgcn_readfirstlane(old);
       if (old + fz.take != fz.pm) return;  // wave-uniform: another unit finishes the sequence
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       // the next used slot of the range at or after k, other than this unit's own
       auto next_used = [&](int64_t k) {
         for (; k <= fz.hi; ++k) {
@@ -601,15 +617,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (ks[u] <= fz.hi) {
-            const uint8_t* sk = state_at(ks[u]);
+            const auto rs = state_rsrc(ks[u]);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-              const f32x4* sa = reinterpret_cast<const f32x4*>(sk + t * kStateBytes);
 #pragma unroll
-              for (int m = 0; m < 8; ++m) x[u][t][m] = sa[m * 64 + lane];
-              const float* sm = reinterpret_cast<const float*>(sk + t * kStateBytes + 8 * 64 * 16);
-              rk[u][t] = sm[lane];
-              lk[u][t] = sm[64 + lane];
+              for (int m = 0; m < 8; ++m)
+                x[u][t][m] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rs, t * kStateBytes + (m * 64 + lane) * 16, 0, kAuxDevice));
+              rk[u][t] = bits_f(__builtin_amdgcn_raw_buffer_load_b32(
+                  rs, t * kStateBytes + kML + 4 * lane, 0, kAuxDevice));
+              lk[u][t] = bits_f(__builtin_amdgcn_raw_buffer_load_b32(
+                  rs, t * kStateBytes + kML + 256 + 4 * lane, 0, kAuxDevice));
             }
           }
         }
