@@ -7,9 +7,7 @@
 // q[r QL + j, h, :] . k[t, :], with k = e2m1(code) * e4m3(scale of its 16-dim group);
 // -inf when the page holds no such token.
 //
-// Design: one wave per (request, page), four waves per workgroup (measured on MI355X:
-// more pages per wave, with the next page loaded under the current one, lose to the
-// extra waves in flight).  The code keeps the multi-page loop (kPagesPerWave).
+// Design:
 //   * Every e2m1 * e4m3 product and every e4m3 query value is exact in f16, so the page
 //     is dequantised exactly (one v_cvt_scalef32_pk_f16_fp4 with unit scale and one
 //     packed f16 multiply per byte) and the dot products run on v_mfma_f32_16x16x32_f16
@@ -18,9 +16,23 @@
 //     rows (columns = (j, h), at most 32: two column tiles).  The output layout puts
 //     4 tokens of one column in a lane; masked tokens are selected to -inf (never
 //     multiplied, so garbage past the sequence cannot leak), the page max is kept per
-//     lane and reduced across the four lane rows once per page.
-//   * A whole page (8 tiles: 128 code bytes + 1 scale word per lane, non-temporal) is in
-//     registers before its first MFMA; the query operands are converted once per wave.
+//     lane and reduced across the four lane rows once per page.  A page that every row
+//     sees whole skips the causal selects.
+//   * A whole page (8 tiles: 128 code bytes + 1 scale word per lane, non-temporal, one
+//     buffer resource) is in registers before its first MFMA.
+//   * Up to 64 requests: one wave per LIVE page.  The lengths give each request's live
+//     pages; all requests' live pages form one list, and wave g of the launch takes
+//     entries g, g + NW, ... with NW = the waves the chip holds at once.  A wave's chain
+//     is lengths (one load, shared through L2) -> table entry -> page.  Measured on
+//     MI355X (32 requests, L ~ U[1024, 32768], back-to-back launches on cold pages): one
+//     wave per (request, page slot) of the grid, 40 % of them past their sequence and
+//     two rounds of waves: 13.9 / 19.0 us (QL 1 x H 1 / QL 8 x H 4); persistent waves
+//     over contiguous shares of the list, two per SIMD: 16.2 / 19.3 us; one wave per live
+//     page: 11.7 / 15.6 us.  Wave timestamps of the last: every wave starts within 1 us,
+//     the pages arrive between 2.8 and 9.2 us (45 MB at ~7 TB/s), each page then takes
+//     ~1.5 us of dequant and MFMA.
+//   * More requests: one wave per (request, page slot), the table entry read after the
+//     length says the page is live.
 #include "uq_device.h"
 #include "uq_kernels.h"
 
@@ -34,8 +46,8 @@ constexpr int kCodeBytes = 64;    // per token: 128 e2m1 codes
 constexpr int kScaleBytes = 8;    // per token: one e4m3 scale per 16 dims
 constexpr int kScaleRegion = kPageTokens * kCodeBytes;
 constexpr int kWaves = 4;
-constexpr int kPagesPerWave = 1;
-constexpr int kPagesPerGroup = kWaves * kPagesPerWave;
+// waves per SIMD of the scorer kernels by column tiles (registers: at most 96 and 128)
+constexpr int kLiveWavesPerSimd[2] = {5, 4};
 
 template <int sel>
 __device__ __forceinline__ f16x2 fp4_pair(uint32_t word) {
@@ -59,128 +71,215 @@ struct Page {
   uint32_t ksw[8];   // the scale word of groups 2q, 2q + 1 of those tokens
 };
 
+// The page through one buffer resource (wave-uniform base): a lane-constant byte offset
+// plus the tile's offset as the scalar offset, so the 16 loads need no per-tile address
+// registers.  Non-temporal (aux bit 1).
 __device__ __forceinline__ void load_page(const uint8_t* pg, int n, int q, Page& d) {
+  const uint64_t base = (uint64_t)pg;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+      kPageTokens * (kCodeBytes + kScaleBytes), 0x00020000);
+  const uint32_t co = (uint32_t)(n * kCodeBytes + 16 * q);
+  const uint32_t so = (uint32_t)(kScaleRegion + n * kScaleBytes + 4 * (q >> 1));
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
-    const int t = 16 * T + n;
-    d.kc[T] = nt_load(reinterpret_cast<const i32x4*>(pg + t * kCodeBytes + 16 * q));
-    d.ksw[T] = nt_load(reinterpret_cast<const uint32_t*>(pg + kScaleRegion + t * kScaleBytes +
-                                                         4 * (q >> 1)));
+    d.kc[T] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 16 * T * kCodeBytes, 2);
+    d.ksw[T] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 16 * T * kScaleBytes, 2);
   }
 }
 
-__global__ __launch_bounds__(64 * kWaves) void index_score_kernel(IndexArgs a) {
+// Score one page: query operands qb (columns c = j * H + h of request r, causal limits
+// lim0[ct] = last visible token of the column's row), page data d at page index b.
+// full (wave-uniform): every token of the page is visible to every row, so the causal
+// selects drop out of the page max.
+template <int NCT>
+__device__ __forceinline__ void score_page(const IndexArgs& a, const Page& d, const f16x8 (&qb)[2][4],
+                                           const int (&lim0)[2], const int r, const int b,
+                                           const int n, const int q, const int R, const bool full) {
+  float best[2] = {-INFINITY, -INFINITY};
+  const int t_page = b * kPageTokens;
+#pragma unroll
+  for (int T = 0; T < 8; ++T) {
+    const uint32_t sw = d.ksw[T] >> (16 * (q & 1));
+    const _Float16 s0h = (_Float16)e4m3_to_f<0>((int)sw), s1h = (_Float16)e4m3_to_f<1>((int)sw);
+    const f16x2 s0 = f16x2{s0h, s0h}, s1 = f16x2{s1h, s1h};
+    f16x8 A[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t wd = (uint32_t)d.kc[T][kk];
+      const f16x2 sc = kk < 2 ? s0 : s1;
+      A[kk] = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc, fp4_pair<2>(wd) * sc,
+                   fp4_pair<3>(wd) * sc);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[kk], qb[ct][kk], c4, 0, 0, 0);
+      if (!full) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int t = t_page + 16 * T + 4 * q + jj;
+          best[ct] = fmaxf(best[ct], t <= lim0[ct] ? c4[jj] : -INFINITY);
+        }
+      } else {
+        best[ct] = fmaxf(fmaxf(best[ct], fmaxf(c4[0], c4[1])), fmaxf(c4[2], c4[3]));
+      }
+    }
+    // one tile's operands at a time (keeps the register count, and so the waves per SIMD)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float m = max_across_rows(best[ct]);
+    const int col = 16 * ct + n;
+    if (q == 0 && col < R) {
+      const int j = col / a.H, hh = col % a.H;
+      a.scores[(int64_t)hh * a.s_sh + ((int64_t)r * a.QL + j) * a.s_st + b] = m;
+    }
+  }
+}
+
+// Query rows of request r as the B operand (columns c = j * H + h, dims 32 q + 8 kk ..),
+// from the raw e4m3 bytes a lane loaded for its column (two 16-byte words per tile).
+template <int NCT = 2>
+__device__ __forceinline__ void load_q_raw(const IndexArgs& a, int r, int n, int q, int R,
+                                           i32x4 (&raw)[2][2]) {
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    if (ct >= NCT) {
+      raw[ct][0] = raw[ct][1] = i32x4{0, 0, 0, 0};
+      continue;
+    }
+    const int col = 16 * ct + n;
+    raw[ct][0] = raw[ct][1] = i32x4{0, 0, 0, 0};
+    if (col < R) {
+      const int j = col / a.H, hh = col % a.H;
+      const uint8_t* src = a.q + ((int64_t)r * a.QL + j) * a.q_st + (int64_t)hh * a.q_sh + 32 * q;
+      raw[ct][0] = *reinterpret_cast<const i32x4*>(src);
+      raw[ct][1] = *reinterpret_cast<const i32x4*>(src + 16);
+    }
+  }
+}
+
+template <int NCT = 2>
+__device__ __forceinline__ void q_operands(const i32x4 (&raw)[2][2], f16x8 (&qb)[2][4]) {
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    qb[ct][0] = e4m3x8_to_f16(raw[ct][0][0], raw[ct][0][1]);
+    qb[ct][1] = e4m3x8_to_f16(raw[ct][0][2], raw[ct][0][3]);
+    qb[ct][2] = e4m3x8_to_f16(raw[ct][1][0], raw[ct][1][1]);
+    qb[ct][3] = e4m3x8_to_f16(raw[ct][1][2], raw[ct][1][3]);
+  }
+}
+
+// One wave per live page, for up to 64 requests.  Lane l holds request l's length and
+// live-page count (b < min(ceil(L / 128), max_blocks)); the live pages of all requests, in
+// request order, form a list of Tp entries, and wave g of the NW launched takes entries g,
+// g + NW, ...  So no wave exists for a page past a sequence, a wave's chain is length ->
+// table entry -> page (the table entry is read only for a live page), and the waves of
+// one launch all fit on the chip at once.
+template <int NCT>
+__global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index_score_live(IndexArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // workgroup = (request r, chunk of kPagesPerGroup pages); wave w scores pages
-  // chunk_base + w, + kWaves, ... (kPagesPerWave of them)
-  const int per_req = (a.max_blocks + kPagesPerGroup - 1) / kPagesPerGroup;
+  const int64_t NW = (int64_t)gridDim.x * kWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+  const int n = lane & 15, q = lane >> 4;
+  const int R = a.QL * a.H;
+  int Ll = lane < a.num_reqs ? a.seq_lens[lane] : 0;
+  Ll = Ll < 0 ? 0 : Ll;
+  int pl = (Ll + kPageTokens - 1) / kPageTokens;
+  pl = pl < a.max_blocks ? pl : a.max_blocks;
+  int incl = pl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d, 64);
+    incl += lane >= d ? u : 0;
+  }
+  const int Tp = __builtin_amdgcn_readlane(incl, 63);
+  for (int e = (int)gw; e < Tp; e += (int)NW) {  // wave-uniform
+    // the request holding entry e: the first lane whose inclusive count exceeds e
+    const int r = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
+    const int b = e - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(pl, r));
+    const int L = __builtin_amdgcn_readlane(Ll, r);
+    const int pid = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r * a.bt_stride + b]);
+    Page cur;
+    load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
+    i32x4 qraw[2][2];
+    load_q_raw<NCT>(a, r, n, q, R, qraw);
+    f16x8 qb[2][4];
+    q_operands<NCT>(qraw, qb);
+    int lim0[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int col = 16 * ct + n;
+      lim0[ct] = col < R ? L - a.QL + col / a.H : -1;  // last visible token of the row
+    }
+    score_page<NCT>(a, cur, qb, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL);
+  }
+}
+
+// One wave per (request, page slot) of the grid; waves past their sequence exit after the
+// length.
+template <int NCT>
+__global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index_score_slots(IndexArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int per_req = (a.max_blocks + kWaves - 1) / kWaves;
   const int r = blockIdx.x / per_req;
-  const int b0 = (blockIdx.x % per_req) * kPagesPerGroup + wave;
-  // The table entries are read together with the length (entries below max_blocks are
-  // inside the table row; one past the sequence is read but never used).
-  int pid = 0;
-  if (lane < kPagesPerWave && b0 + kWaves * lane < a.max_blocks)
-    pid = a.bt[(int64_t)r * a.bt_stride + b0 + kWaves * lane];
+  const int b = (blockIdx.x % per_req) * kWaves + wave;
   const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[r]);
   int nblk = (L + kPageTokens - 1) / kPageTokens;
   nblk = nblk < a.max_blocks ? nblk : a.max_blocks;
-  if (b0 >= nblk) return;  // cells of pages past the sequence are left untouched
-  const int npg = (nblk - b0 + kWaves - 1) / kWaves < kPagesPerWave
-                      ? (nblk - b0 + kWaves - 1) / kWaves : kPagesPerWave;
-
-  const int n = lane & 15;  // token of a tile (A) / column of a tile (B, output)
-  const int q = lane >> 4;  // dims 32q .. 32q + 31
+  if (b >= nblk) return;  // cells of pages past the sequence are left untouched
+  const int n = lane & 15, q = lane >> 4;
   const int R = a.QL * a.H;
-
-  // page ids of this wave's pages: lane i < npg holds page b0 + kWaves i
-  auto page_ptr = [&](int i) {
-    const int id = __builtin_amdgcn_readlane(pid, i);
-    return a.pages + (int64_t)id * a.page_stride;
-  };
-  Page cur, nxt;
-  load_page(page_ptr(0), n, q, cur);
-
-  // ---- query rows: column c = j * H + h; B operand dims 32 q + 8 kk .. + 8
-  const int ncol_tiles = R > 16 ? 2 : 1;
+  // the table entry of a live page only (read after the length)
+  const int pid = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r * a.bt_stride + b]);
+  Page cur;
+  load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
+  i32x4 qraw[2][2];
+  load_q_raw<NCT>(a, r, n, q, R, qraw);
   f16x8 qb[2][4];
+  q_operands<NCT>(qraw, qb);
   int lim0[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int col = 16 * ct + n;
-    lim0[ct] = -1;
-    if (col < R && ct < ncol_tiles) {
-      const int j = col / a.H, hh = col % a.H;
-      lim0[ct] = L - a.QL + j;  // last visible token of row j
-      const uint8_t* src = a.q + ((int64_t)r * a.QL + j) * a.q_st + (int64_t)hh * a.q_sh + 32 * q;
-      const i32x4 w0 = *reinterpret_cast<const i32x4*>(src);
-      const i32x4 w1 = *reinterpret_cast<const i32x4*>(src + 16);
-      qb[ct][0] = e4m3x8_to_f16(w0[0], w0[1]);
-      qb[ct][1] = e4m3x8_to_f16(w0[2], w0[3]);
-      qb[ct][2] = e4m3x8_to_f16(w1[0], w1[1]);
-      qb[ct][3] = e4m3x8_to_f16(w1[2], w1[3]);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qb[ct][kk] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    lim0[ct] = col < R ? L - a.QL + col / a.H : -1;  // last visible token of the row
   }
-
-  for (int i = 0; i < npg; ++i) {
-    if (i + 1 < npg) load_page(page_ptr(i + 1), n, q, nxt);  // next page under this one
-    const int b = b0 + kWaves * i;
-    float best[2] = {-INFINITY, -INFINITY};
-    const int t_page = b * kPageTokens;
-#pragma unroll
-    for (int T = 0; T < 8; ++T) {
-      const uint32_t sw = cur.ksw[T] >> (16 * (q & 1));
-      const _Float16 s0h = (_Float16)e4m3_to_f<0>((int)sw), s1h = (_Float16)e4m3_to_f<1>((int)sw);
-      const f16x2 s0 = f16x2{s0h, s0h}, s1 = f16x2{s1h, s1h};
-      f16x8 A[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t wd = (uint32_t)cur.kc[T][kk];
-        const f16x2 sc = kk < 2 ? s0 : s1;
-        A[kk] = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc, fp4_pair<2>(wd) * sc,
-                     fp4_pair<3>(wd) * sc);
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        if (ct < ncol_tiles) {
-          f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[kk], qb[ct][kk], c4, 0, 0, 0);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int t = t_page + 16 * T + 4 * q + jj;
-            best[ct] = fmaxf(best[ct], t <= lim0[ct] ? c4[jj] : -INFINITY);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      if (ct < ncol_tiles) {
-        const float m = max_across_rows(best[ct]);
-        const int col = 16 * ct + n;
-        if (q == 0 && col < R) {
-          const int j = col / a.H, hh = col % a.H;
-          a.scores[(int64_t)hh * a.s_sh + ((int64_t)r * a.QL + j) * a.s_st + b] = m;
-        }
-      }
-    }
-    cur = nxt;
-  }
+  score_page<NCT>(a, cur, qb, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL);
 }
 
 }  // namespace
 
 hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
-  const int64_t per_req = (a.max_blocks + kPagesPerGroup - 1) / kPagesPerGroup;
+  if (a.num_reqs <= 0) return hipSuccess;
+  if (a.num_reqs <= 64 && a.cus > 0) {
+    // as many waves as fit on the chip at once, never more than there can be live pages
+    const int nct = a.QL * a.H > 16 ? 2 : 1;
+    int64_t waves = (int64_t)kLiveWavesPerSimd[nct - 1] * 4 * a.cus;
+    const int64_t most = (int64_t)a.num_reqs * a.max_blocks;
+    waves = waves < most ? waves : most;
+    const int64_t wgs = (waves + kWaves - 1) / kWaves;
+    if (nct == 2)
+      hipLaunchKernelGGL((index_score_live<2>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((index_score_live<1>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int64_t per_req = (a.max_blocks + kWaves - 1) / kWaves;
   const int64_t wgs = per_req * a.num_reqs;
   if (wgs <= 0) return hipSuccess;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(index_score_kernel, dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
+  if (a.QL * a.H > 16)
+    hipLaunchKernelGGL((index_score_slots<2>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((index_score_slots<1>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

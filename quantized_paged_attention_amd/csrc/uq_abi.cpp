@@ -552,6 +552,7 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
   a.scores = scores;
   a.s_sh = s_stride_head;
   a.s_st = s_stride_row;
+  a.cus = device_cus();  // sizes the one-wave-per-live-page grid
   return launch_status(uq::launch_index_score(a, static_cast<hipStream_t>(stream)), "index_score");
 }
 

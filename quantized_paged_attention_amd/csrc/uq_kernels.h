@@ -75,6 +75,8 @@ struct IndexArgs {
   int32_t num_reqs, QL, H, max_blocks;
   float* scores;
   int64_t s_sh, s_st;
+  int32_t cus;                 // compute units of the device (> 0, up to 64 requests: one
+                               // wave per live page)
 };
 
 // Each returns the hipError_t of its launch.

@@ -159,3 +159,36 @@ def test_shared_pages_across_windows_and_partial():
     log("case nvfp4_index irregular sharing, 70 requests")
     got = run_gpu(case)
     assert_index_match(got, run_oracle(case), case.scores_init(), "irregular sharing")
+
+
+@pytest.mark.parametrize("R", [60, 300])
+def test_many_requests_with_empty_ones(R):
+    """Lengths from 0 to 3000.  60 requests: one wave per live page of the list built from
+    the lengths, request boundaries anywhere; 300 requests (past the 64 lengths a wave
+    holds): one wave per (request, page slot), the table read only for live pages."""
+    need_gpu()
+    rng = np.random.default_rng(130 + R)
+    lens = rng.integers(1, 3001, size=R)
+    lens[::23] = 0
+    lens[1] = 1
+    case = synth.make_index_case("idx_many", 131 + R, seq_lens=[int(x) for x in lens],
+                                 query_len=1, heads=2, max_pages=24)
+    got = run_gpu(case)
+    assert_index_match(got, run_oracle(case), case.scores_init(), f"{R} requests")
+
+
+@pytest.mark.parametrize("R,ql,h", [(64, 1, 1), (64, 8, 4), (512, 1, 1)])
+def test_long_page_lists(R, ql, h):
+    """Requests of ~38k tokens whose tables all point at the same 300 pages.  64 requests:
+    19k live pages, more than the waves of one launch, so each wave loops over several
+    entries of the list; 512 requests: 150k page slots, one wave each."""
+    need_gpu()
+    base = synth.make_index_case("idx_long", 140, seq_lens=[300 * 128], query_len=1, heads=1,
+                                 spare_pages=2)
+    lens = np.array([300 * 128 - (r % 200) for r in range(R)], np.int32)
+    rng = np.random.default_rng(141 + R + ql)
+    q = synth.e4m3_encode(rng.standard_normal((R * ql, h, 128), dtype=np.float32))
+    case = synth.IndexCase("idx_long", q, base.pages, np.repeat(base.block_table, R, axis=0),
+                           lens, ql, h, 300)
+    got = run_gpu(case)
+    assert_index_match(got, run_oracle(case), case.scores_init(), f"long lists R={R} ql={ql}")
