@@ -144,33 +144,73 @@ __device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, i
   return c;
 }
 
-template <typename QT, bool UE>
+// HPW: kv heads per workgroup (2 when Hk is even).  The four waves split as WPH = 4 / HPW
+// waves per head; wave (hw, part) streams head h0 + hw over tokens [TPW part, TPW part +
+// TPW) of each of the unit's tile-groups (TPW = 256 / WPH).  With HPW = 2 the workgroup
+// reads both heads' 272-byte slots of every token it touches, i.e. whole 544-byte token
+// rows and whole physical blocks (Hk = 2), instead of one head's half of each row.
+template <typename QT, bool UE, int HPW>
 __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
-  // Rotated query (f16, row stride kD + 8 halves) during the stream; the four waves'
-  // scaled accumulators in the merge (reused after a barrier).
-  __shared__ __attribute__((aligned(16))) float lds_acc[kW][16][kD];
-  __shared__ float lds_fac[16];
-  __shared__ float lds_m[kW][16];
-  __shared__ float lds_l[kW][16];
-  _Float16* lds_q = reinterpret_cast<_Float16*>(&lds_acc[0][0][0]);
+  constexpr int WPH = kW / HPW;     // waves per head
+  constexpr int TPW = 256 / WPH;    // tokens of a tile-group per wave
+  constexpr int SPT = TPW / 32;     // 32-token steps per tile-group per wave
+  constexpr int RPW = 16 / WPH;     // query rows a wave rotates
   constexpr int kQStride = kD + 8;        // f16 query row (halves)
   constexpr int kQBStride = 2 * kD + 16;  // e4m3 hi row then lo row (bytes)
+  constexpr int kQBytes = HPW * 16 * (UE ? kQBStride : 2 * kQStride);
+  // the merge: waves part > 0 leave their scaled accumulators, lane-major (16 KB each)
+  constexpr int kMergeBytes = HPW * (WPH - 1) * 16 * 64 * 16;
+  constexpr int kLdsBytes = kQBytes > kMergeBytes ? kQBytes : kMergeBytes;
+  // Rotated query during the stream; the merge states after a barrier (same bytes).
+  __shared__ __attribute__((aligned(16))) uint8_t lds_buf[kLdsBytes];
+  __shared__ float lds_fac[HPW][16];
+  __shared__ float lds_m[kW][16];
+  __shared__ float lds_l[kW][16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // workgroup = (kv head h, sequence b, group grp), kv head fastest.  The kv heads of one
-  // (sequence, group) share cache lines (a 272-byte slot is not line aligned), so they are
-  // placed on one XCD -- workgroups are dealt to the 8 XCDs round robin, so the heads go
-  // 8 apart in launch order -- and read the shared lines through one L2 (measured on
-  // MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 % faster).  The grid is padded to
-  // a multiple of 8 Hk, which makes the map a bijection; the padding workgroups exit here.
+  const int hw = wave / WPH, part = wave % WPH;
+  // workgroup = (head group, sequence b, group grp), head group fastest.  With one head
+  // per workgroup the kv heads of one (sequence, group) share cache lines (a 272-byte slot
+  // is not line aligned), so they are placed on one XCD -- workgroups are dealt to the 8
+  // XCDs round robin, so the heads go 8 apart in launch order -- and read the shared lines
+  // through one L2 (measured on MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 %
+  // faster).  The grid is padded to a multiple of 8 NHG, which makes the map a bijection;
+  // the padding workgroups exit here.
+  const int NHG = a.Hk / HPW;
   const int64_t unit0 = blockIdx.x;
   const int64_t xc = unit0 % 8, j = unit0 / 8;
-  const int64_t unit = ((j / a.Hk) * 8 + xc) * a.Hk + j % a.Hk;
-  if (unit >= (int64_t)a.B * a.Hk * a.runs) return;  // workgroup-uniform, before any barrier
-  const int h = (int)(unit % a.Hk);
-  const int b = (int)((unit / a.Hk) % a.B);
-  const int grp = (int)(unit / ((int64_t)a.Hk * a.B));
+  const int64_t unit = ((j / NHG) * 8 + xc) * NHG + j % NHG;
+  if (unit >= (int64_t)a.B * NHG * a.runs) return;  // workgroup-uniform, before any barrier
+  const int h = (int)(unit % NHG) * HPW + hw;
+  const int b = (int)((unit / NHG) % a.B);
+  const int grp = (int)(unit / ((int64_t)NHG * a.B));
+  _Float16* lds_q = reinterpret_cast<_Float16*>(lds_buf) + hw * 16 * kQStride;
+  uint8_t* lds_qb = lds_buf + hw * 16 * kQBStride;
+
+  // The query rows this wave rotates (rows [RPW part, RPW part + RPW) of head h, four at a
+  // time, lane: row + lane / 16, dims 16 c .. 16 c + 15) and the rotation signs are loaded
+  // first: they do not depend on the length, so they arrive with it, and the rotation,
+  // which waits only for them (vector loads return in order), runs under the first KV
+  // step's loads.
+  const int NR = a.QL * a.QG;
+  constexpr int kQW = sizeof(QT) == 4 ? 4 : 2;  // 16-byte words of a lane's 16 dims
+  i32x4 q_raw[RPW / 4][kQW];
+  i32x4 sg_raw = i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int rp = 0; rp < RPW; rp += 4) {
+    const int row = RPW * part + rp + (lane >> 4);
+#pragma unroll
+    for (int k = 0; k < kQW; ++k) q_raw[rp / 4][k] = i32x4{0, 0, 0, 0};
+    if (row < NR) {
+      const QT* src = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.QL + row / a.QG) * a.q_ss +
+                      (int64_t)(h * a.QG + row % a.QG) * a.q_sh + 16 * (lane & 15);
+#pragma unroll
+      for (int k = 0; k < kQW; ++k)
+        q_raw[rp / 4][k] = *reinterpret_cast<const i32x4*>(src + k * (16 / (int)sizeof(QT)));
+    }
+  }
+  if (a.rot_signs) sg_raw = *reinterpret_cast<const i32x4*>(a.rot_signs + 16 * (lane & 15));
 
   int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
   L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
@@ -204,23 +244,21 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   const int q = lane >> 4;   // lane row group
   // unit rows r = j * QG + g: query row j (of QL per sequence), head g; query row j sees
   // the tokens t < L - QL + 1 + j (the causal window of its row)
-  const int NR = a.QL * a.QG;
   const int L_row = L - a.QL + 1 + (n < NR ? n / a.QG : 0);
 
-  // ---- the stream.  Wave w takes tokens [64w, 64w + 64) of each of the workgroup's
-  //      tile-groups.  The first step's loads go out before the query rotation, so the
-  //      rotation runs under their latency.
-  const int blk_per_wave = 64 / a.block_size > 0 ? 64 / a.block_size : 1;
+  // ---- the stream.  Wave (hw, part) takes tokens [TPW part, TPW part + TPW) of each of
+  //      the workgroup's tile-groups.  The first step's loads go out before the query
+  //      rotation, so the rotation runs under their latency.
   const int bs_shift = 31 - __builtin_clz(a.block_size);
   // The wave's stream: 32-token steps c = 0, 1, ... ; step c covers tokens
-  // [s_k + 32 (c & 1), + 32) of tile-group k = c >> 1, s_k = 256 tg_k + 64 wave.  Steps
+  // [s_k + 32 (c % SPT), + 32) of tile-group k = c / SPT, s_k = 256 tg_k + TPW part.  Steps
   // holding tokens form a prefix.  Block ids of a window of tile-groups are preloaded
-  // (lane i: tile-group kw + i / bpw, block i % bpw of its 64 tokens, clamped to the last
+  // (lane i: tile-group kw + i / bpw, block i % bpw of its TPW tokens, clamped to the last
   // visible block so that no table entry past the sequence is read).
-  const int bpw = blk_per_wave;
+  const int bpw = TPW / a.block_size > 0 ? TPW / a.block_size : 1;
   const int win_tgs = 64 / bpw;
   int ids = 0, kw = -win_tgs;
-  auto s_of = [&](int k) { return (part_first + k * tg_step) * kTileGroup + 64 * wave; };
+  auto s_of = [&](int k) { return (part_first + k * tg_step) * kTileGroup + TPW * part; };
   auto load_ids = [&](int k0) {
     kw = k0;
     const int k = k0 + lane / bpw;
@@ -236,51 +274,46 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
     }
     ids = v;
   };
-  auto step_t0 = [&](int c) { return s_of(c >> 1) + 32 * (c & 1); };
-  auto step_ok = [&](int c) { return c < 2 * n_tg && step_t0(c) < L; };
+  auto step_t0 = [&](int c) { return s_of(c / SPT) + 32 * (c % SPT); };
+  auto step_ok = [&](int c) { return c < SPT * n_tg && step_t0(c) < L; };
   auto load_step = [&](int c, Chunk& dst) {
-    const int k = c >> 1;
+    const int k = c / SPT;
     if (k >= kw + win_tgs) load_ids(k);
     const int sk = s_of(k);
     dst = load_chunk<UE>(a, n, q, ids, (sk >> bs_shift) - (k - kw) * bpw, step_t0(c), L, h,
                          bs_shift);
   };
+  // the first step's KV loads as soon as its block ids are in; the rotation below runs
+  // under their latency (its query words were loaded before them)
   Chunk cA, cB;
   if (step_ok(0)) load_step(0, cA);
 
 
-  // ---- rotated query: wave w, lane (row 4w + lane/16, dims 16 c .. 16 c + 15)
-  {
-    const int row = 4 * wave + (lane >> 4);
+  // ---- rotated query of head h: wave (hw, part) takes rows [RPW part, RPW part + RPW),
+  //      four at a time, lane (row + lane/16, dims 16 c .. 16 c + 15)
+#pragma unroll
+  for (int rp = 0; rp < RPW; rp += 4) {
+    const int row = RPW * part + rp + (lane >> 4);
     const int c = lane & 15;
     float x[16];
-    if (row < NR) {
-      const QT* src = reinterpret_cast<const QT*>(a.q) + ((int64_t)b * a.QL + row / a.QG) * a.q_ss +
-                      (int64_t)(h * a.QG + row % a.QG) * a.q_sh + 16 * c;
-      if constexpr (sizeof(QT) == 4) {
+    if constexpr (sizeof(QT) == 4) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4 * k);
+      for (int k = 0; k < 4; ++k)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * k + e] = v[e];
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const i32x4 v = *reinterpret_cast<const i32x4*>(src + 8 * k);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[8 * k + 2 * e] = bf16_to_f((uint32_t)v[e] & 0xFFFFu);
-            x[8 * k + 2 * e + 1] = bf16_to_f((uint32_t)v[e] >> 16);
-          }
-        }
-      }
+        for (int e = 0; e < 4; ++e) x[4 * k + e] = bits_f((uint32_t)q_raw[rp / 4][k][e]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = 0.f;
+      for (int k = 0; k < 2; ++k) {
+        const i32x4 v = q_raw[rp / 4][k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * k + 2 * e] = bf16_to_f((uint32_t)v[e] & 0xFFFFu);
+          x[8 * k + 2 * e + 1] = bf16_to_f((uint32_t)v[e] >> 16);
+        }
+      }
     }
     if (a.rot_signs) {
-      const i32x4 sg = *reinterpret_cast<const i32x4*>(a.rot_signs + 16 * c);
+      const i32x4 sg = sg_raw;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int s8 = (int)(int8_t)((uint32_t)sg[e >> 2] >> (8 * (e & 3)));
@@ -334,7 +367,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
       uint8_t* dst = reinterpret_cast<uint8_t*>(lds_q + row * kQStride + 16 * c);
       *reinterpret_cast<i32x4*>(dst) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       *reinterpret_cast<i32x4*>(dst + 16) = i32x4{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-      if (c == 0) lds_fac[row] = a.softmax_scale * kLog2e * __builtin_ldexpf(1.f, -sh);
+      if (c == 0) lds_fac[hw][row] = a.softmax_scale * kLog2e * __builtin_ldexpf(1.f, -sh);
     } else {
       // e4m3 hi + lo pair of q' s_q, s_q = 2^(7 - E) putting amax in [64, 128): the pair
       // carries about 8 significant bits (the scaled MFMA takes fp8 for the query)
@@ -344,7 +377,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         E = E < -100 ? -100 : (E > 100 ? 100 : E);
       }
       const float s_q = __builtin_ldexpf(1.f, 7 - E);
-      int hw[4], lw[4];
+      int hiw[4], low[4];
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
         const float y0 = x[4 * w4] * s_q, y1 = x[4 * w4 + 1] * s_q;
@@ -353,13 +386,13 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
         hv = cvt_pk_e4m3<true>(y2, y3, hv);
         int lv = cvt_pk_e4m3<false>(y0 - e4m3_to_f<0>(hv), y1 - e4m3_to_f<1>(hv), 0);
         lv = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hv), y3 - e4m3_to_f<3>(hv), lv);
-        hw[w4] = hv;
-        lw[w4] = lv;
+        hiw[w4] = hv;
+        low[w4] = lv;
       }
-      uint8_t* dst = reinterpret_cast<uint8_t*>(lds_q) + row * kQBStride + 16 * c;
-      *reinterpret_cast<i32x4*>(dst) = i32x4{hw[0], hw[1], hw[2], hw[3]};
-      *reinterpret_cast<i32x4*>(dst + kD) = i32x4{lw[0], lw[1], lw[2], lw[3]};
-      if (c == 0) lds_fac[row] = a.softmax_scale * kLog2e / s_q;
+      uint8_t* dst = lds_qb + row * kQBStride + 16 * c;
+      *reinterpret_cast<i32x4*>(dst) = i32x4{hiw[0], hiw[1], hiw[2], hiw[3]};
+      *reinterpret_cast<i32x4*>(dst + kD) = i32x4{low[0], low[1], low[2], low[3]};
+      if (c == 0) lds_fac[hw][row] = a.softmax_scale * kLog2e / s_q;
     }
   }
   __syncthreads();
@@ -367,8 +400,8 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   // B operand of QK is read from LDS at each use: f16 head n, dims 64 q + 8 kk .. + 8
   // (e4m3 scales), or e4m3 hi/lo bytes of head n from dim 16 q on (UE8M0 scales)
   const _Float16* qrow = lds_q + n * kQStride + 64 * q;
-  const uint8_t* qbrow = reinterpret_cast<const uint8_t*>(lds_q) + n * kQBStride + 16 * q;
-  const float fac = lds_fac[n];
+  const uint8_t* qbrow = lds_qb + n * kQBStride + 16 * q;
+  const float fac = lds_fac[hw][n];
 
   float m_run = -INFINITY;  // reference of head n (exp2 units); acc/l are relative to it
   float l_run = 0.f;        // this lane's share of sum p for head n
@@ -572,72 +605,76 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
     }
   }
 
-  // ---- merge the four waves: (m, l) per head, then the scaled accumulators
+  // ---- merge the WPH waves of each head: (m, l) per row, then the scaled accumulators.
+  //      Waves part > 0 leave acc * factor in LDS, lane-major (conflict-free 16-byte
+  //      accesses, the same lane layout on both sides); wave part 0 adds them to its own
+  //      and writes the rows.
   const float l_tot = sum_across_rows(l_run);
-  __syncthreads();  // every wave is done with the rotated query in lds_acc
+  __syncthreads();  // every wave is done with the rotated query (the same LDS bytes)
   if (q == 0) {
     lds_m[wave][n] = m_run;
     lds_l[wave][n] = l_tot;
   }
   __syncthreads();
-  {
-    float fself[4];
+  f32x4 fs;  // this wave's factor for rows 4q .. 4q + 3
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int hd = 4 * q + jj;
-      float M = -INFINITY;
+  for (int jj = 0; jj < 4; ++jj) {
+    const int hd = 4 * q + jj;
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kW; ++w) M = fmaxf(M, lds_m[w][hd]);
-      float lsum = 0.f;
+    for (int w = 0; w < WPH; ++w) M = fmaxf(M, lds_m[hw * WPH + w][hd]);
+    float lsum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kW; ++w) {
-        const float mw = lds_m[w][hd];
-        lsum += mw == -INFINITY ? 0.f : lds_l[w][hd] * fast_exp2(mw - M);
-      }
-      const float ms = lds_m[wave][hd];
-      fself[jj] = (ms == -INFINITY || !(lsum > 0.f)) ? 0.f : fast_exp2(ms - M) / lsum;
-      if (wave == 0 && n == 0 && hd < NR) {
-        const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * NR + hd;
-        a.part_m[row] = M * kLn2;
-        a.part_l[row] = lsum;
-        // the run's other partitions: empty states
-        for (int pe = part_first + 1; pe < p_end; ++pe) {
-          a.part_m[row + (int64_t)(pe - p) * NR] = -INFINITY;
-          a.part_l[row + (int64_t)(pe - p) * NR] = 0.f;
-        }
-      }
+    for (int w = 0; w < WPH; ++w) {
+      const float mw = lds_m[hw * WPH + w][hd];
+      lsum += mw == -INFINITY ? 0.f : lds_l[hw * WPH + w][hd] * fast_exp2(mw - M);
     }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      float* dst = &lds_acc[wave][4 * q + jj][16 * n];
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-        *reinterpret_cast<f32x4*>(dst + 4 * k4) =
-            f32x4{acc[4 * k4][jj], acc[4 * k4 + 1][jj], acc[4 * k4 + 2][jj], acc[4 * k4 + 3][jj]} *
-            fself[jj];
+    const float ms = lds_m[wave][hd];
+    fs[jj] = (ms == -INFINITY || !(lsum > 0.f)) ? 0.f : fast_exp2(ms - M) / lsum;
+    if (part == 0 && n == 0 && hd < NR) {
+      const int64_t row = (((int64_t)b * a.Hk + h) * a.P + p) * NR + hd;
+      a.part_m[row] = M * kLn2;
+      a.part_l[row] = lsum;
+      // the run's other partitions: empty states
+      for (int pe = part_first + 1; pe < p_end; ++pe) {
+        a.part_m[row + (int64_t)(pe - p) * NR] = -INFINITY;
+        a.part_l[row + (int64_t)(pe - p) * NR] = 0.f;
+      }
     }
   }
-  __syncthreads();
-  {
-    const int row = 4 * wave + (lane >> 4);
-    const int c = lane & 15;
-    if (row < NR) {
-      f32x4 o[4];
+  f32x4* st = reinterpret_cast<f32x4*>(lds_buf);
+  if constexpr (WPH > 1) {
+    if (part > 0) {
+      f32x4* mine = st + (hw * (WPH - 1) + part - 1) * 16 * 64;
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        o[k4] = *reinterpret_cast<const f32x4*>(&lds_acc[0][row][16 * c + 4 * k4]);
+      for (int mm = 0; mm < 16; ++mm) mine[mm * 64 + lane] = acc[mm] * fs;
+    }
+    __syncthreads();
+  }
+  if (part == 0) {
+    // acc[mm][jj] = O[row 4q + jj][dim 16n + mm]
 #pragma unroll
-        for (int w = 1; w < kW; ++w)
-          o[k4] += *reinterpret_cast<const f32x4*>(&lds_acc[w][row][16 * c + 4 * k4]);
+    for (int mm = 0; mm < 16; ++mm) {
+      f32x4 o = acc[mm] * fs;
+#pragma unroll
+      for (int w = 1; w < WPH; ++w) o += st[((hw * (WPH - 1) + w - 1) * 16 + mm) * 64 + lane];
+      acc[mm] = o;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = 4 * q + jj;
+      if (row < NR) {
+        const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + p) * NR + row;
+        uint16_t* dst = a.part_o + prow * kD + 16 * n;
+        i32x4 w0, w1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0[e] = (int)pack_bf16x2(acc[2 * e][jj], acc[2 * e + 1][jj]);
+          w1[e] = (int)pack_bf16x2(acc[8 + 2 * e][jj], acc[8 + 2 * e + 1][jj]);
+        }
+        *reinterpret_cast<i32x4*>(dst) = w0;
+        *reinterpret_cast<i32x4*>(dst + 8) = w1;
       }
-      const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + p) * NR + row;
-      uint16_t* dst = a.part_o + prow * kD + 16 * c;
-      *reinterpret_cast<i32x4*>(dst) =
-          i32x4{(int)pack_bf16x2(o[0][0], o[0][1]), (int)pack_bf16x2(o[0][2], o[0][3]),
-                (int)pack_bf16x2(o[1][0], o[1][1]), (int)pack_bf16x2(o[1][2], o[1][3])};
-      *reinterpret_cast<i32x4*>(dst + 8) =
-          i32x4{(int)pack_bf16x2(o[2][0], o[2][1]), (int)pack_bf16x2(o[2][2], o[2][3]),
-                (int)pack_bf16x2(o[3][0], o[3][1]), (int)pack_bf16x2(o[3][2], o[3][3])};
     }
   }
 }
@@ -645,23 +682,29 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, bool ue8m0, hipStream_t stream) {
-  const int64_t units = (int64_t)a.B * a.Hk * a.runs;  // runs: workgroups per (b, h)
+  // two kv heads per workgroup when they pair up (whole token rows per workgroup)
+  const int hpw = a.Hk % 2 == 0 ? 2 : 1;
+  const int64_t nhg = a.Hk / hpw;
+  const int64_t units = (int64_t)a.B * nhg * a.runs;  // runs: workgroups per (b, head group)
   if (units <= 0) return hipSuccess;
-  // padded to a multiple of 8 Hk for the XCD placement of the kv heads (see the kernel)
-  const int64_t pad = 8 * (int64_t)a.Hk;
+  // padded to a multiple of 8 NHG for the XCD placement of the head groups (see the kernel)
+  const int64_t pad = 8 * nhg;
   const int64_t wgs = (units + pad - 1) / pad * pad;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs), block(64 * kW);
-  if (ue8m0) {
-    if (q_is_f32)
-      hipLaunchKernelGGL((decode_fp4_kernel<float, true>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_fp4_kernel<uint16_t, true>), grid, block, 0, stream, a);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
+  if (hpw == 2) {
+    if (ue8m0) {
+      if (q_is_f32) go(decode_fp4_kernel<float, true, 2>); else go(decode_fp4_kernel<uint16_t, true, 2>);
+    } else {
+      if (q_is_f32) go(decode_fp4_kernel<float, false, 2>); else go(decode_fp4_kernel<uint16_t, false, 2>);
+    }
   } else {
-    if (q_is_f32)
-      hipLaunchKernelGGL((decode_fp4_kernel<float, false>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_fp4_kernel<uint16_t, false>), grid, block, 0, stream, a);
+    if (ue8m0) {
+      if (q_is_f32) go(decode_fp4_kernel<float, true, 1>); else go(decode_fp4_kernel<uint16_t, true, 1>);
+    } else {
+      if (q_is_f32) go(decode_fp4_kernel<float, false, 1>); else go(decode_fp4_kernel<uint16_t, false, 1>);
+    }
   }
   return hipGetLastError();
 }
