@@ -144,14 +144,21 @@ __device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, i
   return c;
 }
 
-// HPW: kv heads per workgroup (2 when Hk is even).  The four waves split as WPH = 4 / HPW
-// waves per head; wave (hw, part) streams head h0 + hw over tokens [TPW part, TPW part +
-// TPW) of each of the unit's tile-groups (TPW = 256 / WPH).  With HPW = 2 the workgroup
-// reads both heads' 272-byte slots of every token it touches, i.e. whole 544-byte token
-// rows and whole physical blocks (Hk = 2), instead of one head's half of each row.
-template <typename QT, bool UE, int HPW>
-__global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
-  constexpr int WPH = kW / HPW;     // waves per head
+// One unit of the FP4 decode for a whole workgroup (every wave calls it with the same
+// arguments): the tile-groups part_first + k tg_step (k < n_tg) of sequence b (length L)
+// for kv head h0, merged into partition part_first; the unit's other partitions in
+// [part_first, p_end) are written as empty.  Wave w (part) streams tokens [64 w, 64 w + 64)
+// of each tile-group.  (The code keeps a head index hw: covering both heads of a token row
+// with one workgroup, whole 544-byte rows, measured slower on MI355X: 52.4 vs 50.6 us at
+// QG 16, as did balanced slices of 8 waves per CU, 52.4 us.)
+template <typename QT, bool UE>
+__device__ __forceinline__ void fp4_unit(const DecodeArgs& a, const int lane, const int wave,
+                                         const int b, const int h0, const int L,
+                                         const int part_first, const int p_end,
+                                         const int n_tg, const int tg_step) {
+  constexpr int HPW = 1;            // kv heads per workgroup
+  constexpr int W = kW;             // waves per workgroup
+  constexpr int WPH = W / HPW;      // waves per head
   constexpr int TPW = 256 / WPH;    // tokens of a tile-group per wave
   constexpr int SPT = TPW / 32;     // 32-token steps per tile-group per wave
   constexpr int RPW = 16 / WPH;     // query rows a wave rotates
@@ -164,35 +171,19 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   // Rotated query during the stream; the merge states after a barrier (same bytes).
   __shared__ __attribute__((aligned(16))) uint8_t lds_buf[kLdsBytes];
   __shared__ float lds_fac[HPW][16];
-  __shared__ float lds_m[kW][16];
-  __shared__ float lds_l[kW][16];
+  __shared__ float lds_m[W][16];
+  __shared__ float lds_l[W][16];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int hw = wave / WPH, part = wave % WPH;
-  // workgroup = (head group, sequence b, group grp), head group fastest.  With one head
-  // per workgroup the kv heads of one (sequence, group) share cache lines (a 272-byte slot
-  // is not line aligned), so they are placed on one XCD -- workgroups are dealt to the 8
-  // XCDs round robin, so the heads go 8 apart in launch order -- and read the shared lines
-  // through one L2 (measured on MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 %
-  // faster).  The grid is padded to a multiple of 8 NHG, which makes the map a bijection;
-  // the padding workgroups exit here.
-  const int NHG = a.Hk / HPW;
-  const int64_t unit0 = blockIdx.x;
-  const int64_t xc = unit0 % 8, j = unit0 / 8;
-  const int64_t unit = ((j / NHG) * 8 + xc) * NHG + j % NHG;
-  if (unit >= (int64_t)a.B * NHG * a.runs) return;  // workgroup-uniform, before any barrier
-  const int h = (int)(unit % NHG) * HPW + hw;
-  const int b = (int)((unit / NHG) % a.B);
-  const int grp = (int)(unit / ((int64_t)NHG * a.B));
+  const int h = h0 + hw;
+  const int p = part_first;
   _Float16* lds_q = reinterpret_cast<_Float16*>(lds_buf) + hw * 16 * kQStride;
   uint8_t* lds_qb = lds_buf + hw * 16 * kQBStride;
 
   // The query rows this wave rotates (rows [RPW part, RPW part + RPW) of head h, four at a
   // time, lane: row + lane / 16, dims 16 c .. 16 c + 15) and the rotation signs are loaded
-  // first: they do not depend on the length, so they arrive with it, and the rotation,
-  // which waits only for them (vector loads return in order), runs under the first KV
-  // step's loads.
+  // before the block-table window: the rotation, which waits only for them (vector loads
+  // return in order), runs under the first KV step's loads.
   const int NR = a.QL * a.QG;
   constexpr int kQW = sizeof(QT) == 4 ? 4 : 2;  // 16-byte words of a lane's 16 dims
   i32x4 q_raw[RPW / 4][kQW];
@@ -212,33 +203,6 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
   }
   if (a.rot_signs) sg_raw = *reinterpret_cast<const i32x4*>(a.rot_signs + 16 * (lane & 15));
 
-  int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
-  L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
-  const int ntg = (L + kTileGroup - 1) / kTileGroup;
-  // Partitions with tokens: p < pmax.  With one tile-group per partition the workgroup
-  // owns the run of partitions [part_first, part_first + R) (R = run_len) and merges
-  // them into partition part_first (the others are written as empty); otherwise it owns
-  // partition part_first and its strided tile-groups p, p + P, ...
-  const int pmax = a.P < ntg ? a.P : ntg;
-  const int R = a.run_len > 0 ? a.run_len : 1;
-  int part_first, p_end, n_tg, tg_step;
-  if (a.run_len > 0) {
-    // this sequence's pmax partitions in G nearly equal runs of at most R
-    const int G = (pmax + R - 1) / R;
-    if (grp >= G) return;  // workgroup-uniform: nothing written, never read
-    part_first = (int)((int64_t)grp * pmax / G);
-    p_end = (int)((int64_t)(grp + 1) * pmax / G);
-    n_tg = p_end - part_first;
-    tg_step = 1;
-  } else {
-    part_first = grp;
-    if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
-    p_end = part_first + 1;
-    n_tg = (ntg - part_first + a.P - 1) / a.P;
-    n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
-    tg_step = a.P;
-  }
-  const int p = part_first;
 
   const int n = lane & 15;   // unit row of the QK / softmax layout; PV column group
   const int q = lane >> 4;   // lane row group
@@ -677,34 +641,77 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
       }
     }
   }
+
+}
+
+template <typename QT, bool UE>
+__global__ __launch_bounds__(64 * kW, 2) void decode_fp4_kernel(DecodeArgs a) {
+  constexpr int HPW = 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  {
+    // workgroup = (kv head, sequence b, group grp), kv head fastest.  The kv heads of one
+    // (sequence, group) share cache lines (a 272-byte slot is not line aligned), so they
+    // are placed on one XCD -- workgroups are dealt to the 8 XCDs round robin, so the heads
+    // go 8 apart in launch order -- and read the shared lines through one L2 (measured on
+    // MI355X: HBM reads 1.42x -> 1.01x the slot bytes, 8 % faster).  The grid is padded to
+    // a multiple of 8 Hk, which makes the map a bijection; the padding workgroups exit
+    // here.
+    const int NHG = a.Hk / HPW;
+    const int64_t unit0 = blockIdx.x;
+    const int64_t xc = unit0 % 8, j = unit0 / 8;
+    const int64_t unit_id = ((j / NHG) * 8 + xc) * NHG + j % NHG;
+    if (unit_id >= (int64_t)a.B * NHG * a.runs) return;  // workgroup-uniform, before any barrier
+    const int b = (int)((unit_id / NHG) % a.B);
+    const int grp = (int)(unit_id / ((int64_t)NHG * a.B));
+
+    int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+    L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    const int ntg = (L + kTileGroup - 1) / kTileGroup;
+    // Partitions with tokens: p < pmax.  With one tile-group per partition the workgroup
+    // owns the run of partitions [part_first, part_first + R) (R = run_len) and merges
+    // them into partition part_first (the others are written as empty); otherwise it owns
+    // partition part_first and its strided tile-groups p, p + P, ...
+    const int pmax = a.P < ntg ? a.P : ntg;
+    const int R = a.run_len > 0 ? a.run_len : 1;
+    int part_first, p_end, n_tg, tg_step;
+    if (a.run_len > 0) {
+      // this sequence's pmax partitions in G nearly equal runs of at most R
+      const int G = (pmax + R - 1) / R;
+      if (grp >= G) return;  // workgroup-uniform: nothing written, never read
+      part_first = (int)((int64_t)grp * pmax / G);
+      p_end = (int)((int64_t)(grp + 1) * pmax / G);
+      n_tg = p_end - part_first;
+      tg_step = 1;
+    } else {
+      part_first = grp;
+      if (part_first >= pmax) return;  // workgroup-uniform: nothing written, never read
+      p_end = part_first + 1;
+      n_tg = (ntg - part_first + a.P - 1) / a.P;
+      n_tg = n_tg < a.TGPP ? n_tg : a.TGPP;
+      tg_step = a.P;
+    }
+
+    fp4_unit<QT, UE>(a, lane, wave, b, (int)(unit_id % NHG) * HPW, L, part_first, p_end, n_tg,
+                     tg_step);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_fp4(const DecodeArgs& a, bool q_is_f32, bool ue8m0, hipStream_t stream) {
-  // two kv heads per workgroup when they pair up (whole token rows per workgroup)
-  const int hpw = a.Hk % 2 == 0 ? 2 : 1;
-  const int64_t nhg = a.Hk / hpw;
-  const int64_t units = (int64_t)a.B * nhg * a.runs;  // runs: workgroups per (b, head group)
+  const int64_t units = (int64_t)a.B * a.Hk * a.runs;  // runs: workgroups per (b, h)
   if (units <= 0) return hipSuccess;
-  // padded to a multiple of 8 NHG for the XCD placement of the head groups (see the kernel)
-  const int64_t pad = 8 * nhg;
+  // padded to a multiple of 8 Hk for the XCD placement of the kv heads (see the kernel)
+  const int64_t pad = 8 * (int64_t)a.Hk;
   const int64_t wgs = (units + pad - 1) / pad * pad;
   if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs), block(64 * kW);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, block, 0, stream, a); };
-  if (hpw == 2) {
-    if (ue8m0) {
-      if (q_is_f32) go(decode_fp4_kernel<float, true, 2>); else go(decode_fp4_kernel<uint16_t, true, 2>);
-    } else {
-      if (q_is_f32) go(decode_fp4_kernel<float, false, 2>); else go(decode_fp4_kernel<uint16_t, false, 2>);
-    }
+  if (ue8m0) {
+    if (q_is_f32) go(decode_fp4_kernel<float, true>); else go(decode_fp4_kernel<uint16_t, true>);
   } else {
-    if (ue8m0) {
-      if (q_is_f32) go(decode_fp4_kernel<float, true, 1>); else go(decode_fp4_kernel<uint16_t, true, 1>);
-    } else {
-      if (q_is_f32) go(decode_fp4_kernel<float, false, 1>); else go(decode_fp4_kernel<uint16_t, false, 1>);
-    }
+    if (q_is_f32) go(decode_fp4_kernel<float, false>); else go(decode_fp4_kernel<uint16_t, false>);
   }
   return hipGetLastError();
 }

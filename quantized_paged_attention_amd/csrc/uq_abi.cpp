@@ -150,13 +150,11 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len) {
     // (ties: the shorter run).  Measured on MI355X (B=4, Hk=2, ctx 75000, 512 partitions,
     // 512 slots, 20 launches back to back): R = 5 (472 groups, one round) 38.6 us;
     // R = 3, 4, 6, 8: 51.7, 48.9, 42.3, 50.9 us.
-    // (a workgroup covers two kv heads when Hk is even)
     const int64_t slots = 2LL * device_cus();
-    const int64_t head_groups = Hk % 2 == 0 ? Hk / 2 : Hk;
     int best_r = 1;
     int64_t best_cost = -1;
     for (int r = 1; r <= 8; ++r) {
-      const int64_t groups = (int64_t)B * head_groups * ((pmax + r - 1) / r);
+      const int64_t groups = (int64_t)B * Hk * ((pmax + r - 1) / r);
       const int64_t cost = (groups + slots - 1) / slots * (r + 1);
       if (best_cost < 0 || cost < best_cost) {
         best_cost = cost;
