@@ -253,6 +253,26 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
 size_t uq_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t qg,
                                  int32_t head_dim, int32_t num_partitions);
 
+/* uq_paged_attention_noalloc -- uq_paged_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, arguments and results, without the workspace argument.  Its
+ * workspace is a 64 MiB array in the library's device data (one copy per GPU, held until
+ * the process ends); the library allocates nothing.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two threads) race.  The
+ * arrival counters in it start at zero and every completed call leaves them at zero.
+ * A call whose uq_attention_workspace_bytes exceeds 64 MiB returns UQ_ERR_INVALID_ARG
+ * before launching anything (use uq_paged_attention); other errors as uq_paged_attention. */
+int uq_paged_attention_noalloc(const void* query, int q_dtype, int64_t q_stride_seq,
+                               int64_t q_stride_head, const uint8_t* kv_cache,
+                               int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                               int32_t slot_bytes, int kv_format, const float* k_scale,
+                               const float* v_scale, const int8_t* rot_signs,
+                               const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                               int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                               float softmax_scale, int32_t num_partitions, void* out,
+                               int64_t o_stride_seq, int64_t o_stride_head, void* stream);
+
 /* Bytes of the uq_paged_attention workspace for these sizes on the current device (the
  * work decomposition depends on its compute-unit count); 0 on invalid sizes.  Host-only. */
 size_t uq_attention_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t query_len,

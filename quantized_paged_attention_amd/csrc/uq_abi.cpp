@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/uq_paged.h"
 #include "uq_kernels.h"
@@ -557,3 +558,85 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
 }
 
 }  // extern "C"
+
+// ---- uq_paged_attention_noalloc: the same step with its workspace in a file-scope device
+//      array (one copy per GPU, held until the process ends), for callers that cannot
+//      allocate.  The host name `scratch` is a stand-in, not a device address: the address
+//      of each GPU's copy comes from hipGetSymbolAddress, once per device, with that device
+//      current.  The arrival counters at its start are zero from module load and every
+//      completed call leaves them zero again; the rest is written before it is read.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch`, or NULL (the last error set) on failure
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(UQ_ERR_LAUNCH, "no current HIP device (or device index >= %d)", kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(UQ_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int uq_paged_attention_noalloc(const void* query, int q_dtype, int64_t q_stride_seq,
+                               int64_t q_stride_head, const uint8_t* kv_cache,
+                               int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                               int32_t slot_bytes, int kv_format, const float* k_scale,
+                               const float* v_scale, const int8_t* rot_signs,
+                               const int32_t* block_table, int32_t bt_stride,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t query_len,
+                               int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                               float softmax_scale, int32_t num_partitions, void* out,
+                               int64_t o_stride_seq, int64_t o_stride_head, void* stream) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(UQ_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, num_kv_heads);
+  const size_t need = uq_attention_workspace_bytes(num_seqs, num_kv_heads, query_len,
+                                                   num_q_heads / num_kv_heads, head_dim,
+                                                   num_partitions, max_seq_len, kv_format);
+  if (need == 0)
+    return fail(UQ_ERR_INVALID_ARG, "invalid sizes (num_seqs %d, query_len %d, head_dim %d, "
+                "num_partitions %d, max_seq_len %d, kv_format %d)", num_seqs, query_len,
+                head_dim, num_partitions, max_seq_len, kv_format);
+  if (need > kScratchBytes)
+    return fail(UQ_ERR_INVALID_ARG, "this call needs %zu bytes of workspace, more than the %zu "
+                "of the no-allocation scratch; use uq_paged_attention with a workspace",
+                need, kScratchBytes);
+  if (num_seqs == 0)
+    return uq_paged_attention(query, q_dtype, q_stride_seq, q_stride_head, kv_cache, num_blocks,
+                              block_size, num_kv_heads, slot_bytes, kv_format, k_scale, v_scale,
+                              rot_signs, block_table, bt_stride, seq_lens, num_seqs, query_len,
+                              num_q_heads, head_dim, max_seq_len, softmax_scale, num_partitions,
+                              nullptr, 0, out, o_stride_seq, o_stride_head, stream);
+  void* ws = scratch_of_current_device();
+  if (!ws) return UQ_ERR_LAUNCH;
+  return uq_paged_attention(query, q_dtype, q_stride_seq, q_stride_head, kv_cache, num_blocks,
+                            block_size, num_kv_heads, slot_bytes, kv_format, k_scale, v_scale,
+                            rot_signs, block_table, bt_stride, seq_lens, num_seqs, query_len,
+                            num_q_heads, head_dim, max_seq_len, softmax_scale, num_partitions, ws,
+                            kScratchBytes, out, o_stride_seq, o_stride_head, stream);
+}
+
+}  // extern "C"
+

@@ -23,7 +23,8 @@ UQ_KV_FP8_E4M3, UQ_KV_FP4_E2M1_E4M3S, UQ_KV_FP4_E2M1_UE8M0S = 0, 1, 2
 UQ_KV_FP8_E4M3_TOKSCALE = 3
 
 EXPORTS = ("uq_paged_decode", "uq_paged_reduce", "uq_paged_decode_mtp", "uq_paged_reduce_mtp",
-           "uq_paged_attention", "uq_index_score", "uq_decode_workspace_bytes",
+           "uq_paged_attention", "uq_paged_attention_noalloc", "uq_index_score",
+           "uq_decode_workspace_bytes",
            "uq_attention_workspace_bytes", "uq_last_error")
 
 _lock = threading.Lock()
@@ -70,6 +71,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                            ctypes.c_int, V, V, V, V, i32, V, i32, i32, i32,
                                            i32, i32, f32, i32, V, ctypes.c_size_t, V, i64,
                                            i64, V]
+        lib.uq_paged_attention_noalloc.restype = ctypes.c_int
+        lib.uq_paged_attention_noalloc.argtypes = [V, ctypes.c_int, i64, i64, V, i64, i32, i32,
+                                                   i32, ctypes.c_int, V, V, V, V, i32, V, i32,
+                                                   i32, i32, i32, i32, f32, i32, V, i64, i64, V]
         lib.uq_attention_workspace_bytes.restype = ctypes.c_size_t
         lib.uq_attention_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32,
                                                      ctypes.c_int]
@@ -270,6 +275,28 @@ def paged_attention(query, kv_cache, block_table, seq_lens, *, kv_format, max_se
         *head, QL, Hq, D, int(max_seq_len), float(softmax_scale), int(num_partitions),
         _ptr(workspace), workspace.numel(), _ptr(out), out.stride(0), out.stride(1),
         _stream(stream)))
+    return out
+
+
+def paged_attention_noalloc(query, kv_cache, block_table, seq_lens, *, kv_format,
+                            max_seq_len, num_partitions, out=None, softmax_scale=0.0,
+                            k_scale=None, v_scale=None, rot_signs=None, query_len=1,
+                            stream=None):
+    """One decode step through uq_paged_attention_noalloc: as paged_attention, with the
+    workspace in the library's per-GPU scratch (no allocation by the library; calls that
+    overlap in time on one GPU race).  out is allocated here when None."""
+    lib = load_library()
+    head, (B, QL, Hq, D, hk) = _decode_head(query, kv_cache, block_table, seq_lens, kv_format,
+                                            max_seq_len, k_scale, v_scale, rot_signs,
+                                            query_len)
+    if out is None:
+        out = torch.empty(B * QL, Hq, D, dtype=query.dtype, device=query.device)
+    if out.dtype != query.dtype or out.dim() != 3 or out.stride(2) != 1 or \
+            tuple(out.shape) != (B * QL, Hq, D):
+        raise ValueError("out must be [B*QL, Hq, D] of the query dtype with a contiguous head dim")
+    _check(lib.uq_paged_attention_noalloc(
+        *head, QL, Hq, D, int(max_seq_len), float(softmax_scale), int(num_partitions),
+        _ptr(out), out.stride(0), out.stride(1), _stream(stream)))
     return out
 
 

@@ -253,3 +253,17 @@ def test_attention_workspace_bytes(lib):
         n = uq.attention_workspace_bytes(4, hk, 2, 8, D, 512, 75000, fmt)
         assert n == up(4 * hk * 4) + uq.decode_workspace_bytes(4, hk, 16, D, 512)
     assert uq.attention_workspace_bytes(4, 2, 0, 8, 256, 512, 75000, 1) == 0
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """uq_paged_attention_noalloc refuses, before any HIP call, sizes whose workspace
+    exceeds its 64 MiB scratch."""
+    big_B = 1 << 20
+    assert uq.attention_workspace_bytes(big_B, 2, 1, 16, 256, 512, 75000,
+                                        uq.UQ_KV_FP4_E2M1_E4M3S) > (64 << 20)
+    st = lib.uq_paged_attention_noalloc(
+        FAKE, uq.UQ_BF16, 32 * 256, 256, FAKE, 1, 64, 2, 272, uq.UQ_KV_FP4_E2M1_E4M3S, None,
+        None, None, FAKE, 1172, FAKE, big_B, 1, 32, 256, 75000, 0.0, 512, FAKE, 32 * 256, 256,
+        None)
+    assert st == uq.UQ_ERR_INVALID_ARG
+    assert "no-allocation scratch" in lib.uq_last_error().decode()
