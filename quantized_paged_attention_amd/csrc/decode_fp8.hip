@@ -26,8 +26,10 @@
 //     runs merged into one partial, the partials stay in L2 until the kernel ends.
 //   * Query rows are carried as T tiles of 8 MFMA columns (T = 1 or 2); the K/V loads,
 //     the K operand and the V^T transpose are shared by the tiles, each tile has its own
-//     query operand, softmax state and accumulators.  Wider groups run one launch per
-//     16 rows.
+//     query operand, softmax state and accumulators.  Wider groups (head groups) split
+//     their rows over 2 or 4 waves of a workgroup that stream the same kv head (row
+//     slices: the KV bytes come from HBM once and from the caches for the sibling
+//     waves); otherwise they run one launch per 16 rows.
 //   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
 //     from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query group as an
 //     e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
@@ -43,7 +45,12 @@
 //     6.2 TB/s.
 //   * Softmax is online in exp2 units against a reference max raised (with 4 units of
 //     headroom) only when a score exceeds it, p = 2^(s - ref + 8) <= 256 split into an
-//     e4m3 hi/lo pair in columns 0-7 / 8-15.  PV is a 16x16x32 fp8 MFMA per 8 head dims
+//     e4m3 hi/lo pair in columns 0-7 / 8-15.  Each lane tests its own scores against the
+//     reference; the cross-lane row maximum is taken only on a raise.  The causal mask
+//     is applied only to a tile pair that reaches past the shortest row window.  With
+//     per-tensor scales the row sums of P come from one more MFMA (a block of e4m3 ones
+//     times P), so the sums are those of the codes the PV MFMA multiplies.  Measured on
+//     MI355X (B=128, Hk=8, L ~ U[4k, 16k], QG=16, fused step): 451 -> 436 us.  PV is a 16x16x32 fp8 MFMA per 8 head dims
 //     with A = V^T: each lane pair loads 16 dims of 4 tokens with 16-byte loads, swaps
 //     halves (DPP) and byte-transposes (v_perm), so V codes go to the MFMA untouched.
 //   * Per-token scales (the PR's per_token_kv mode): each lane loads the K and V scale of
@@ -93,12 +100,12 @@ struct FuseUnit {
 // set to zero: the flash-combine of a sequence without tokens.
 template <typename QT, int T>
 __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int lane, const int b,
-                                                 const int h) {
+                                                 const int h, const int RB) {
   const int NR = a.QL * a.QG;
   constexpr int kLanesPerRow = kD * (int)sizeof(QT) / 16;
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
-  const int u_end = a.row_base + 8 * T < NR ? a.row_base + 8 * T : NR;
-  for (int u0 = a.row_base; u0 < u_end; u0 += kRowsPerPass) {
+  const int u_end = RB + 8 * T < NR ? RB + 8 * T : NR;
+  for (int u0 = RB; u0 < u_end; u0 += kRowsPerPass) {
     const int u = u0 + lane / kLanesPerRow;
     if (u < u_end) {
       QT* dst = reinterpret_cast<QT*>(a.out) + ((int64_t)b * a.QL + u / a.QG) * a.o_ss +
@@ -109,7 +116,7 @@ __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int 
   }
 }
 
-// T: tiles of 8 query rows (QL x QG <= 8 T).  The K/V stream, the K operand and the V^T
+// T: tiles of 8 query rows (QL x QG <= 8 T) from unit row RB on.  The K/V stream, the K operand and the V^T
 // transpose are shared by the tiles; each tile has its own query operand, softmax state,
 // accumulators, QK MFMA and PV MFMAs (the pages' M-tiles for wide groups).
 // One work unit of a wave: kv head h of sequence b (length L, already clamped), the
@@ -118,12 +125,18 @@ __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int 
 // partition part_first and marks the others of [part_first, p_end) empty; with FUSE it
 // takes part in the flash-combine of the sequence (FuseUnit) and, as the last of the
 // sequence's units, writes the output rows.
-template <typename QT, int W, bool TOK, bool HG, int T, bool FUSE = false>
+// RSPL: the wave's rows are one of a.row_splits slices of the group; the waves of a
+// workgroup that share a kv head read the same KV lines, so the loads keep the default
+// cache policy (the sibling waves are served from the caches), and the fused state and
+// counter of the unit are the slice rsi's own.
+template <typename QT, int W, bool TOK, bool HG, int T, bool FUSE = false, bool RSPL = false>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane, const int wave,
                                             const int b, const int h, const int L,
                                             const int part_first, const int p_end,
                                             const int first_tg, const int n_tg,
-                                            const int step, const FuseUnit fz = FuseUnit{}) {
+                                            const int step, const int RB, const int rsi,
+                                            const FuseUnit fz = FuseUnit{}) {
+  constexpr int kAux = RSPL ? 0 : kAuxNT;  // cache policy of the KV loads
   static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
   // staging of the merged partition's bf16 output rows (8 rows of 256 bytes per tile, one
   // tile at a time; one stage per wave with head groups; fused: rows of the query dtype),
@@ -143,7 +156,6 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   //      row_base + 8 t + g = (query qj, head qh) of QL query rows x QG heads; query qj
   //      sees the tokens t < L_row (the causal window of its row)
   const int NR = a.QL * a.QG;
-  const int RB = a.row_base;
   // per-tensor scales (the per-token ones are applied per token below)
   const float k_scale = (!TOK && a.k_scale) ? *a.k_scale : 1.f;
   const float v_scale = (!TOK && a.v_scale) ? *a.v_scale : 1.f;
@@ -209,11 +221,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   // l_run the sum of 2^(s - m_run + 8)
   float m_run[T], m_true[T], l_run[T];
   f32x4 acc[T][8];
+  // With per-tensor scales the sums of P come from an MFMA (lacc: every element holds the
+  // column sum of the P codes over the tokens so far, in columns 0-7 the hi and in 8-15
+  // the lo parts); with per-token scales P carries the V scale, so they are summed on
+  // the VALU from the unscaled weights (l_run, per lane).
+  constexpr bool kSumByMfma = !TOK;
+  constexpr long kOnesE4m3x8 = 0x3838383838383838L;  // e4m3 1.0 in every byte
+  f32x4 lacc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     m_run[t] = -INFINITY;
     m_true[t] = -INFINITY;
     l_run[t] = 0.f;
+    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -312,16 +332,16 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   // lane (r, n) loads the scale of token 4 r + (n & 3) of a tile
   const uint32_t s_off = 4u * (uint32_t)(4 * r + (n & 3));
   auto load_s = [&](__amdgpu_buffer_rsrc_t rs) {
-    return bits_f((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, s_off, 0, kAuxNT));
+    return bits_f((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, s_off, 0, kAux));
   };
   auto load_k = [&](__amdgpu_buffer_rsrc_t rs, KTile& d) {
-    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, ka_off, 0, kAuxNT);
-    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, kb_off, 0, kAuxNT);
+    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, ka_off, 0, kAux);
+    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, kb_off, 0, kAux);
   };
   auto load_v = [&](__amdgpu_buffer_rsrc_t rs, VTile& d) {
-    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kAuxNT);
+    d.a = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, 0, kAux);
     // the second token's offset rides in the scalar offset
-    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, (int)pos, kAuxNT);
+    d.b = __builtin_amdgcn_raw_buffer_load_b128(rs, v_off, (int)pos, kAux);
   };
 
   // The stream walks tile pairs (32 tokens).  The K loads of pair i + 1 are issued as
@@ -400,10 +420,20 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float mul = TOK ? ksq[j] * qk_mul[t] : qk_mul[t];
-            const float v = (z[j] + row_ror8(z[j])) * mul;
-            s[t][tt][j] = pair_start + 16 * tt + 4 * r + j < L_row[t] ? v : -INFINITY;
+            s[t][tt][j] = (z[j] + row_ror8(z[j])) * mul;
           }
         }
+      }
+      // causal window: only a pair that reaches past the shortest row window (L - QL + 1
+      // tokens) has invisible tokens (wave-uniform)
+      if (pair_start + 32 > L - a.QL + 1) {
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              s[t][tt][j] = pair_start + 16 * tt + 4 * r + j < L_row[t] ? s[t][tt][j] : -INFINITY;
       }
       // Stage order is fixed: the scheduler must not hoist the prefetch loads above the
       // instructions that free their registers, nor sink them below later waits (vector
@@ -423,17 +453,23 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       // ---- softmax against a reference max m_run >= every score seen.  It is raised
       // (with 4 units of base-2 headroom, so raises are rare) only when a score exceeds
       // it; then the running sums are rescaled.  p * 256 = 2^(s - m_run + 8) <= 256.
+      // Each lane checks its own scores; only when one exceeds the reference does the wave
+      // take the row maximum across lanes (m_true, the true maximum, is kept per lane and
+      // reduced across lanes once, after the stream).
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        float mx = fmaxf(fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3])),
-                         fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
-        mx = max_across_rows(mx);
-        m_true[t] = fmaxf(m_true[t], mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m_run[t])) {  // wave-uniform
+        float lmx = max3f(s[t][0][0], s[t][0][1], s[t][0][2]);
+        lmx = max3f(lmx, s[t][0][3], s[t][1][0]);
+        lmx = max3f(lmx, s[t][1][1], s[t][1][2]);
+        lmx = max3f(lmx, s[t][1][3], s[t][1][3]);
+        m_true[t] = max3f(m_true[t], lmx, lmx);
+        if (__builtin_amdgcn_ballot_w64(lmx > m_run[t])) {  // wave-uniform
+          const float mx = max_across_rows(lmx);
           const float m_new = mx > m_run[t] ? mx + 4.f : m_run[t];
           // 0 when m_run = -inf; 1 for a row that has seen no token yet (both -inf)
           const float alpha = m_run[t] == m_new ? 1.f : fast_exp2(m_run[t] - m_new);
-          l_run[t] *= alpha;
+          if constexpr (kSumByMfma) lacc[t] *= alpha;
+          else l_run[t] *= alpha;
 #pragma unroll
           for (int m = 0; m < 8; ++m) acc[t][m] *= alpha;
           m_run[t] = m_new;
@@ -473,16 +509,17 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             y[j] = fast_exp2(s[t][tt][j] - m8);
-            l_run[t] += y[j];
+            if constexpr (!kSumByMfma) l_run[t] += y[j];
             if constexpr (TOK) y[j] *= vq[tt][j] * v_inv;
           }
-          int hw = cvt_pk_e4m3<false>(y[0], y[1], 0);
-          hw = cvt_pk_e4m3<true>(y[2], y[3], hw);
-          int lw = cvt_pk_e4m3<false>(y[0] - e4m3_to_f<0>(hw), y[1] - e4m3_to_f<1>(hw), 0);
-          lw = cvt_pk_e4m3<true>(y[2] - e4m3_to_f<2>(hw), y[3] - e4m3_to_f<3>(hw), lw);
-          pw[tt] = lo_col ? lw : hw;
+          // the score is dead once exponentiated: its register seeds the code word
+          pw[tt] = e4m3_hilo_word(y[0], y[1], y[2], y[3], lo_col, (int)f_bits(s[t][tt][0]));
         }
         pop[t] = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
+        // the row sums of P as the PV MFMA sees them (hi + lo columns, combined after
+        // the stream): one MFMA against a block of ones instead of 8 VALU additions
+        if constexpr (kSumByMfma) lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+            kOnesE4m3x8, pop[t], lacc[t], 0, 0, 0);
       }
 
       // ---- V^T: exchange halves with the neighbouring lane, then byte-transpose 8 dims
@@ -525,6 +562,16 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 
   }
 
+  // the row maxima and sums over all lanes of the column (l_sum: equal on every lane of
+  // the 8 rows' columns g and g + 8)
+  float l_sum[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    m_true[t] = max_across_rows(m_true[t]);
+    if constexpr (kSumByMfma) l_sum[t] = lacc[t][0] + row_ror8(lacc[t][0]);
+    else l_sum[t] = sum_across_rows(l_run[t]);
+  }
+
   // per-token V scales: the accumulators hold the sums in units of v_ref
   if constexpr (TOK) {
 #pragma unroll
@@ -541,7 +588,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       ref[t] = m_run[t] == -INFINITY ? -INFINITY : m_run[t] - 8.f;
-      lsum[t] = sum_across_rows(l_run[t]);
+      lsum[t] = l_sum[t];
     }
     if (fz.take < fz.pm) {
       // Leave the state in this unit's slot with device-scope stores (written through to
@@ -550,9 +597,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       // the states with device-scope loads; the others are done.  (A release / acquire
       // fence pair would also write back and invalidate the whole L2 of the XCD at every
       // unit end: measured on MI355X, B=128 ctx <= 16k, that costs ~110 us per step.)
+      const int RSN = a.row_splits > 1 ? a.row_splits : 1;
       auto state_rsrc = [&](int64_t k) {
-        const uint64_t base = (uint64_t)(a.states + ((k * a.Hk + h) * a.state_tiles) *
-                                                        (int64_t)kStateBytes);
+        const uint64_t base = (uint64_t)(a.states + (((k * a.Hk + h) * RSN + rsi) *
+                                                     a.state_tiles) * (int64_t)kStateBytes);
         const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
         const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
         return __builtin_amdgcn_make_buffer_rsrc(
@@ -577,7 +625,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
         }
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state stores have completed
-      int32_t* cnt = a.counters + (int64_t)b * a.Hk + h;
+      int32_t* cnt = a.counters + ((int64_t)b * a.Hk + h) * RSN + rsi;
       int old = 0;
       if (lane == 0)
         old = __hip_atomic_fetch_add(cnt, fz.take, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -695,7 +743,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   //      its column (query head), so the merge is lane-local once the states meet in LDS
   float l_tot[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) l_tot[t] = sum_across_rows(l_run[t]);
+  for (int t = 0; t < T; ++t) l_tot[t] = l_sum[t];
   if constexpr (kMerge) {
     if (wave > 0) {
 #pragma unroll
@@ -801,22 +849,33 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 //     blocks together.
 //   Otherwise: workgroup = (kv head, sequence, group of W runs) with the W runs split over
 //     the waves and merged in LDS.
-template <typename QT, int W, bool TOK, bool HG, int T, bool BAL, bool FUSE>
-__global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8_kernel(
+template <typename QT, int W, bool TOK, bool HG, int T, bool BAL, bool FUSE, bool RSPL>
+__global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8_kernel(
     DecodeArgs a) {
   static_assert(!BAL || HG, "balanced slices are built on head groups");
   static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
+  static_assert(!RSPL || HG, "row slices are built on head groups");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t item = blockIdx.x;
-  const int nhs = HG ? a.Hk / W : a.Hk;
+  // Row slices (RSPL): the W waves take W / RS kv heads x RS slices of 16 rows each (wave
+  // w: head w / RS, rows 16 (w % RS) ..); otherwise W heads (head groups) or one.
+  const int RS = RSPL ? a.row_splits : 1;
+  const int HPW = HG ? W / RS : 1;  // kv heads per workgroup
+  const int rsi = RSPL ? wave % RS : 0;
+  const int RB = a.row_base + 16 * rsi;
+  const int hw = RSPL ? wave / RS : wave;  // this wave's head within the workgroup
+  // a slice past the group's rows (33..48 rows in 4 slices): nothing to compute or write;
+  // head-group waves never synchronise, so the wave may leave at once
+  if (RSPL && RB >= a.QL * a.QG) return;
+  const int nhs = HG ? a.Hk / HPW : a.Hk;
   if constexpr (BAL) {
     {
       // Balanced slices: the partitions of all sequences, in sequence order, form one list
       // of Tt entries; slice s of N takes entries [s Tt / N, (s + 1) Tt / N), so every
       // workgroup streams the same number of partitions however ragged the lengths are.
       // A slice that crosses a sequence boundary is streamed as one unit per sequence.
-      const int hh = (int)(item % nhs) * W + wave;
+      const int hh = (int)(item % nhs) * HPW + hw;
       const int64_t slice = item / nhs, N = a.balanced_items;
       auto parts_of = [&](int bb) {  // partitions of sequence bb that hold tokens
         int Lb = a.seq_lens[bb];
@@ -850,7 +909,7 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
       auto zero_empty = [&]() {
         if constexpr (FUSE) {
           for (int64_t bz = slice; bz < a.B; bz += N)
-            if (parts_of((int)bz) == 0) zero_output_rows<QT, T>(a, lane, (int)bz, hh);
+            if (parts_of((int)bz) == 0) zero_output_rows<QT, T>(a, lane, (int)bz, hh, RB);
         }
       };
       if (s0 >= s1) {  // workgroup-uniform
@@ -895,8 +954,8 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
           fz.Tt = Tt;
           fz.N = N;
         }
-        decode_unit<QT, W, TOK, HG, T, FUSE>(a, lane, wave, bb, hh, Lb, p_lo, p_lo + take, p_lo,
-                                             take, 1, fz);
+        decode_unit<QT, W, TOK, HG, T, FUSE, RSPL>(a, lane, wave, bb, hh, Lb, p_lo, p_lo + take,
+                                                   p_lo, take, 1, RB, rsi, fz);
         left -= take;
         e += take;
       }
@@ -904,7 +963,7 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
       return;
     }
   }
-  const int h = (int)(item % nhs) * (HG ? W : 1) + (HG ? wave : 0);
+  const int h = (int)(item % nhs) * HPW + (HG ? hw : 0);
   const int b = (int)((item / nhs) % a.B);
   const int grp = (int)(item / ((int64_t)nhs * a.B));
 
@@ -923,7 +982,7 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
   if constexpr (FUSE) {
     // a sequence without tokens: zero output rows from the first workgroup of its heads
     if (pmax == 0) {
-      if (grp == 0) zero_output_rows<QT, T>(a, lane, b, h);
+      if (grp == 0) zero_output_rows<QT, T>(a, lane, b, h, RB);
       return;
     }
   }
@@ -983,8 +1042,8 @@ __global__ __launch_bounds__(64 * W, BAL ? 1 : (T == 1 ? 3 : 2)) void decode_fp8
     fz.Tt = 0;
     fz.N = 1;
   }
-  decode_unit<QT, W, TOK, HG, T, FUSE>(a, lane, wave, b, h, L, part_first, p_end, first_tg,
-                                       n_tg, step, fz);
+  decode_unit<QT, W, TOK, HG, T, FUSE, RSPL>(a, lane, wave, b, h, L, part_first, p_end,
+                                             first_tg, n_tg, step, RB, rsi, fz);
 }
 
 }  // namespace
@@ -993,24 +1052,29 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
                              hipStream_t stream) {
   constexpr int W = 4;
   const bool hg = a.head_groups != 0;
-  if (hg && a.Hk % W != 0) return hipErrorInvalidValue;
+  // row tiles of 8 query rows, 1 or 2 per wave (4 tiles per wave would spill); wider
+  // groups either split their rows over the waves of a workgroup (row_splits, one launch)
+  // or run in passes of 16 rows, each reading the KV stream once
+  const int rows = a.QL * a.QG;
+  if (rows > 64) return hipErrorInvalidValue;
+  const int RS = a.row_splits > 1 ? a.row_splits : 1;
+  if (RS > 1 && (!hg || (RS != 2 && RS != 4) || rows <= 16 || rows > 16 * RS))
+    return hipErrorInvalidValue;
+  const int HPW = hg ? W / RS : 1;  // kv heads per workgroup
+  if (hg && a.Hk % HPW != 0) return hipErrorInvalidValue;
   // balanced slices hold up to 16 sequence lengths per lane
   if (a.balanced_items > 0 && (!hg || a.B > 1024)) return hipErrorInvalidValue;
-  // row tiles of 8 query rows, 1 or 2 per launch; wider groups run in passes of 16 rows,
-  // each reading the KV stream once (4 tiles per wave would spill)
-  const int rows = a.QL * a.QG;
   const int T = rows <= 8 ? 1 : 2;
-  if (rows > 64) return hipErrorInvalidValue;
   const bool fuse = a.fused != 0;
   if (fuse && (!hg || !a.out || !a.counters || !a.states || a.state_tiles != T))
     return hipErrorInvalidValue;
   const int R = a.run_len > 0 ? a.run_len : 1;
-  // BAL: one workgroup per (W kv heads, slice); HG: per (W kv heads, sequence, run); else
-  // per (kv head, sequence, W runs)
+  // BAL: one workgroup per (HPW kv heads, slice); HG: per (HPW kv heads, sequence, run);
+  // else per (kv head, sequence, W runs)
   const int64_t groups = hg ? (int64_t)a.runs
                             : ((int64_t)a.runs * R + (int64_t)W * R - 1) / ((int64_t)W * R);
-  const int64_t items = a.balanced_items > 0 ? (int64_t)a.balanced_items * (a.Hk / W)
-                                             : groups * a.B * (hg ? a.Hk / W : a.Hk);
+  const int64_t items = a.balanced_items > 0 ? (int64_t)a.balanced_items * (a.Hk / HPW)
+                                             : groups * a.B * (hg ? a.Hk / HPW : a.Hk);
   if (items <= 0) return hipSuccess;
   if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)items), block(64 * W);
@@ -1018,34 +1082,44 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   auto go = [&](auto kernel, const DecodeArgs& p) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
   };
-  // one instantiation per (query type, per-token scales, order, row tiles, fused)
+  // one instantiation per (query type, per-token scales, order, row tiles, fused, slices)
   auto pick = [&](auto qt, auto tok, const DecodeArgs& p) {
     using QT = decltype(qt);
     constexpr bool TOK = decltype(tok)::value;
-    if (bal) {
-      if (fuse) {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, true>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true>, p);
+    if (RS > 1) {  // two row tiles, head groups
+      if (bal) {
+        if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, true>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, true>, p);
       } else {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, false>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false>, p);
+        if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, true>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, true>, p);
+      }
+    } else if (bal) {
+      if (fuse) {
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, true, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, false>, p);
+      } else {
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, false>, p);
       }
     } else if (hg) {
       if (fuse) {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, true>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true>, p);
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, true, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, false>, p);
       } else {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, false>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false>, p);
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, false>, p);
       }
     } else {
-      if (T == 1) go(decode_fp8_kernel<QT, W, TOK, false, 1, false, false>, p);
-      else go(decode_fp8_kernel<QT, W, TOK, false, 2, false, false>, p);
+      if (T == 1) go(decode_fp8_kernel<QT, W, TOK, false, 1, false, false, false>, p);
+      else go(decode_fp8_kernel<QT, W, TOK, false, 2, false, false, false>, p);
     }
   };
-  for (int rb = 0; rb < rows; rb += 16) {
+  const int pass_rows = 16 * RS;
+  for (int rb = 0; rb < rows; rb += pass_rows) {
     DecodeArgs p = a;
     p.row_base = rb;
+    p.row_splits = RS;
     if (tok_scales) {
       if (q_is_f32) pick(float{}, std::true_type{}, p); else pick(uint16_t{}, std::true_type{}, p);
     } else {

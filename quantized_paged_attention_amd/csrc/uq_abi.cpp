@@ -84,11 +84,12 @@ namespace {
 struct Plan {
   int TGPP;            // tile-groups per partition
   int run_len, runs;   // partitions per work item (0: one partition, strided tile-groups)
-  int head_groups;     // fp8: workgroups of 4 neighbouring kv heads
+  int head_groups;     // fp8: workgroups of 4 / row_splits neighbouring kv heads
+  int row_splits;      // fp8 head groups: waves per kv head (16 query rows each)
   int balanced_items;  // fp8 head groups: slices per head group (0: runs per sequence)
 };
 
-Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len) {
+Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len, int rows) {
   Plan p{};
   const int ntg = (max_seq_len + uq::kTileGroup - 1) / uq::kTileGroup;
   p.TGPP = ntg == 0 ? 1 : (ntg + P - 1) / P;
@@ -118,10 +119,21 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len) {
     // lengths.  Measured on MI355X (fp8, Hk=8, 64 partitions): B=16, L=16k: run 8
     // (256 workgroups) 86 us, runs 4 / 6 / 16: 89 / 102 / 129 us; B=128, L ~ U[4k, 16k]:
     // run 11 472 us, runs 8 / 16 / 22: 482 / 494 / 506 us.
-    if (Hk % 4 == 0) {
+    //   Wider query groups (more than 16 rows) split their rows over RS = 2 or 4 waves
+    // of a workgroup (4 / RS kv heads each): one launch reads the KV stream once from
+    // HBM, the sibling waves of a head hit the caches, and balanced slices put two
+    // workgroups on each compute unit (a wave is latency-bound, so a unit needs four kv
+    // heads in flight).  Measured on MI355X (B=128, Hk=8, L ~ U[4k, 16k], decode):
+    // QG=32: passes of 16 rows 915 us, row slices with one workgroup per unit 837 us,
+    // with two 666 us; QG=64: 1836 / 1631 / 1160 us.  QG=16 (one wave per head) stays
+    // at one workgroup per unit: 451 us, two per unit 465 us.
+    const int RS = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const int HPW = 4 / RS;
+    if (Hk % HPW == 0) {
       p.head_groups = 1;
+      p.row_splits = RS;
       if (p.TGPP == 1 && B > 0) {
-        const int64_t units = (int64_t)B * (Hk / 4);
+        const int64_t units = (int64_t)B * (Hk / HPW);  // workgroups per run
         const int64_t cus = device_cus();
         int64_t G;  // runs per (sequence, head group)
         if (units * pmax <= 16 * cus)
@@ -138,7 +150,7 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len) {
         // workgroups per unit 439 / 453 us.  With little work the runs above already fill
         // one round (B=16, L=16k: 88 us either way).
         if (units * pmax > 16 * cus && B <= 1024) {
-          const int64_t per_hg = cus / (Hk / 4);
+          const int64_t per_hg = (RS > 1 ? 2 : 1) * cus / (Hk / HPW);
           p.balanced_items = (int)(per_hg > 0 ? per_hg : 1);
         }
       }
@@ -168,9 +180,9 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len) {
   return p;
 }
 
-// Workspace of uq_paged_attention: the [B, Hk] arrival counters, then either the fused
-// states (fp8 head groups: one slot per work unit of a sequence, kStateBytes per kv head
-// and row tile) or the three decode partial buffers.
+// Workspace of uq_paged_attention: the [B, Hk, row slices] arrival counters, then either
+// the fused states (fp8 head groups: one slot per work unit of a sequence, kStateBytes per
+// kv head, row slice and row tile) or the three decode partial buffers.
 struct AttnLayout {
   bool fused;
   int tiles;              // row tiles per fused state
@@ -180,9 +192,11 @@ struct AttnLayout {
 
 AttnLayout attn_layout(int fmt, int B, int Hk, int QL, int QG, int D, int P, int max_seq_len) {
   AttnLayout l{};
-  const Plan p = plan_decode(fmt, B, Hk, P, max_seq_len);
-  const int rows = QL * QG;
-  l.counter_bytes = up256((size_t)B * Hk * 4);
+  const int64_t rows64 = (int64_t)QL * QG;
+  const int rows = rows64 > 1024 ? 1024 : (int)rows64;
+  const Plan p = plan_decode(fmt, B, Hk, P, max_seq_len, rows);
+  const int RS = p.row_splits > 1 ? p.row_splits : 1;
+  l.counter_bytes = up256((size_t)B * Hk * RS * 4);
   l.fused = (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) && p.head_groups;
   if (l.fused) {
     l.tiles = rows <= 8 ? 1 : 2;
@@ -190,7 +204,7 @@ AttnLayout attn_layout(int fmt, int B, int Hk, int QL, int QG, int D, int P, int
     // b * runs + g
     l.slots = p.balanced_items > 0 ? (int64_t)p.balanced_items + B - 1 : (int64_t)B * p.runs;
     if (l.slots < 1) l.slots = 1;
-    l.body_bytes = up256((size_t)l.slots * Hk * l.tiles * uq::kStateBytes);
+    l.body_bytes = up256((size_t)l.slots * Hk * RS * l.tiles * uq::kStateBytes);
   } else {
     l.body_bytes = uq_decode_workspace_bytes(B, Hk, rows, D, P);
   }
@@ -271,7 +285,9 @@ int decode_impl(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_
   if (reinterpret_cast<uintptr_t>(kv_cache) & 15)
     return fail(UQ_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
 
-  const Plan plan = plan_decode(kv_format, num_seqs, num_kv_heads, num_partitions, max_seq_len);
+  const int64_t rows64 = (int64_t)query_len * QG;
+  const Plan plan = plan_decode(kv_format, num_seqs, num_kv_heads, num_partitions, max_seq_len,
+                                rows64 > 1024 ? 1024 : (int)rows64);
   uq::DecodeArgs a{};
   a.q = query;
   a.q_ss = q_stride_seq;
@@ -297,6 +313,7 @@ int decode_impl(const void* query, int q_dtype, int64_t q_stride_seq, int64_t q_
   a.run_len = plan.run_len;
   a.runs = plan.runs;
   a.head_groups = plan.head_groups;
+  a.row_splits = plan.row_splits;
   a.balanced_items = plan.balanced_items;
   a.softmax_scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
   a.part_o = static_cast<uint16_t*>(part_out);

@@ -41,19 +41,21 @@ __device__ __forceinline__ float sum_across_rows(float x) {
   return bits_f(b[0]) + bits_f(b[1]);
 }
 
-// Exchange with the lane n ^ 8 of the same 16-lane row (DPP row rotate by 8).
+// Exchange with the lane n ^ 8 of the same 16-lane row (DPP row rotate by 8).  The DPP
+// moves here read valid lanes only, so bound_ctrl changes no result; it lets the compiler
+// fold the move into the VALU instruction that consumes it (one v_add_f32_dpp, say).
 __device__ __forceinline__ float row_ror8(float v) {
-  return bits_f((uint32_t)__builtin_amdgcn_mov_dpp((int)f_bits(v), 0x128, 0xF, 0xF, false));
+  return bits_f((uint32_t)__builtin_amdgcn_mov_dpp((int)f_bits(v), 0x128, 0xF, 0xF, true));
 }
 
 // The four values of the lane's quad (lanes 4k .. 4k+3), each broadcast to every lane of
 // the quad (DPP quad_perm [j, j, j, j] for j = 0..3).
 __device__ __forceinline__ void quad_values(float v, float out[4]) {
   const int x = (int)f_bits(v);
-  out[0] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, false));
-  out[1] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, false));
-  out[2] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, false));
-  out[3] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, false));
+  out[0] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, true));
+  out[1] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, true));
+  out[2] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, true));
+  out[3] = bits_f((uint32_t)__builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -79,6 +81,29 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old) {
 template <int sel>
 __device__ __forceinline__ float e4m3_to_f(int word) {
   return __builtin_amdgcn_cvt_f32_fp8(word, sel);
+}
+
+// Four floats as one word of e4m3 codes: hi(y) = the nearest e4m3 values when lo is false,
+// the nearest e4m3 values of the residuals y - hi(y) when lo is true (RNE).  `scratch` is
+// any dead value: the conversion keeps the other half of its destination, so passing a
+// dead register spares the move that would clear it.
+__device__ __forceinline__ int e4m3_hilo_word(float y0, float y1, float y2, float y3, bool lo,
+                                              int scratch) {
+  int hw = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, scratch, false);
+  hw = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, hw, true);
+  const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+  const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+  const float c = lo ? -1.f : 0.f;  // y - hi(y) for lo, y itself (exactly) for hi
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(fmaf(c, h01[0], y0), fmaf(c, h01[1], y1), hw, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(fmaf(c, h23[0], y2), fmaf(c, h23[1], y3), w, true);
+}
+
+// max(a, b, c) in one v_max3_f32.  fmaxf would first quiet each operand that the compiler
+// cannot prove is no signalling NaN (one extra instruction per operand).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // 4x4 byte transpose: in[j] holds bytes (m = 0..3) of token j; out[m] holds byte m of
@@ -110,7 +135,7 @@ __device__ __forceinline__ void transpose4x4_bytes_sel(const uint32_t in[4], uin
 
 // Swap a value with the neighbouring lane (lane 2k <-> 2k+1; DPP quad_perm [1,0,3,2]).
 __device__ __forceinline__ int swap_adjacent(int v) {
-  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);
 }
 
 template <typename T>

@@ -29,6 +29,10 @@ struct DecodeArgs {
   int32_t head_groups;  // fp8: 1 = a workgroup's waves are consecutive kv heads of one run
   int32_t row_base;     // fp8: first unit row of this launch (wide groups run in passes of
                         // 16 rows; set by the launcher)
+  int32_t row_splits;   // fp8 head groups, more than 16 rows: 2 or 4 = one launch in which
+                        // each kv head's rows are split over that many waves of a workgroup
+                        // (16 rows each; 4 / row_splits kv heads per workgroup); 0 or 1 =
+                        // passes of 16 rows
   int32_t balanced_items;  // fp8 head groups: > 0 = the partitions of all sequences are
                            // split on the device into this many equal slices per head group
   float softmax_scale;
@@ -43,8 +47,8 @@ struct DecodeArgs {
   int32_t fused;               // 1: the above; 0: write partials
   void* out;                   // [B*QL, Hq, D] of the query dtype, element strides o_ss, o_sh
   int64_t o_ss, o_sh;
-  int32_t* counters;           // [B * Hk], zero between calls
-  uint8_t* states;             // kStateBytes per (slot, kv head, row tile)
+  int32_t* counters;           // [B * Hk * RS], zero between calls (RS = row_splits or 1)
+  uint8_t* states;             // kStateBytes per (slot, kv head, row slice, row tile)
   int32_t state_tiles;         // row tiles per state (1 or 2)
 };
 
