@@ -41,6 +41,18 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out_dir: str) -> str:
+    """The same library with AddressSanitizer and UndefinedBehaviorSanitizer (gcc); load it
+    through $UQ_ORACLE_LIB with gcc's libasan preloaded."""
+    os.makedirs(out_dir, exist_ok=True)
+    lib = os.path.join(out_dir, "liboracle_san.so")
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fno-fast-math", "-ffp-contract=off",
+           "-fopenmp", "-fPIC", "-shared", "-Wall", "-o", lib, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return lib
+
+
 def _load():
     global _lib
     with _lock:

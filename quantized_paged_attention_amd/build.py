@@ -53,5 +53,38 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+def build_host_sanitized(out_dir: str) -> str:
+    """libuq.so with AddressSanitizer and UndefinedBehaviorSanitizer in its host code (the
+    C ABI: argument checks, planning, workspace layout), linked with the kernel objects of
+    the last build().  Device code is built exactly as in build(): every -fsanitize= flag
+    applies to the host side only.  Load it with clang's ASan runtime preloaded."""
+    objs = [os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES[1:]]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose=False)
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"]
+    obj = os.path.join(out_dir, "uq_abi_san.o")
+    cmd = [HIPCC, "-O1", "-g", *COMMON[1:], *DEVICE_FLAGS, *san, "-x", "hip", "-c",
+           os.path.join(CSRC, "uq_abi.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for uq_abi.cpp (sanitized):\n{r.stderr}")
+    lib = os.path.join(out_dir, "libuq_san.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan",
+           "-o", lib, obj, *objs]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return lib
+
+
+def asan_runtime() -> str:
+    """Path of the ASan runtime that build_host_sanitized() links against."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
     build()

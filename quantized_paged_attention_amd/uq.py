@@ -38,12 +38,14 @@ class UqError(RuntimeError):
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
-    """Load libuq.so (built by ``python -m quantized_paged_attention_amd.build``)."""
+    """Load libuq.so (built by ``python -m quantized_paged_attention_amd.build``), or the
+    library at ``path``, or at $UQ_LIB when that is set (another build of the same
+    sources, e.g. one with host-side sanitizers)."""
     global _lib
     with _lock:
         if _lib is not None and path is None:
             return _lib
-        p = path or LIB_PATH
+        p = path or os.environ.get("UQ_LIB") or LIB_PATH
         if not os.path.exists(p):
             raise RuntimeError(f"{p} is missing: build it with "
                                "`python -m quantized_paged_attention_amd.build`")
