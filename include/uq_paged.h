@@ -193,19 +193,21 @@ int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float
  *                   for the same sizes, 256-byte aligned.  It must be zero-filled once
  *                   before its first use (e.g. hipMemset after allocating it); every
  *                   call that completes leaves it fit for the next call of any sizes
- *                   that fit it (the arrival counters it holds return to zero), so it can
- *                   be reused across calls and graph replays.  Calls that overlap in time
+ *                   that fit it (its first 256 KiB hold arrival counters, which
+ *                   every call leaves at zero and nothing else writes), so it can be
+ *                   reused across calls and graph replays.  Calls that overlap in time
  *                   on one workspace race.
  *   out             [num_seqs * query_len, num_q_heads, head_dim] of q_dtype, element
  *                   strides o_stride_seq / o_stride_head (> 0, 16-byte multiples; the head
  *                   dim is contiguous, out 16-byte aligned).
- * How it runs: with the fp8 formats and num_kv_heads a multiple of 4 one launch; every work
- * unit of a (sequence, kv head) that does not cover the whole sequence leaves its softmax
- * state in the workspace and counts its partitions with a device-scope atomic, and the
- * unit that completes the count merges the states and writes the output rows.  Other
- * formats and head counts run the decode into partials held in the workspace, then the
- * reduce (two launches).  Errors as uq_paged_decode_mtp, plus UQ_ERR_INVALID_ARG for a
- * NULL, misaligned or too small workspace or output. */
+ * How it runs: with the fp8 formats and head groups (num_kv_heads a multiple of 4, or of
+ * 2 / 1 for groups of 17-32 / 33-64 rows) one launch; every work unit of a (sequence, kv
+ * head) that does not cover the whole sequence leaves its softmax state in the workspace
+ * and counts its partitions with a device-scope atomic, and the unit that completes the
+ * count merges the states and writes the output rows.  Other formats and head counts run
+ * the decode into partials held in the workspace, then the reduce (two launches).  Errors
+ * as uq_paged_decode_mtp, plus UQ_ERR_INVALID_ARG for a NULL, misaligned or too small
+ * workspace or output. */
 int uq_paged_attention(const void* query, int q_dtype, int64_t q_stride_seq,
                        int64_t q_stride_head, const uint8_t* kv_cache, int64_t num_blocks,
                        int32_t block_size, int32_t num_kv_heads, int32_t slot_bytes,
@@ -259,7 +261,8 @@ size_t uq_decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t
  * workspace is a 64 MiB array in the library's device data (one copy per GPU, held until
  * the process ends); the library allocates nothing.  Every call on a GPU shares that GPU's
  * array: calls that overlap in time on one GPU (two streams, two threads) race.  The
- * arrival counters in it start at zero and every completed call leaves them at zero.
+ * counters in its first 256 KiB start at zero and every completed call leaves them at
+ * zero; nothing else is written there.
  * A call whose uq_attention_workspace_bytes exceeds 64 MiB returns UQ_ERR_INVALID_ARG
  * before launching anything (use uq_paged_attention); other errors as uq_paged_attention. */
 int uq_paged_attention_noalloc(const void* query, int q_dtype, int64_t q_stride_seq,

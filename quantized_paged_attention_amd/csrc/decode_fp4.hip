@@ -150,7 +150,10 @@ __device__ __forceinline__ Chunk load_chunk(const DecodeArgs& a, int n, int q, i
 // [part_first, p_end) are written as empty.  Wave w (part) streams tokens [64 w, 64 w + 64)
 // of each tile-group.  (The code keeps a head index hw: covering both heads of a token row
 // with one workgroup, whole 544-byte rows, measured slower on MI355X: 52.4 vs 50.6 us at
-// QG 16, as did balanced slices of 8 waves per CU, 52.4 us.)
+// QG 16, as did balanced slices of 8 waves per CU, 52.4 us.  So did a work queue:
+// persistent workgroups on a head pair taking 128-token items from a device counter, one
+// barrier and one block-table read per item, 68 us per step against 54 us for these
+// static runs; the same items dealt statically, 71 us.)
 template <typename QT, bool UE>
 __device__ __forceinline__ void fp4_unit(const DecodeArgs& a, const int lane, const int wave,
                                          const int b, const int h0, const int L,

@@ -180,9 +180,17 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len, int rows) {
   return p;
 }
 
-// Workspace of uq_paged_attention: the [B, Hk, row slices] arrival counters, then either
-// the fused states (fp8 head groups: one slot per work unit of a sequence, kStateBytes per
-// kv head, row slice and row tile) or the three decode partial buffers.
+// Workspace of uq_paged_attention: a fixed region of arrival counters (the fp8 fused
+// step: [B, Hk, row slices]), then either the fused states (fp8 head groups: one slot per
+// work unit of a sequence, kStateBytes per kv head, row slice and row tile) or the three
+// decode partial buffers.
+// The counter region has the same size for every call, and nothing else is ever written
+// there, so the zeros that each completed call leaves in it hold for a later call of any
+// sizes (a region that grew with the sizes would take in the bodies of earlier, smaller
+// calls).  A call that needs more counters than the region holds runs the two-launch
+// decode + reduce instead.
+constexpr size_t kCounterBytes = (size_t)256 << 10;
+
 struct AttnLayout {
   bool fused;
   int tiles;              // row tiles per fused state
@@ -196,8 +204,9 @@ AttnLayout attn_layout(int fmt, int B, int Hk, int QL, int QG, int D, int P, int
   const int rows = rows64 > 1024 ? 1024 : (int)rows64;
   const Plan p = plan_decode(fmt, B, Hk, P, max_seq_len, rows);
   const int RS = p.row_splits > 1 ? p.row_splits : 1;
-  l.counter_bytes = up256((size_t)B * Hk * RS * 4);
-  l.fused = (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) && p.head_groups;
+  l.counter_bytes = kCounterBytes;
+  l.fused = (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) && p.head_groups &&
+            (size_t)B * Hk * RS * 4 <= kCounterBytes;
   if (l.fused) {
     l.tiles = rows <= 8 ? 1 : 2;
     // balanced slices: unit (b, slice s) uses slot s + b; runs: unit (b, run g) slot
@@ -580,8 +589,9 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
 //      array (one copy per GPU, held until the process ends), for callers that cannot
 //      allocate.  The host name `scratch` is a stand-in, not a device address: the address
 //      of each GPU's copy comes from hipGetSymbolAddress, once per device, with that device
-//      current.  The arrival counters at its start are zero from module load and every
-//      completed call leaves them zero again; the rest is written before it is read.
+//      current.  The counter region at its start (the same 256 KiB for every call, written
+//      by nothing else) is zero from module load and every completed call leaves it zero
+//      again; the rest is written before it is read.
 namespace {
 
 constexpr size_t kScratchBytes = (size_t)64 << 20;

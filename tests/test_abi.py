@@ -242,16 +242,24 @@ def test_attention_zero_sequences_is_a_no_op(lib):
 
 
 def test_attention_workspace_bytes(lib):
-    """Counters [B, Hk] then the fused states (fp8 head groups) or the decode partials.
-    With no GPU the planner assumes 256 compute units: the fp8 high-batch shape takes
-    balanced slices, 128 per head group, so 128 + 127 state slots of one row tile."""
+    """A fixed 256 KiB counter region, then the fused states (fp8 head groups) or the
+    decode partials.  With no GPU the planner assumes 256 compute units: the fp8
+    high-batch shape takes balanced slices, 128 per head group, so 128 + 127 state slots
+    of one row tile; with QG=32 two row slices per head and two workgroups per unit."""
     up = lambda x: (x + 255) // 256 * 256
+    counters = 256 << 10
+    state = 8 * 64 * 16 + 2 * 64 * 4
     n = uq.attention_workspace_bytes(128, 8, 1, 8, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
-    assert n == up(128 * 8 * 4) + up(255 * 8 * 1 * (8 * 64 * 16 + 2 * 64 * 4))
+    assert n == counters + up(255 * 8 * 1 * state)
+    n = uq.attention_workspace_bytes(128, 8, 1, 32, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
+    assert n == counters + up((128 + 127) * 8 * 2 * 2 * state)
     # fp8 with an odd head count and fp4: decode partials after the counters
     for fmt, hk, D in ((uq.UQ_KV_FP8_E4M3, 3, 128), (uq.UQ_KV_FP4_E2M1_E4M3S, 2, 256)):
         n = uq.attention_workspace_bytes(4, hk, 2, 8, D, 512, 75000, fmt)
-        assert n == up(4 * hk * 4) + uq.decode_workspace_bytes(4, hk, 16, D, 512)
+        assert n == counters + uq.decode_workspace_bytes(4, hk, 16, D, 512)
+    # more arrival counters than the region holds: the decode + reduce layout
+    n = uq.attention_workspace_bytes(9000, 8, 1, 8, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
+    assert n == counters + uq.decode_workspace_bytes(9000, 8, 8, 128, 64)
     assert uq.attention_workspace_bytes(4, 2, 0, 8, 256, 512, 75000, 1) == 0
 
 

@@ -77,8 +77,9 @@ def test_balanced_whole_sequences_in_slices():
 
 
 def test_workspace_reused_across_sizes():
-    """One workspace for two calls in a row, the second with a smaller batch and other
-    lengths: both match the oracle and the counters are zero after each."""
+    """One workspace for calls in a row, the second with a smaller batch and other
+    lengths, the third with more arrival counters than either (sequences x kv heads):
+    all match the oracle and the counters are zero after each."""
     need_gpu()
     big = fp8(sparse_lens(320), hk=8, qg=8, seed=321)
     ws = uq.alloc_workspace(big.B, 8, 1, 8, 128, big.num_partitions, big.max_seq_len,
@@ -93,6 +94,13 @@ def test_workspace_reused_across_sizes():
     got, _ = run_decode(small, workspace=ws)
     assert_decode_close(got, oracle_decode(small), "fused reuse, second call")
     assert not counters_of(ws, small.B, 8).any()
+    grow = fp8(np.random.default_rng(323).integers(0, 2000, size=200), hk=8, qg=8, seed=324)
+    need = uq.attention_workspace_bytes(grow.B, 8, 1, 8, 128, grow.num_partitions,
+                                       grow.max_seq_len, grow.kv_format)
+    assert need <= ws.numel()
+    got, _ = run_decode(grow, workspace=ws)
+    assert_decode_close(got, oracle_decode(grow), "fused reuse, third call")
+    assert not counters_of(ws, grow.B, 8).any()
 
 
 @pytest.mark.parametrize("ql,qg,hk", [(2, 16, 4), (4, 8, 8), (1, 48, 4)])

@@ -1,7 +1,9 @@
 """uq_paged_attention_noalloc (the no-allocation variant of uq_paged_attention, its
 workspace in the library's per-GPU scratch) against uq_paged_attention with a workspace
-of its own, on two calls in a row, the second with a smaller input; both against the
-oracle as well.  Runs alone in a fresh process and after the other tests."""
+of its own, on two calls in a row, the second with a smaller input, then a third larger
+than the first (more arrival counters than either: the counters sit in a fixed region
+that no other data ever touches); all against the oracle as well.  Runs alone in a
+fresh process and after the other tests."""
 
 import numpy as np
 import pytest
@@ -35,21 +37,25 @@ def run_both(case):
 
 @pytest.mark.parametrize("kind", ["fp8_fused", "fp4_split"])
 def test_noalloc_matches_workspace_entry(kind):
-    """Two calls in a row on the shared scratch, the second smaller: each output equals the
-    workspace entry point's within 1e-3 of max|out| (the fused merge order may differ) and
-    the oracle within the decode tolerance."""
+    """Calls in a row on the shared scratch, the second smaller, the third larger: each
+    output equals the workspace entry point's within 1e-3 of max|out| (the merge order may
+    differ) and the oracle within the decode tolerance."""
     need_gpu()
     rng = np.random.default_rng(500)
     if kind == "fp8_fused":
         big = fp8_case(rng.integers(1, 9000, size=96), hk=8, qg=8, seed=501)
         small = fp8_case((1, 700, 5000, 0, 257), hk=8, qg=8, seed=502)
+        grow = fp8_case(rng.integers(0, 3000, size=128), hk=8, qg=8, seed=505)
     else:
         big = synth.make_fp4_case("noalloc4", 503, seq_lens=[300, 5000, 20000, 64], num_kv_heads=2,
                                   qg=16, head_dim=256, block_size=64, rotate=True, spare_blocks=3)
         small = synth.make_fp4_case("noalloc4", 504, seq_lens=[1000, 33], num_kv_heads=2,
                                     qg=8, head_dim=256, block_size=64, rotate=True,
                                     spare_blocks=3)
-    for i, case in enumerate((big, small)):
+        grow = synth.make_fp4_case("noalloc4", 506, seq_lens=[900, 3000, 12, 7000, 260, 5],
+                                   num_kv_heads=4, qg=4, head_dim=256, block_size=64,
+                                   rotate=True, spare_blocks=3)
+    for i, case in enumerate((big, small, grow)):
         log(f"case noalloc {kind} call {i} B={case.B}")
         got, ref = run_both(case)
         assert np.isfinite(got).all()
