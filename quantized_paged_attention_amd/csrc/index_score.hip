@@ -30,7 +30,9 @@
 //     over contiguous shares of the list, two per SIMD: 16.2 / 19.3 us; one wave per live
 //     page: 11.7 / 15.6 us.  Wave timestamps of the last: every wave starts within 1 us,
 //     the pages arrive between 2.8 and 9.2 us (45 MB at ~7 TB/s), each page then takes
-//     ~1.5 us of dequant and MFMA.
+//     ~1.5 us of dequant and MFMA.  The query bytes are loaded before the table entry and
+//     the page, tile by tile, so a page's first tiles are scored while its last ones are
+//     in flight (graph-timed on MI355X: 11.8 -> 11.45 us at QL 1 x H 1).
 //   * More requests: one wave per (request, page slot), the table entry read after the
 //     length says the page is live.
 #include "uq_device.h"
@@ -83,10 +85,13 @@ __device__ __forceinline__ void load_page(const uint8_t* pg, int n, int q, Page&
       kPageTokens * (kCodeBytes + kScaleBytes), 0x00020000);
   const uint32_t co = (uint32_t)(n * kCodeBytes + 16 * q);
   const uint32_t so = (uint32_t)(kScaleRegion + n * kScaleBytes + 4 * (q >> 1));
+  // tile by tile (codes, then the scale word): loads return in order, so tile T can be
+  // scored as soon as its two loads are back
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
     d.kc[T] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 16 * T * kCodeBytes, 2);
     d.ksw[T] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 16 * T * kScaleBytes, 2);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -206,11 +211,13 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
     const int r = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
     const int b = e - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(pl, r));
     const int L = __builtin_amdgcn_readlane(Ll, r);
+    // the query bytes first: vector loads return in order, so with them ahead of the
+    // page the first tile's MFMAs can start while the rest of the page is in flight
+    i32x4 qraw[2][2];
+    load_q_raw<NCT>(a, r, n, q, R, qraw);
     const int pid = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r * a.bt_stride + b]);
     Page cur;
     load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
-    i32x4 qraw[2][2];
-    load_q_raw<NCT>(a, r, n, q, R, qraw);
     f16x8 qb[2][4];
     q_operands<NCT>(qraw, qb);
     int lim0[2];
@@ -238,12 +245,13 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
   if (b >= nblk) return;  // cells of pages past the sequence are left untouched
   const int n = lane & 15, q = lane >> 4;
   const int R = a.QL * a.H;
-  // the table entry of a live page only (read after the length)
+  // the query bytes, then the table entry of a live page only (read after the length),
+  // then the page
+  i32x4 qraw[2][2];
+  load_q_raw<NCT>(a, r, n, q, R, qraw);
   const int pid = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r * a.bt_stride + b]);
   Page cur;
   load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
-  i32x4 qraw[2][2];
-  load_q_raw<NCT>(a, r, n, q, R, qraw);
   f16x8 qb[2][4];
   q_operands<NCT>(qraw, qb);
   int lim0[2];
