@@ -143,8 +143,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   // and the states of waves 1..W-1 handed to wave 0 (per lane and tile: 32 accumulators,
   // m_run, m_true, l)
   constexpr bool kMerge = W > 1 && !HG;
-  constexpr int kStageElems = (FUSE ? (int)sizeof(QT) / 2 : 1) * 8 * kD;  // 16-bit units
-  __shared__ __attribute__((aligned(16))) uint16_t o_stage[(HG ? W : 1) * kStageElems];
+  // stage rows: 8 output rows of the query dtype (fused) or bf16, padded by 16 bytes so
+  // that the 16 rows a b128 store instruction touches start in different banks
+  constexpr int kStageRow = (FUSE ? (int)sizeof(QT) : 2) * kD + 16;  // bytes
+  constexpr int kStageBytes = 8 * kStageRow;
+  __shared__ __attribute__((aligned(16))) uint8_t o_stage[(HG ? W : 1) * kStageBytes];
   __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][T][32][64];
   __shared__ float st_ml[kMerge ? W - 1 : 1][T][3][64];
   const int r = lane >> 4, n = lane & 15;
@@ -691,7 +694,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
     }
     // ---- output rows: o = v_scale acc / l (0 without tokens), hi and lo columns added;
     //      the rows go through this wave's LDS stage so that each is written whole
-    uint16_t* stage = o_stage + wave * kStageElems;
+    uint8_t* stage = o_stage + wave * kStageBytes;
     constexpr int kRowBytes = kD * (int)sizeof(QT);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -707,7 +710,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
         float o[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) o[m] = (acc[t][m][j] + row_ror8(acc[t][m][j])) * inv;
-        uint8_t* row = reinterpret_cast<uint8_t*>(stage) + n * kRowBytes;
+        uint8_t* row = stage + n * kStageRow;
         if (n < nrow) {
           if constexpr (sizeof(QT) == 4) {
             *reinterpret_cast<f32x4*>(row + 4 * (32 * r + 8 * j)) = f32x4{o[0], o[1], o[2], o[3]};
@@ -732,8 +735,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
                     (int64_t)(h * a.QG + urow % a.QG) * a.o_sh;
           const int chunk = lane % kLanesPerRow;
           *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(dst) + 16 * chunk) =
-              *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) +
-                                              i * kRowBytes + 16 * chunk);
+              *reinterpret_cast<const i32x4*>(stage + i * kStageRow + 16 * chunk);
         }
       }
     }
@@ -761,7 +763,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
     if (wave > 0) return;
   }
   const int64_t row0 = (((int64_t)b * a.Hk + h) * a.P + part_first) * NR;
-  uint16_t* stage = o_stage + (HG ? wave : 0) * 8 * kD;
+  uint8_t* stage = o_stage + (HG ? wave : 0) * kStageBytes;
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     // statistics relative to the true maximum M over the workgroup's tokens
@@ -808,7 +810,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
         const float o1 = (acc[t][2 * e + 1][j] + row_ror8(acc[t][2 * e + 1][j])) * inv;
         w[e] = (int)pack_bf16x2(o0, o1);
       }
-      if (n < nrow) *reinterpret_cast<i32x4*>(stage + n * kD + 32 * r + 8 * j) = w;
+      if (n < nrow) *reinterpret_cast<i32x4*>(stage + n * kStageRow + 2 * (32 * r + 8 * j)) = w;
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
@@ -816,10 +818,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
     uint16_t* out = a.part_o + (row0 + RB + 8 * t) * kD;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int byte = c * 1024 + 16 * lane;
+      const int byte = c * 1024 + 16 * lane;  // of the nrow contiguous 256-byte rows
       if (byte < nbytes)
         *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
-            *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(stage) + byte);
+            *reinterpret_cast<const i32x4*>(stage + (byte >> 8) * kStageRow + (byte & 255));
     }
     if (n < nrow && r == 0) {
       a.part_m[row0 + RB + 8 * t + n] = M * kLn2;
