@@ -26,8 +26,9 @@ def fp8(lens, hk=4, qg=8, seed=0, **kw):
                                num_kv_heads=hk, qg=qg, spare_blocks=5, **kw)
 
 
-def counters_of(ws: torch.Tensor, B: int, hk: int) -> np.ndarray:
-    return ws[:4 * B * hk].view(torch.int32).cpu().numpy()
+def counters_of(ws: torch.Tensor, B: int = 0, hk: int = 0) -> np.ndarray:
+    """The whole fixed counter region at the start of the workspace (256 KiB)."""
+    return ws[:256 << 10].view(torch.int32).cpu().numpy()
 
 
 def sparse_lens(seed=300, B=80):
@@ -101,6 +102,26 @@ def test_workspace_reused_across_sizes():
     got, _ = run_decode(grow, workspace=ws)
     assert_decode_close(got, oracle_decode(grow), "fused reuse, third call")
     assert not counters_of(ws, grow.B, 8).any()
+
+
+@pytest.mark.parametrize("ql,qg,q_dtype", [(1, 32, "bf16"), (1, 48, "f32"), (2, 32, "bf16"),
+                                            (1, 64, "bf16")])
+def test_balanced_row_slices(ql, qg, q_dtype):
+    """Groups of 32-64 rows split over 2 or 4 waves per kv head (row slices, a fourth
+    slice idle at 48 rows) inside balanced slices (the sparse batch at Hk = 4: two
+    workgroups per CU); through the fused step and through decode + reduce."""
+    need_gpu()
+    case = fp8(sparse_lens(360), hk=4, qg=qg, seed=361 + qg + ql, q_dtype=q_dtype,
+               query_len=ql)
+    log(f"case fused balanced row slices ql={ql} qg={qg} q={q_dtype}")
+    ws = uq.alloc_workspace(case.B, 4, ql, qg, 128, case.num_partitions, case.max_seq_len,
+                            case.kv_format)
+    ref = oracle_decode(case)
+    got, _ = run_decode(case, workspace=ws)
+    assert_decode_close(got, ref, f"fused row slices ql={ql} qg={qg}")
+    assert not counters_of(ws).any()
+    split, _ = run_decode(case, mode="split")
+    assert_decode_close(split, ref, f"split row slices ql={ql} qg={qg}")
 
 
 @pytest.mark.parametrize("ql,qg,hk", [(2, 16, 4), (4, 8, 8), (1, 48, 4)])
