@@ -72,6 +72,8 @@
 namespace uq {
 namespace {
 
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kD = 128;
 constexpr int kTiles = 16;     // tiles of 16 tokens per tile-group
 constexpr int kAuxNT = 2;      // KV loads non-temporal (buffer aux bit 1, see below)
@@ -96,15 +98,33 @@ struct FuseUnit {
   int64_t Tt, N;
 };
 
+// 8 e4m3 codes (two words, low byte first) -> 8 f16 (exact)
+__device__ __forceinline__ f16x8 e4m3x8_f16(uint32_t w0, uint32_t w1) {
+  const h16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, false);
+  const h16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w0, 1.0f, true);
+  const h16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, false);
+  const h16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 floats -> 8 f16 (round to nearest even)
+__device__ __forceinline__ f16x8 f32x8_f16(const float (&y)[8]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  h16x2 p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = __builtin_convertvector((f32x2{y[2 * i], y[2 * i + 1]}), h16x2);
+  return f16x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+}
+
 // Output rows of unit rows RB .. RB + 8 T - 1 (those below NR) of sequence b, kv head h
 // set to zero: the flash-combine of a sequence without tokens.
-template <typename QT, int T>
+template <typename QT, int T, int TR = 8>
 __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int lane, const int b,
                                                  const int h, const int RB) {
   const int NR = a.QL * a.QG;
   constexpr int kLanesPerRow = kD * (int)sizeof(QT) / 16;
   constexpr int kRowsPerPass = 64 / kLanesPerRow;
-  const int u_end = RB + 8 * T < NR ? RB + 8 * T : NR;
+  const int u_end = RB + TR * T < NR ? RB + TR * T : NR;
   for (int u0 = RB; u0 < u_end; u0 += kRowsPerPass) {
     const int u = u0 + lane / kLanesPerRow;
     if (u < u_end) {
@@ -129,7 +149,13 @@ __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int 
 // workgroup that share a kv head read the same KV lines, so the loads keep the default
 // cache policy (the sibling waves are served from the caches), and the fused state and
 // counter of the unit are the slice rsi's own.
-template <typename QT, int W, bool TOK, bool HG, int T, bool FUSE = false, bool RSPL = false>
+// F16 (wide groups): row tiles of 16 rows on f16 MFMAs.  The query is one f16 term
+// (exact for bf16, after a per-row power of two), K and V codes are converted to f16
+// exactly once per tile and shared by the row tiles, P is f16: a 16-row tile costs the
+// per-row work of an 8-row e4m3 hi/lo tile, and the K / V handling is paid once for up to
+// 32 rows.
+template <typename QT, int W, bool TOK, bool HG, int T, bool FUSE = false, bool RSPL = false,
+          bool F16 = false>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane, const int wave,
                                             const int b, const int h, const int L,
                                             const int part_first, const int p_end,
@@ -138,6 +164,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
                                             const FuseUnit fz = FuseUnit{}) {
   constexpr int kAux = RSPL ? 0 : kAuxNT;  // cache policy of the KV loads
   static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
+  static_assert(!F16 || HG, "f16 row tiles are built on head groups");
+  constexpr int kTR = F16 ? 16 : 8;  // rows per row tile
   // staging of the merged partition's bf16 output rows (8 rows of 256 bytes per tile, one
   // tile at a time; one stage per wave with head groups; fused: rows of the query dtype),
   // and the states of waves 1..W-1 handed to wave 0 (per lane and tile: 32 accumulators,
@@ -146,13 +174,14 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   // stage rows: 8 output rows of the query dtype (fused) or bf16, padded by 16 bytes so
   // that the 16 rows a b128 store instruction touches start in different banks
   constexpr int kStageRow = (FUSE ? (int)sizeof(QT) : 2) * kD + 16;  // bytes
-  constexpr int kStageBytes = 8 * kStageRow;
+  constexpr int kStageBytes = kTR * kStageRow;
   __shared__ __attribute__((aligned(16))) uint8_t o_stage[(HG ? W : 1) * kStageBytes];
   __shared__ __attribute__((aligned(16))) float st_acc[kMerge ? W - 1 : 1][T][32][64];
   __shared__ float st_ml[kMerge ? W - 1 : 1][T][3][64];
   const int r = lane >> 4, n = lane & 15;
   const int g = n & 7;
   const bool lo_col = n >= 8;
+  const int crow = F16 ? n : g;  // this lane's row within a row tile
 
   // ---- query operands.  Byte j of lane group r holds head dim d = 32 r + j (the K
   //      operand's map after the chunk exchange).  Column g of tile t holds unit row
@@ -162,12 +191,13 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   // per-tensor scales (the per-token ones are applied per token below)
   const float k_scale = (!TOK && a.k_scale) ? *a.k_scale : 1.f;
   const float v_scale = (!TOK && a.v_scale) ? *a.v_scale : 1.f;
-  i32x8 q_own[T];  // hi(q s_q) in columns 0-7, lo(q s_q) in columns 8-15
+  i32x8 q_own[F16 ? 1 : T];  // hi(q s_q) in columns 0-7, lo(q s_q) in columns 8-15
+  f16x8 q16[F16 ? T : 1][4];  // F16: q s_q, dims 32 r + 8 s .. + 7 for MFMA k-step s
   float qk_mul[T];
   int L_row[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int urow = RB + 8 * t + g;
+    const int urow = RB + kTR * t + crow;
     const bool qvalid = urow < NR;
     const int qj = qvalid ? urow / a.QG : 0, qh = qvalid ? urow % a.QG : 0;
     L_row[t] = L - a.QL + 1 + qj;
@@ -197,6 +227,25 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
     amax = max_across_rows(amax);
+    if constexpr (F16) {
+      // s_q = 2^(15 - E) with amax = f 2^E, f in [0.5, 1): amax * s_q in [2^14, 2^15), every
+      // bf16 element above 2^-24 / s_q exact in f16
+      int E = 0;
+      if (amax > 0.f) {
+        E = (int)((f_bits(amax) >> 23) & 0xFF) - 126;
+        E = E < -100 ? -100 : E;
+      }
+      const float s_q = bits_f((uint32_t)(127 + 15 - E) << 23);
+      qk_mul[t] = a.softmax_scale * k_scale * kLog2e / s_q;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = qvalid ? x[8 * st + e] * s_q : 0.f;
+        q16[F16 ? t : 0][st] = f32x8_f16(y);
+      }
+      continue;
+    }
     // s_q = 2^(7 - E) with amax = f 2^E, f in [0.5, 1): amax * s_q in [64, 128)
     int E = 0;
     if (amax > 0.f) {
@@ -215,7 +264,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       lw = cvt_pk_e4m3<true>(y2 - e4m3_to_f<2>(hw), y3 - e4m3_to_f<3>(hw), lw);
       hw = qvalid ? hw : 0;
       lw = qvalid ? lw : 0;
-      q_own[t][w] = lo_col ? lw : hw;
+      q_own[F16 ? 0 : t][w] = lo_col ? lw : hw;
     }
   }
 
@@ -230,6 +279,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
   // the VALU from the unscaled weights (l_run, per lane).
   constexpr bool kSumByMfma = !TOK;
   constexpr long kOnesE4m3x8 = 0x3838383838383838L;  // e4m3 1.0 in every byte
+  const f16x8 kOnesF16x8 = {1, 1, 1, 1, 1, 1, 1, 1};
   f32x4 lacc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
@@ -415,15 +465,32 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
         }
         float ksq[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (TOK) quad_values(ksc[pr & 1][tt], ksq);  // K scales of tokens 4r..4r+3
+        if constexpr (F16) {
+          // k-step st: dims 32 r + 8 st .. + 7 of token n (bytes 8 st .. of its chunk pair)
+          f16x8 kf[4];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own[t], z, 0, 0, 0, 127, 0,
-                                                                127);
+          for (int st = 0; st < 4; ++st)
+            kf[st] = e4m3x8_f16((uint32_t)kop[2 * st], (uint32_t)kop[2 * st + 1]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float mul = TOK ? ksq[j] * qk_mul[t] : qk_mul[t];
-            s[t][tt][j] = (z[j] + row_ror8(z[j])) * mul;
+          for (int t = 0; t < T; ++t) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+              z = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[st], q16[F16 ? t : 0][st], z, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s[t][tt][j] = z[j] * (TOK ? ksq[j] * qk_mul[t] : qk_mul[t]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, q_own[F16 ? 0 : t], z, 0, 0,
+                                                                  0, 127, 0, 127);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float mul = TOK ? ksq[j] * qk_mul[t] : qk_mul[t];
+              s[t][tt][j] = (z[j] + row_ror8(z[j])) * mul;
+            }
           }
         }
       }
@@ -500,11 +567,28 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
           v_inv = 1.f / vmx;
         }
       }
-      long pop[T];
+      long pop[F16 ? 1 : T];
+      f16x8 p16[F16 ? T : 1];  // F16: P of tokens (tile 0: 4r..4r+3, tile 1: 16+4r..) x row n
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         // a row that has seen no token (m_run = -inf) has only -inf scores: weight 0
         const float m8 = m_run[t] == -INFINITY ? 0.f : m_run[t] - 8.f;
+        if constexpr (F16) {
+          float y[8];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float v = fast_exp2(s[t][tt][j] - m8);
+              if constexpr (!kSumByMfma) l_run[t] += v;
+              if constexpr (TOK) v *= vq[tt][j] * v_inv;
+              y[4 * tt + j] = v;
+            }
+          p16[F16 ? t : 0] = f32x8_f16(y);
+          if constexpr (kSumByMfma) lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              kOnesF16x8, p16[F16 ? t : 0], lacc[t], 0, 0, 0);
+          continue;
+        }
         int pw[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -518,11 +602,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
           // the score is dead once exponentiated: its register seeds the code word
           pw[tt] = e4m3_hilo_word(y[0], y[1], y[2], y[3], lo_col, (int)f_bits(s[t][tt][0]));
         }
-        pop[t] = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
+        pop[F16 ? 0 : t] = (long)(uint32_t)pw[0] | ((long)(uint32_t)pw[1] << 32);
         // the row sums of P as the PV MFMA sees them (hi + lo columns, combined after
         // the stream): one MFMA against a block of ones instead of 8 VALU additions
         if constexpr (kSumByMfma) lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-            kOnesE4m3x8, pop[t], lacc[t], 0, 0, 0);
+            kOnesE4m3x8, pop[F16 ? 0 : t], lacc[t], 0, 0, 0);
       }
 
       // ---- V^T: exchange halves with the neighbouring lane, then byte-transpose 8 dims
@@ -556,10 +640,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       // ---- PV: acc[t][m][j'] holds O^T[d = 32 r' + 8 j' + m][column n'] of row tile t
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const long vop = (long)vtr[0][m] | ((long)vtr[1][m] << 32);
+        if constexpr (F16) {
+          const f16x8 vf = e4m3x8_f16(vtr[0][m], vtr[1][m]);
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-          acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop[t], acc[t][m], 0, 0, 0);
+          for (int t = 0; t < T; ++t)
+            acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, p16[F16 ? t : 0], acc[t][m], 0,
+                                                              0, 0);
+        } else {
+          const long vop = (long)vtr[0][m] | ((long)vtr[1][m] << 32);
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(vop, pop[F16 ? 0 : t], acc[t][m],
+                                                                   0, 0, 0);
+        }
       }
     }
 
@@ -571,7 +664,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     m_true[t] = max_across_rows(m_true[t]);
-    if constexpr (kSumByMfma) l_sum[t] = lacc[t][0] + row_ror8(lacc[t][0]);
+    if constexpr (kSumByMfma) l_sum[t] = F16 ? lacc[t][0] : lacc[t][0] + row_ror8(lacc[t][0]);
     else l_sum[t] = sum_across_rows(l_run[t]);
   }
 
@@ -698,7 +791,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
     constexpr int kRowBytes = kD * (int)sizeof(QT);
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int nrow = NR - RB - 8 * t < 8 ? NR - RB - 8 * t : 8;
+      const int nrow = NR - RB - kTR * t < kTR ? NR - RB - kTR * t : kTR;
       if (nrow <= 0) break;  // wave-uniform
       const float inv = v_scale / (lsum[t] > 0.f ? lsum[t] : 1.f);
       if (t > 0) {
@@ -709,7 +802,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       for (int j = 0; j < 4; ++j) {
         float o[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) o[m] = (acc[t][m][j] + row_ror8(acc[t][m][j])) * inv;
+        for (int m = 0; m < 8; ++m)
+          o[m] = (F16 ? acc[t][m][j] : acc[t][m][j] + row_ror8(acc[t][m][j])) * inv;
         uint8_t* row = stage + n * kStageRow;
         if (n < nrow) {
           if constexpr (sizeof(QT) == 4) {
@@ -727,10 +821,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       constexpr int kLanesPerRow = kRowBytes / 16;
       constexpr int kRowsPerPass = 64 / kLanesPerRow;
 #pragma unroll
-      for (int c = 0; c < 8 / kRowsPerPass; ++c) {
+      for (int c = 0; c < kTR / kRowsPerPass; ++c) {
         const int i = c * kRowsPerPass + lane / kLanesPerRow;  // stage row
         if (i < nrow) {
-          const int urow = RB + 8 * t + i;
+          const int urow = RB + kTR * t + i;
           QT* dst = reinterpret_cast<QT*>(a.out) + ((int64_t)b * a.QL + urow / a.QG) * a.o_ss +
                     (int64_t)(h * a.QG + urow % a.QG) * a.o_sh;
           const int chunk = lane % kLanesPerRow;
@@ -790,8 +884,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       }
     }
     const float inv = v_scale / (l_all > 0.f ? l_all : 1.f);
-    // rows RB + 8t .. RB + 8t + nrow - 1 of this partition's partial
-    const int nrow = NR - RB - 8 * t < 8 ? NR - RB - 8 * t : 8;
+    // rows RB + kTR t .. RB + kTR t + nrow - 1 of this partition's partial
+    const int nrow = NR - RB - kTR * t < kTR ? NR - RB - kTR * t : kTR;
     if (nrow <= 0) break;  // wave-uniform
     // Every lane joins the DPP exchange (lanes of the lo columns feed the hi columns).
     // The bf16 rows go through LDS so that the partial is written with whole-line
@@ -806,8 +900,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
       i32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float o0 = (acc[t][2 * e][j] + row_ror8(acc[t][2 * e][j])) * inv;
-        const float o1 = (acc[t][2 * e + 1][j] + row_ror8(acc[t][2 * e + 1][j])) * inv;
+        const float o0 =
+            (F16 ? acc[t][2 * e][j] : acc[t][2 * e][j] + row_ror8(acc[t][2 * e][j])) * inv;
+        const float o1 =
+            (F16 ? acc[t][2 * e + 1][j] : acc[t][2 * e + 1][j] + row_ror8(acc[t][2 * e + 1][j])) *
+            inv;
         w[e] = (int)pack_bf16x2(o0, o1);
       }
       if (n < nrow) *reinterpret_cast<i32x4*>(stage + n * kStageRow + 2 * (32 * r + 8 * j)) = w;
@@ -815,23 +912,23 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
     const int nbytes = nrow * kD * 2;  // contiguous partial rows of this tile
-    uint16_t* out = a.part_o + (row0 + RB + 8 * t) * kD;
+    uint16_t* out = a.part_o + (row0 + RB + kTR * t) * kD;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < kTR / 4; ++c) {
       const int byte = c * 1024 + 16 * lane;  // of the nrow contiguous 256-byte rows
       if (byte < nbytes)
         *reinterpret_cast<i32x4*>(reinterpret_cast<uint8_t*>(out) + byte) =
             *reinterpret_cast<const i32x4*>(stage + (byte >> 8) * kStageRow + (byte & 255));
     }
     if (n < nrow && r == 0) {
-      a.part_m[row0 + RB + 8 * t + n] = M * kLn2;
-      a.part_l[row0 + RB + 8 * t + n] = l_all;
+      a.part_m[row0 + RB + kTR * t + n] = M * kLn2;
+      a.part_l[row0 + RB + kTR * t + n] = l_all;
     }
   }
   // the workgroup's other partitions that hold tokens: empty states
   for (int pe = part_first + 1 + r; pe < p_end; pe += 4) {
     const int64_t prow = (((int64_t)b * a.Hk + h) * a.P + pe) * NR;
-    const int u_end = RB + 8 * T < NR ? RB + 8 * T : NR;
+    const int u_end = RB + kTR * T < NR ? RB + kTR * T : NR;
     for (int u = RB + n; u < u_end; u += 16) {
       a.part_m[prow + u] = -INFINITY;
       a.part_l[prow + u] = 0.f;
@@ -851,24 +948,27 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 //     blocks together.
 //   Otherwise: workgroup = (kv head, sequence, group of W runs) with the W runs split over
 //     the waves and merged in LDS.
-template <typename QT, int W, bool TOK, bool HG, int T, bool BAL, bool FUSE, bool RSPL>
+template <typename QT, int W, bool TOK, bool HG, int T, bool BAL, bool FUSE, bool RSPL,
+          bool F16>
 __global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8_kernel(
     DecodeArgs a) {
   static_assert(!BAL || HG, "balanced slices are built on head groups");
   static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
   static_assert(!RSPL || HG, "row slices are built on head groups");
+  static_assert(!F16 || (HG && T == 2), "f16 row tiles: head groups, two tiles");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t item = blockIdx.x;
-  // Row slices (RSPL): the W waves take W / RS kv heads x RS slices of 16 rows each (wave
-  // w: head w / RS, rows 16 (w % RS) ..); otherwise W heads (head groups) or one.
+  // Row slices (RSPL): the W waves take W / RS kv heads x RS slices of the rows (16 each,
+  // or 32 with f16 row tiles; wave w: head w / RS, slice w % RS); otherwise W heads (head
+  // groups) or one.
   const int RS = RSPL ? a.row_splits : 1;
   const int HPW = HG ? W / RS : 1;  // kv heads per workgroup
   const int rsi = RSPL ? wave % RS : 0;
-  const int RB = a.row_base + 16 * rsi;
+  const int RB = a.row_base + (F16 ? 32 : 16) * rsi;
   const int hw = RSPL ? wave / RS : wave;  // this wave's head within the workgroup
-  // a slice past the group's rows (33..48 rows in 4 slices): nothing to compute or write;
-  // head-group waves never synchronise, so the wave may leave at once
+  // a slice past the group's rows: nothing to compute or write; head-group waves never
+  // synchronise, so the wave may leave at once
   if (RSPL && RB >= a.QL * a.QG) return;
   const int nhs = HG ? a.Hk / HPW : a.Hk;
   if constexpr (BAL) {
@@ -911,7 +1011,8 @@ __global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8
       auto zero_empty = [&]() {
         if constexpr (FUSE) {
           for (int64_t bz = slice; bz < a.B; bz += N)
-            if (parts_of((int)bz) == 0) zero_output_rows<QT, T>(a, lane, (int)bz, hh, RB);
+            if (parts_of((int)bz) == 0)
+              zero_output_rows<QT, T, F16 ? 16 : 8>(a, lane, (int)bz, hh, RB);
         }
       };
       if (s0 >= s1) {  // workgroup-uniform
@@ -956,8 +1057,8 @@ __global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8
           fz.Tt = Tt;
           fz.N = N;
         }
-        decode_unit<QT, W, TOK, HG, T, FUSE, RSPL>(a, lane, wave, bb, hh, Lb, p_lo, p_lo + take,
-                                                   p_lo, take, 1, RB, rsi, fz);
+        decode_unit<QT, W, TOK, HG, T, FUSE, RSPL, F16>(a, lane, wave, bb, hh, Lb, p_lo,
+                                                        p_lo + take, p_lo, take, 1, RB, rsi, fz);
         left -= take;
         e += take;
       }
@@ -984,7 +1085,7 @@ __global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8
   if constexpr (FUSE) {
     // a sequence without tokens: zero output rows from the first workgroup of its heads
     if (pmax == 0) {
-      if (grp == 0) zero_output_rows<QT, T>(a, lane, b, h, RB);
+      if (grp == 0) zero_output_rows<QT, T, F16 ? 16 : 8>(a, lane, b, h, RB);
       return;
     }
   }
@@ -1044,8 +1145,8 @@ __global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8
     fz.Tt = 0;
     fz.N = 1;
   }
-  decode_unit<QT, W, TOK, HG, T, FUSE, RSPL>(a, lane, wave, b, h, L, part_first, p_end,
-                                             first_tg, n_tg, step, RB, rsi, fz);
+  decode_unit<QT, W, TOK, HG, T, FUSE, RSPL, F16>(a, lane, wave, b, h, L, part_first, p_end,
+                                                  first_tg, n_tg, step, RB, rsi, fz);
 }
 
 }  // namespace
@@ -1054,14 +1155,15 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
                              hipStream_t stream) {
   constexpr int W = 4;
   const bool hg = a.head_groups != 0;
-  // row tiles of 8 query rows, 1 or 2 per wave (4 tiles per wave would spill); wider
-  // groups either split their rows over the waves of a workgroup (row_splits, one launch)
-  // or run in passes of 16 rows, each reading the KV stream once
+  // Row tiles: e4m3 hi/lo tiles of 8 rows, 1 or 2 per wave, up to 16 rows; head groups
+  // with more rows take f16 tiles of 16 rows, two per wave (32 rows), and split wider
+  // groups over 2 waves of a workgroup (row slices, one launch).  Without head groups a
+  // wider group runs in passes of 16 rows, each reading the KV stream once.
   const int rows = a.QL * a.QG;
   if (rows > 64) return hipErrorInvalidValue;
+  const bool f16 = hg && rows > 16;
   const int RS = a.row_splits > 1 ? a.row_splits : 1;
-  if (RS > 1 && (!hg || (RS != 2 && RS != 4) || rows <= 16 || rows > 16 * RS))
-    return hipErrorInvalidValue;
+  if (RS != (f16 && rows > 32 ? 2 : 1)) return hipErrorInvalidValue;
   const int HPW = hg ? W / RS : 1;  // kv heads per workgroup
   if (hg && a.Hk % HPW != 0) return hipErrorInvalidValue;
   // balanced slices hold up to 16 sequence lengths per lane
@@ -1088,36 +1190,46 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   auto pick = [&](auto qt, auto tok, const DecodeArgs& p) {
     using QT = decltype(qt);
     constexpr bool TOK = decltype(tok)::value;
-    if (RS > 1) {  // two row tiles, head groups
-      if (bal) {
-        if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, true>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, true>, p);
+    if (f16) {  // f16 row tiles (two per wave), head groups
+      if (RS > 1) {
+        if (bal) {
+          if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, true, true>, p);
+          else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, true, true>, p);
+        } else {
+          if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, true, true>, p);
+          else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, true, true>, p);
+        }
       } else {
-        if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, true>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, true>, p);
+        if (bal) {
+          if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, false, true>, p);
+          else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, false, true>, p);
+        } else {
+          if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, false, true>, p);
+          else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, false, true>, p);
+        }
       }
     } else if (bal) {
       if (fuse) {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, true, false>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, false>, p);
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, true, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, false, false>, p);
       } else {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, false, false>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, false>, p);
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, false, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, true, false, false, false>, p);
       }
     } else if (hg) {
       if (fuse) {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, true, false>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, false>, p);
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, true, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, true, false, false>, p);
       } else {
-        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, false, false>, p);
-        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, false>, p);
+        if (T == 1) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, false, false, false>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 2, false, false, false, false>, p);
       }
     } else {
-      if (T == 1) go(decode_fp8_kernel<QT, W, TOK, false, 1, false, false, false>, p);
-      else go(decode_fp8_kernel<QT, W, TOK, false, 2, false, false, false>, p);
+      if (T == 1) go(decode_fp8_kernel<QT, W, TOK, false, 1, false, false, false, false>, p);
+      else go(decode_fp8_kernel<QT, W, TOK, false, 2, false, false, false, false>, p);
     }
   };
-  const int pass_rows = 16 * RS;
+  const int pass_rows = f16 ? 32 * RS : 16;
   for (int rb = 0; rb < rows; rb += pass_rows) {
     DecodeArgs p = a;
     p.row_base = rb;

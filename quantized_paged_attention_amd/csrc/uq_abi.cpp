@@ -127,7 +127,7 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len, int rows) {
     // QG=32: passes of 16 rows 915 us, row slices with one workgroup per unit 837 us,
     // with two 666 us; QG=64: 1836 / 1631 / 1160 us.  QG=16 (one wave per head) stays
     // at one workgroup per unit: 451 us, two per unit 465 us.
-    const int RS = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    const int RS = rows <= 32 ? 1 : 2;
     const int HPW = 4 / RS;
     if (Hk % HPW == 0) {
       p.head_groups = 1;
