@@ -107,15 +107,17 @@ enum { UQ_KV_FP8_E4M3 = 0, UQ_KV_FP4_E2M1_E4M3S = 1, UQ_KV_FP4_E2M1_UE8M0S = 2,
  * partitions into the first of them (m, l, o of their union) and write the others of the
  * set as empty (m = -inf, l = 0, o rows left unwritten).  Combining all written states
  * with uq_paged_reduce gives the attention output either way.  The kernels merge the
- * run of consecutive partitions streamed for one kv head by one wave (fp8 with
- * num_kv_heads a multiple of 4) or by one workgroup (otherwise); the run length is
+ * run of consecutive partitions streamed for one kv head by one wave (fp8 with head
+ * groups: num_kv_heads a multiple of 4, or of 2 for groups of 33-64 rows) or by one
+ * workgroup (otherwise); the run length is
  * chosen by the launcher from the problem size and the device's compute units.
  * With num_partitions = 1 part_* hold exactly the statistics above.
  * Supported: (UQ_KV_FP8_E4M3 or UQ_KV_FP8_E4M3_TOKSCALE, D = 128, QG <= 64) and
  * (UQ_KV_FP4_E2M1_E4M3S or UQ_KV_FP4_E2M1_UE8M0S, D = 256, QG <= 16); anything else
  * returns UQ_ERR_UNSUPPORTED ([P3] wide GQA: groups above 16 rows).  The fp8 kernels
- * carry up to 16 query rows per kv head in one pass over the cache; a wider group runs
- * one pass per 16 rows.  QG > 64 returns UQ_ERR_INVALID_ARG.
+ * read the cache once per kv head for all its query rows with head groups (up to 32
+ * rows per wave, 33-64 rows on two waves of a workgroup); without head groups a group
+ * wider than 16 rows runs one pass per 16 rows.  QG > 64 returns UQ_ERR_INVALID_ARG.
  * Device preconditions: 0 <= seq_lens[b] <= max_seq_len (larger values are clamped to
  * max_seq_len); block_table[b][t / block_size] in [0, num_blocks) for every t < L_b;
  * entries past a sequence's last block are never read; slot bytes of tokens t >= L_b are
@@ -201,7 +203,7 @@ int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float
  *                   strides o_stride_seq / o_stride_head (> 0, 16-byte multiples; the head
  *                   dim is contiguous, out 16-byte aligned).
  * How it runs: with the fp8 formats and head groups (num_kv_heads a multiple of 4, or of
- * 2 / 1 for groups of 17-32 / 33-64 rows) one launch; every work unit of a (sequence, kv
+ * 2 for groups of 33-64 rows) one launch; every work unit of a (sequence, kv
  * head) that does not cover the whole sequence leaves its softmax state in the workspace
  * and counts its partitions with a device-scope atomic, and the unit that completes the
  * count merges the states and writes the output rows.  Other formats and head counts run

@@ -24,12 +24,16 @@
 //     cost far more than their bytes (88 MB of partials: +90 us on a 480 us stream);
 //     the same stores kept L2-resident cost ~4 us.  With non-temporal KV loads and whole
 //     runs merged into one partial, the partials stay in L2 until the kernel ends.
-//   * Query rows are carried as T tiles of 8 MFMA columns (T = 1 or 2); the K/V loads,
-//     the K operand and the V^T transpose are shared by the tiles, each tile has its own
-//     query operand, softmax state and accumulators.  Wider groups (head groups) split
-//     their rows over 2 or 4 waves of a workgroup that stream the same kv head (row
-//     slices: the KV bytes come from HBM once and from the caches for the sibling
-//     waves); otherwise they run one launch per 16 rows.
+//   * Query rows are carried as T row tiles (T = 1 or 2); the K/V loads, the K operand
+//     and the V^T transpose are shared by the tiles, each tile has its own query
+//     operand, softmax state and accumulators.  Up to 8 rows: one e4m3 hi/lo tile of 8
+//     rows (below).  Head groups of 9-32 rows: f16 tiles of 16 rows (one or two), 33-64
+//     rows: two waves of a workgroup stream the same kv head with 32 rows each (row
+//     slices: the KV bytes come from HBM once and from the caches for the sibling wave).
+//     Without head groups, e4m3 tiles up to 16 rows and one launch per 16 rows beyond.
+//     B=128, Hk=8, L ~ U[4k, 16k], fused step on MI355X: 8 rows 413 us; 16 rows 435 us
+//     as two e4m3 tiles, 417 us as one f16 tile; 32 rows 658 us as e4m3 row slices, 454
+//     us as two f16 tiles; 64 rows 1108 / 688 us.
 //   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
 //     from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query group as an
 //     e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
@@ -136,8 +140,8 @@ __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int 
   }
 }
 
-// T: tiles of 8 query rows (QL x QG <= 8 T) from unit row RB on.  The K/V stream, the K operand and the V^T
-// transpose are shared by the tiles; each tile has its own query operand, softmax state,
+// T: row tiles of 8 query rows (16 with F16; QL x QG <= 8 T or 16 T) from unit row RB on.
+// The K/V stream, the K operand and the V^T transpose are shared by the tiles; each tile has its own query operand, softmax state,
 // accumulators, QK MFMA and PV MFMAs (the pages' M-tiles for wide groups).
 // One work unit of a wave: kv head h of sequence b (length L, already clamped), the
 // tile-groups first_tg, first_tg + step, ... (n_tg of them) of the partitions
@@ -152,8 +156,8 @@ __device__ __forceinline__ void zero_output_rows(const DecodeArgs& a, const int 
 // F16 (wide groups): row tiles of 16 rows on f16 MFMAs.  The query is one f16 term
 // (exact for bf16, after a per-row power of two), K and V codes are converted to f16
 // exactly once per tile and shared by the row tiles, P is f16: a 16-row tile costs the
-// per-row work of an 8-row e4m3 hi/lo tile, and the K / V handling is paid once for up to
-// 32 rows.
+// MFMA work of an 8-row e4m3 hi/lo tile and needs no hi/lo combine, and the K / V
+// conversion is paid once for up to 32 rows.
 template <typename QT, int W, bool TOK, bool HG, int T, bool FUSE = false, bool RSPL = false,
           bool F16 = false>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane, const int wave,
@@ -950,12 +954,12 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
 //     the waves and merged in LDS.
 template <typename QT, int W, bool TOK, bool HG, int T, bool BAL, bool FUSE, bool RSPL,
           bool F16>
-__global__ __launch_bounds__(64 * W, T == 1 ? (BAL ? 1 : 3) : 2) void decode_fp8_kernel(
+__global__ __launch_bounds__(64 * W, T == 1 && !F16 ? (BAL ? 1 : 3) : (BAL && F16 && T == 1 ? 1 : 2)) void decode_fp8_kernel(
     DecodeArgs a) {
   static_assert(!BAL || HG, "balanced slices are built on head groups");
   static_assert(!FUSE || HG, "the fused flash-combine is built on head groups");
   static_assert(!RSPL || HG, "row slices are built on head groups");
-  static_assert(!F16 || (HG && T == 2), "f16 row tiles: head groups, two tiles");
+  static_assert(!F16 || HG, "f16 row tiles are built on head groups");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t item = blockIdx.x;
@@ -1155,20 +1159,21 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
                              hipStream_t stream) {
   constexpr int W = 4;
   const bool hg = a.head_groups != 0;
-  // Row tiles: e4m3 hi/lo tiles of 8 rows, 1 or 2 per wave, up to 16 rows; head groups
-  // with more rows take f16 tiles of 16 rows, two per wave (32 rows), and split wider
-  // groups over 2 waves of a workgroup (row slices, one launch).  Without head groups a
-  // wider group runs in passes of 16 rows, each reading the KV stream once.
+  // Row tiles: up to 8 rows, one e4m3 hi/lo tile of 8 rows; head groups with 9-32 rows
+  // take one or two f16 tiles of 16 rows, and split 33-64 rows over 2 waves of a
+  // workgroup (row slices, one launch).  Without head groups, e4m3 tiles up to 16 rows,
+  // and a wider group runs in passes of 16 rows, each reading the KV stream once.
   const int rows = a.QL * a.QG;
   if (rows > 64) return hipErrorInvalidValue;
-  const bool f16 = hg && rows > 16;
+  const bool f16 = hg && rows > 8;
   const int RS = a.row_splits > 1 ? a.row_splits : 1;
   if (RS != (f16 && rows > 32 ? 2 : 1)) return hipErrorInvalidValue;
   const int HPW = hg ? W / RS : 1;  // kv heads per workgroup
   if (hg && a.Hk % HPW != 0) return hipErrorInvalidValue;
   // balanced slices hold up to 16 sequence lengths per lane
   if (a.balanced_items > 0 && (!hg || a.B > 1024)) return hipErrorInvalidValue;
-  const int T = rows <= 8 ? 1 : 2;
+  // tiles per wave: e4m3 up to 8 rows in one tile, 16 in two; f16 up to 16 rows in one
+  const int T = f16 ? (rows <= 16 ? 1 : 2) : (rows <= 8 ? 1 : 2);
   const bool fuse = a.fused != 0;
   if (fuse && (!hg || !a.out || !a.counters || !a.states || a.state_tiles != T))
     return hipErrorInvalidValue;
@@ -1190,7 +1195,15 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, bool q_is_f32, bool tok_scales
   auto pick = [&](auto qt, auto tok, const DecodeArgs& p) {
     using QT = decltype(qt);
     constexpr bool TOK = decltype(tok)::value;
-    if (f16) {  // f16 row tiles (two per wave), head groups
+    if (f16 && T == 1) {  // one f16 row tile (9-16 rows), head groups
+      if (bal) {
+        if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 1, true, true, false, true>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 1, true, false, false, true>, p);
+      } else {
+        if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 1, false, true, false, true>, p);
+        else go(decode_fp8_kernel<QT, W, TOK, true, 1, false, false, false, true>, p);
+      }
+    } else if (f16) {  // f16 row tiles (two per wave), head groups
       if (RS > 1) {
         if (bal) {
           if (fuse) go(decode_fp8_kernel<QT, W, TOK, true, 2, true, true, true, true>, p);

@@ -85,7 +85,7 @@ struct Plan {
   int TGPP;            // tile-groups per partition
   int run_len, runs;   // partitions per work item (0: one partition, strided tile-groups)
   int head_groups;     // fp8: workgroups of 4 / row_splits neighbouring kv heads
-  int row_splits;      // fp8 head groups: waves per kv head (16 query rows each)
+  int row_splits;      // fp8 head groups: waves per kv head (up to 32 query rows each)
   int balanced_items;  // fp8 head groups: slices per head group (0: runs per sequence)
 };
 
@@ -119,14 +119,15 @@ Plan plan_decode(int fmt, int B, int Hk, int P, int max_seq_len, int rows) {
     // lengths.  Measured on MI355X (fp8, Hk=8, 64 partitions): B=16, L=16k: run 8
     // (256 workgroups) 86 us, runs 4 / 6 / 16: 89 / 102 / 129 us; B=128, L ~ U[4k, 16k]:
     // run 11 472 us, runs 8 / 16 / 22: 482 / 494 / 506 us.
-    //   Wider query groups (more than 16 rows) split their rows over RS = 2 or 4 waves
-    // of a workgroup (4 / RS kv heads each): one launch reads the KV stream once from
-    // HBM, the sibling waves of a head hit the caches, and balanced slices put two
-    // workgroups on each compute unit (a wave is latency-bound, so a unit needs four kv
-    // heads in flight).  Measured on MI355X (B=128, Hk=8, L ~ U[4k, 16k], decode):
-    // QG=32: passes of 16 rows 915 us, row slices with one workgroup per unit 837 us,
-    // with two 666 us; QG=64: 1836 / 1631 / 1160 us.  QG=16 (one wave per head) stays
-    // at one workgroup per unit: 451 us, two per unit 465 us.
+    //   A wave carries up to 32 query rows (two f16 tiles of 16 rows).  Wider groups
+    // split their rows over RS = 2 waves of a workgroup (2 kv heads each): one launch
+    // reads the KV stream once from HBM, the sibling wave of a head hits the caches, and
+    // balanced slices put two workgroups on each compute unit (a wave is latency-bound,
+    // so a unit needs four kv heads in flight).  Measured on MI355X (B=128, Hk=8,
+    // L ~ U[4k, 16k], fused step): QG=32 454 us with one workgroup per unit, 476 us with
+    // two; QG=64 688 us either way.  Before the f16 tiles (e4m3 tiles of 8 rows, 16 rows
+    // per wave): QG=32 as passes of 16 rows 915 us, 2 row slices with two workgroups per
+    // unit 658 us; QG=64 1836 / 1108 us (4 row slices).
     const int RS = rows <= 32 ? 1 : 2;
     const int HPW = 4 / RS;
     if (Hk % HPW == 0) {
@@ -208,7 +209,7 @@ AttnLayout attn_layout(int fmt, int B, int Hk, int QL, int QG, int D, int P, int
   l.fused = (fmt == UQ_KV_FP8_E4M3 || fmt == UQ_KV_FP8_E4M3_TOKSCALE) && p.head_groups &&
             (size_t)B * Hk * RS * 4 <= kCounterBytes;
   if (l.fused) {
-    l.tiles = rows <= 8 ? 1 : 2;
+    l.tiles = rows <= 16 ? 1 : 2;  // e4m3 tiles of 8 rows up to 8, f16 tiles of 16 above
     // balanced slices: unit (b, slice s) uses slot s + b; runs: unit (b, run g) slot
     // b * runs + g
     l.slots = p.balanced_items > 0 ? (int64_t)p.balanced_items + B - 1 : (int64_t)B * p.runs;

@@ -117,6 +117,22 @@ def oracle_decode(case, P=0):
                          v_scale_tok=case.v_scale_tok)
 
 
+def oracle_decode_seqs(case, idx):
+    """The oracle on the sequences idx only (all their query rows and heads): rows
+    b * query_len + i of the output for b in idx, in that order."""
+    from oracle import oracle
+    idx = np.asarray(idx)
+    QL = case.query_len
+    rows = (idx[:, None] * QL + np.arange(QL)[None, :]).reshape(-1)
+    ref = oracle.decode(case.q[rows], case.cache, case.block_table[idx], case.seq_lens[idx],
+                        num_kv_heads=case.num_kv_heads, kv_format=case.kv_format,
+                        softmax_scale=case.softmax_scale, k_scale=case.k_scale,
+                        v_scale=case.v_scale, rot_signs=case.rot_signs, num_partitions=0,
+                        query_len=QL, k_scale_tok=case.k_scale_tok,
+                        v_scale_tok=case.v_scale_tok)
+    return rows, ref
+
+
 def rel_err(got, ref):
     scale = np.abs(ref).max()
     return float(np.abs(got - ref).max() / (scale if scale > 0 else 1.0))

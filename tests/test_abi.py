@@ -245,14 +245,20 @@ def test_attention_workspace_bytes(lib):
     """A fixed 256 KiB counter region, then the fused states (fp8 head groups) or the
     decode partials.  With no GPU the planner assumes 256 compute units: the fp8
     high-batch shape takes balanced slices, 128 per head group, so 128 + 127 state slots
-    of one row tile; with QG=32 two row slices per head and two workgroups per unit."""
+    of one row tile (8 rows of e4m3 codes, or 16 rows in f16 at QG=16); QG=32 takes two
+    16-row tiles per state; QG=64 two row slices per kv head (four head groups of two
+    heads, two workgroups per compute unit: still 128 slices per group)."""
     up = lambda x: (x + 255) // 256 * 256
     counters = 256 << 10
     state = 8 * 64 * 16 + 2 * 64 * 4
     n = uq.attention_workspace_bytes(128, 8, 1, 8, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
     assert n == counters + up(255 * 8 * 1 * state)
+    n = uq.attention_workspace_bytes(128, 8, 1, 16, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
+    assert n == counters + up(255 * 8 * 1 * state)
     n = uq.attention_workspace_bytes(128, 8, 1, 32, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
-    assert n == counters + up((128 + 127) * 8 * 2 * 2 * state)
+    assert n == counters + up(255 * 8 * 2 * state)
+    n = uq.attention_workspace_bytes(128, 8, 1, 64, 128, 64, 16384, uq.UQ_KV_FP8_E4M3)
+    assert n == counters + up(255 * 8 * 2 * 2 * state)
     # fp8 with an odd head count and fp4: decode partials after the counters
     for fmt, hk, D in ((uq.UQ_KV_FP8_E4M3, 3, 128), (uq.UQ_KV_FP4_E2M1_E4M3S, 2, 256)):
         n = uq.attention_workspace_bytes(4, hk, 2, 8, D, 512, 75000, fmt)

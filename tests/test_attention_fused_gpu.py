@@ -45,8 +45,11 @@ def sparse_lens(seed=300, B=80):
     return lens
 
 
-@pytest.mark.parametrize("qg,q_dtype", [(8, "bf16"), (8, "f32"), (16, "bf16"), (5, "f32")])
+@pytest.mark.parametrize("qg,q_dtype", [(8, "bf16"), (8, "f32"), (16, "bf16"), (5, "f32"),
+                                        (12, "f32")])
 def test_balanced_sparse_slices(qg, q_dtype):
+    """Balanced slices over a sparse batch (one long sequence, empty ones): e4m3 row
+    tiles of 8 rows (QG 5, 8) and one f16 tile of 16 rows (QG 12, 16)."""
     need_gpu()
     case = fp8(sparse_lens(), hk=4, qg=qg, seed=301 + qg, q_dtype=q_dtype)
     log(f"case fused sparse slices qg={qg} q={q_dtype}")
@@ -107,9 +110,10 @@ def test_workspace_reused_across_sizes():
 @pytest.mark.parametrize("ql,qg,q_dtype", [(1, 32, "bf16"), (1, 48, "f32"), (2, 32, "bf16"),
                                             (1, 64, "bf16")])
 def test_balanced_row_slices(ql, qg, q_dtype):
-    """Groups of 32-64 rows split over 2 or 4 waves per kv head (row slices, a fourth
-    slice idle at 48 rows) inside balanced slices (the sparse batch at Hk = 4: two
-    workgroups per CU); through the fused step and through decode + reduce."""
+    """Groups of 32-64 rows in f16 tiles of 16 rows: 32 rows as two tiles of one wave, 48
+    and 64 rows split over two waves per kv head (row slices; at 48 rows the second
+    wave's second tile is empty), inside balanced slices (the sparse batch at Hk = 4);
+    through the fused step and through decode + reduce."""
     need_gpu()
     case = fp8(sparse_lens(360), hk=4, qg=qg, seed=361 + qg + ql, q_dtype=q_dtype,
                query_len=ql)
@@ -124,10 +128,13 @@ def test_balanced_row_slices(ql, qg, q_dtype):
     assert_decode_close(split, ref, f"split row slices ql={ql} qg={qg}")
 
 
-@pytest.mark.parametrize("ql,qg,hk", [(2, 16, 4), (4, 8, 8), (1, 48, 4)])
+@pytest.mark.parametrize("ql,qg,hk", [(2, 16, 4), (4, 8, 8), (1, 48, 4), (1, 12, 4), (1, 40, 6),
+                                      (2, 16, 3)])
 def test_fused_query_rows_and_passes(ql, qg, hk):
-    """Two row tiles, and groups of more than 16 rows (one launch per 16 rows, each a
-    complete flash-combine that leaves the counters at zero for the next)."""
+    """Head-group runs (short batch, 16 partitions) with f16 row tiles: one tile (12
+    rows), two (32 rows), row slices (40 rows at Hk = 6, 48 at Hk = 4); and, without
+    head groups (Hk = 3), 32 rows in two launches of 16 rows, each a complete
+    flash-combine that leaves the counters at zero for the next."""
     need_gpu()
     lens = (1, 2, 3, 255, 256, 257, 1000, 3000, 9000)
     case = fp8(lens, hk=hk, qg=qg, seed=330 + ql + qg, query_len=ql)

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 from quantized_paged_attention_amd import synth
-from tests.gpu_util import assert_decode_close, log, need_gpu, oracle_decode, run_decode
+from tests.gpu_util import (assert_decode_close, log, need_gpu, oracle_decode,
+                            oracle_decode_seqs, run_decode)
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +130,20 @@ def test_fp8_high_mtp_full():
     log(f"case fp8_high_mtp2_qg4 (full GPU run, full oracle) kv_bytes={case.kv_bytes()}")
     got, _ = run_decode(case)
     assert_decode_close(got, oracle_decode(case), "fp8_high_mtp")
+
+
+@pytest.mark.parametrize("ql,qg", [(1, 16), (2, 8), (1, 12), (1, 32), (1, 64)])
+def test_fp8_high_wide_groups_full(ql, qg):
+    """The high-batch fp8 shape with 9-64 query rows per kv head (one f16 row tile of 16
+    rows, two per wave, or two row slices per kv head), run at full size in the
+    benchmark's launch configuration; every output row of every fourth sequence (32 of
+    128, all their query rows and heads) is compared with the oracle."""
+    need_gpu()
+    case = synth.fp8_high_mtp(ql, qg)
+    log(f"case fp8_high_mtp{ql}_qg{qg} (full GPU run, oracle on 32 sequences)")
+    got, _ = run_decode(case)
+    rows, ref = oracle_decode_seqs(case, np.arange(0, case.B, 4))
+    assert_decode_close(got[rows], ref, f"fp8_high_mtp{ql}_qg{qg}")
 
 
 @pytest.mark.parametrize("kind", ["e4m3", "ue8m0"])

@@ -141,16 +141,18 @@ def test_head_groups_per_token(P):
     assert_decode_close(got, oracle_decode(case), f"per-token head groups P={P}")
 
 
-def test_balanced_row_slices_per_token():
-    """Per-token scales with 32 rows per kv head in row slices inside balanced slices (80
-    sequences, one of 16384 tokens, Hk = 4), fused and through decode + reduce."""
+@pytest.mark.parametrize("qg", [12, 32, 64])
+def test_balanced_row_slices_per_token(qg):
+    """Per-token scales with f16 row tiles inside balanced slices (80 sequences, one of
+    16384 tokens, Hk = 4): 12 rows in one tile, 32 in two, 64 in two row slices; fused
+    and through decode + reduce."""
     need_gpu()
     rng = np.random.default_rng(370)
     lens = rng.integers(1, 300, size=80)
     lens[0] = 16384
     lens[[3, 40]] = 0
-    case = tok(371, lens=tuple(int(x) for x in lens), hk=4, qg=32)
-    log("case fp8 per-token balanced row slices qg=32")
+    case = tok(371 + qg, lens=tuple(int(x) for x in lens), hk=4, qg=qg)
+    log(f"case fp8 per-token balanced row slices qg={qg}")
     ref = oracle_decode(case)
     got, _ = run_decode(case)
     assert_decode_close(got, ref, "per-token row slices fused")
