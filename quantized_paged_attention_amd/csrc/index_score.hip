@@ -30,9 +30,14 @@
 //     over contiguous shares of the list, two per SIMD: 16.2 / 19.3 us; one wave per live
 //     page: 11.7 / 15.6 us.  Wave timestamps of the last: every wave starts within 1 us,
 //     the pages arrive between 2.8 and 9.2 us (45 MB at ~7 TB/s), each page then takes
-//     ~1.5 us of dequant and MFMA.  The query bytes are loaded before the table entry and
-//     the page, tile by tile, so a page's first tiles are scored while its last ones are
-//     in flight (graph-timed on MI355X: 11.8 -> 11.45 us at QL 1 x H 1).
+//     ~1.5 us of dequant and MFMA.  The query bytes are loaded before the page, tile by
+//     tile, so a page's first tiles are scored while its last ones are in flight
+//     (graph-timed on MI355X: 11.8 -> 11.45 us at QL 1 x H 1).  The table entries of the
+//     wave's page and of its next one are read before the loop, which the compiler turns
+//     into scalar loads running beside the query loads (11.3 -> 10.6 us); the next page's
+//     chain after the first is then one load.  At QL 8 x H 4 the two column tiles take
+//     4 waves per SIMD: 4096 waves for the 4128 live pages of the workload, so 32 waves
+//     score a second page (12.3 us when they skip it, 14.8 us with it).
 //   * More requests: one wave per (request, page slot), the table entry read after the
 //     length says the page is live.
 #include "uq_device.h"
@@ -79,21 +84,36 @@ struct Page {
 // The page through one buffer resource (wave-uniform base): a lane-constant byte offset
 // plus the tile's offset as the scalar offset, so the 16 loads need no per-tile address
 // registers.  Non-temporal (aux bit 1).
-__device__ __forceinline__ void load_page(const uint8_t* pg, int n, int q, Page& d) {
+// records = 0 gives a resource whose loads all return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pg, int records) {
   const uint64_t base = (uint64_t)pg;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
-  const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
-      kPageTokens * (kCodeBytes + kScaleBytes), 0x00020000);
-  const uint32_t co = (uint32_t)(n * kCodeBytes + 16 * q);
-  const uint32_t so = (uint32_t)(kScaleRegion + n * kScaleBytes + 4 * (q >> 1));
-  // tile by tile (codes, then the scale word): loads return in order, so tile T can be
-  // scored as soon as its two loads are back
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                           (short)0, records, 0x00020000);
+}
+
+// Tile T of a page (codes, then the scale word) at the lane offsets co / so.
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, uint32_t co, uint32_t so,
+                                          int T, Page& d) {
+  d.kc[T] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 16 * T * kCodeBytes, 2);
+  d.ksw[T] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 16 * T * kScaleBytes, 2);
+}
+
+__device__ __forceinline__ uint32_t code_off(int n, int q) {
+  return (uint32_t)(n * kCodeBytes + 16 * q);
+}
+__device__ __forceinline__ uint32_t scale_off(int n, int q) {
+  return (uint32_t)(kScaleRegion + n * kScaleBytes + 4 * (q >> 1));
+}
+
+__device__ __forceinline__ void load_page(const uint8_t* pg, int n, int q, Page& d) {
+  const auto rs = page_rsrc(pg, kPageTokens * (kCodeBytes + kScaleBytes));
+  // tile by tile: loads return in order, so tile T can be scored as soon as its two loads
+  // are back
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
-    d.kc[T] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 16 * T * kCodeBytes, 2);
-    d.ksw[T] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 16 * T * kScaleBytes, 2);
+    load_tile(rs, code_off(n, q), scale_off(n, q), T, d);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -143,7 +163,8 @@ __device__ __forceinline__ void score_page(const IndexArgs& a, const Page& d, co
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const float m = max_across_rows(best[ct]);
-    const int col = 16 * ct + n;
+    int col = 16 * ct + n;
+    if constexpr (NCT == 2) asm volatile("" : "+v"(col));  // the store address is built here
     if (q == 0 && col < R) {
       const int j = col / a.H, hh = col % a.H;
       a.scores[(int64_t)hh * a.s_sh + ((int64_t)r * a.QL + j) * a.s_st + b] = m;
@@ -162,7 +183,12 @@ __device__ __forceinline__ void load_q_raw(const IndexArgs& a, int r, int n, int
       raw[ct][0] = raw[ct][1] = i32x4{0, 0, 0, 0};
       continue;
     }
-    const int col = 16 * ct + n;
+    int col = 16 * ct + n;
+    // two column tiles: opaque to the optimiser, so the lane's query address is rebuilt
+    // for every page rather than hoisted out of the page loop, where its two 64-bit values
+    // were spilled to scratch and reloaded ahead of the query loads (one more memory
+    // round trip per page; QL 8 x H 4 on MI355X: 15.9 -> 14.8 us)
+    if constexpr (NCT == 2) asm volatile("" : "+v"(col));
     raw[ct][0] = raw[ct][1] = i32x4{0, 0, 0, 0};
     if (col < R) {
       const int j = col / a.H, hh = col % a.H;
@@ -209,16 +235,32 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
     incl += lane >= d ? u : 0;
   }
   const int Tp = __builtin_amdgcn_readlane(incl, 63);
-  for (int e = (int)gw; e < Tp; e += (int)NW) {  // wave-uniform
+  // list entry e -> (request r, page b, length L)
+  auto locate = [&](int e, int& r, int& b, int& L) {
     // the request holding entry e: the first lane whose inclusive count exceeds e
-    const int r = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
-    const int b = e - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(pl, r));
-    const int L = __builtin_amdgcn_readlane(Ll, r);
+    r = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
+    b = e - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(pl, r));
+    L = __builtin_amdgcn_readlane(Ll, r);
+  };
+  int e = (int)gw;
+  if (e >= Tp) return;  // wave-uniform
+  int r, b, L;
+  locate(e, r, b, L);
+  // the table entries of this page and of the wave's next one (when the live pages
+  // outnumber the waves) in one round trip, so the next page's chain after this one is
+  // a single load
+  int e2 = e + (int)NW;
+  int r2 = 0, b2 = 0, L2 = 0;
+  if (e2 < Tp) locate(e2, r2, b2, L2);
+  const int id1 = a.bt[(int64_t)r * a.bt_stride + b];
+  const int id2 = e2 < Tp ? a.bt[(int64_t)r2 * a.bt_stride + b2] : 0;
+  int pid = __builtin_amdgcn_readfirstlane(id1);
+  int pid2 = __builtin_amdgcn_readfirstlane(id2);
+  while (true) {
     // the query bytes first: vector loads return in order, so with them ahead of the
     // page the first tile's MFMAs can start while the rest of the page is in flight
     i32x4 qraw[2][2];
     load_q_raw<NCT>(a, r, n, q, R, qraw);
-    const int pid = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r * a.bt_stride + b]);
     Page cur;
     load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
     f16x8 qb[2][4];
@@ -230,6 +272,17 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
       lim0[ct] = col < R ? L - a.QL + col / a.H : -1;  // last visible token of the row
     }
     score_page<NCT>(a, cur, qb, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL);
+    if (e2 >= Tp) break;  // wave-uniform
+    e = e2;
+    r = r2;
+    b = b2;
+    L = L2;
+    pid = pid2;
+    e2 = e + (int)NW;
+    if (e2 < Tp) {  // a third page (more than twice as many live pages as waves)
+      locate(e2, r2, b2, L2);
+      pid2 = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r2 * a.bt_stride + b2]);
+    }
   }
 }
 
