@@ -204,7 +204,18 @@ __device__ __forceinline__ void fp4_unit(const DecodeArgs& a, const int lane, co
         q_raw[rp / 4][k] = *reinterpret_cast<const i32x4*>(src + k * (16 / (int)sizeof(QT)));
     }
   }
-  if (a.rot_signs) sg_raw = *reinterpret_cast<const i32x4*>(a.rot_signs + 16 * (lane & 15));
+  {
+    // through a buffer resource with no records when there are no signs (the load then
+    // returns zeros): no branch, so no copy at a join that would wait for the query loads
+    // before the block-table window is even requested
+    const uint64_t base = (uint64_t)(a.rot_signs ? (const void*)a.rot_signs : a.q);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, a.rot_signs ? kD : 0,
+        0x00020000);
+    sg_raw = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (lane & 15), 0, 0);
+  }
 
 
   const int n = lane & 15;   // unit row of the QK / softmax layout; PV column group
