@@ -58,18 +58,26 @@ __global__ __launch_bounds__(S <= 4 ? 256 : 64 * S) void reduce_kernel(ReduceArg
   float M = -INFINITY, den = 0.f;
 
   if (n <= 64 * kChunks) {
-    // (m, l) of every partition at once: lane p of chunk c holds partition 64 c + p
+    // (m, l) of every partition at once: lane p of chunk c holds partition 64 c + p.
+    // Through buffer resources whose record count ends at partition n: the loads past it
+    // return zero with no branch, so all of them are in flight together (a conditional
+    // load per chunk left a copy at each join that waited for it: one round trip per
+    // chunk and statistic).
+    auto stat_rsrc = [&](const float* base) {
+      const uint64_t ad = (uint64_t)(base + ml0);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)ad);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(ad >> 32));
+      return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                               (short)0, __builtin_amdgcn_readfirstlane(n * a.QG * 4),
+                                               0x00020000);
+    };
+    const auto rl = stat_rsrc(a.part_l), rm = stat_rsrc(a.part_m);
     float mv[kChunks], lv[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      mv[c] = -INFINITY;
-      lv[c] = 0.f;
-      const int p = 64 * c + lane;
-      if (64 * c < n && p < n) {
-        const int64_t ml = ml0 + (int64_t)p * a.QG;
-        lv[c] = a.part_l[ml];
-        mv[c] = a.part_m[ml];
-      }
+      const uint32_t off = (uint32_t)((64 * c + lane) * a.QG * 4);
+      lv[c] = bits_f((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0));
+      mv[c] = bits_f((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rm, off, 0, 0));
     }
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) M = fmaxf(M, lv[c] > 0.f ? mv[c] : -INFINITY);
