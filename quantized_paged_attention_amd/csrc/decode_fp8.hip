@@ -8,10 +8,12 @@
 // partition p) the softmax statistics (m, l, o = v_scale * sum exp(s - m) v / l) of the
 // tokens of tile-groups p, p+P, ...
 //
-// Design (a workgroup of W = 4 waves; KV streamed once per 16 query rows):
-//   * Head groups (Hk a multiple of 4): the 4 waves take 4 neighbouring kv heads of one
-//     (sequence, run of consecutive partitions), so they read the neighbouring head slots
-//     of the same blocks together; each wave streams the run as one online softmax and
+// Design (a workgroup of W = 4 waves; KV streamed once for all of a kv head's query rows
+// with head groups, once per 16 rows without):
+//   * Head groups (Hk a multiple of 4, or of 2 for 33-64 rows, which take two waves per
+//     kv head): the 4 waves take 4 neighbouring kv heads of one (sequence, run of
+//     consecutive partitions), so they read the neighbouring head slots of the same
+//     blocks together; each wave streams the run as one online softmax and
 //     merges it into the statistics of the run's first partition.  Otherwise the 4 waves
 //     split a group of one head's partitions and their states meet in LDS.  Either way
 //     the run's other partitions are written as empty (m = -inf, l = 0), which the
@@ -34,9 +36,9 @@
 //     B=128, Hk=8, L ~ U[4k, 16k], fused step on MI355X: 8 rows 413 us; 16 rows 435 us
 //     as two e4m3 tiles, 417 us as one f16 tile; 32 rows 658 us as e4m3 row slices, 454
 //     us as two f16 tiles; 64 rows 1108 / 688 us.
-//   * Per 16-token tile, QK is one 16x16x128 f8f6f4 MFMA with A = the K codes straight
-//     from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query group as an
-//     e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
+//   * In an e4m3 tile, QK is one 16x16x128 f8f6f4 MFMA per 16 tokens with A = the K
+//     codes straight from HBM (lane = token n, head dims [32r, 32r+32)) and B = the query
+//     group as an e4m3 hi/lo pair -- columns 0-7 hold hi(q s_q), 8-15 lo(q s_q), added by a DPP row
 //     rotate.  s_q is a per-row power of two putting the row's largest magnitude in
 //     [64, 128): the pair reproduces every bf16 element of magnitude >= 2^-2 / s_q (about
 //     amax / 512 to amax / 256) exactly; smaller elements land on the e4m3 subnormal grid
@@ -48,15 +50,18 @@
 //     loads of 16 tokens x half a line stream at 4.5 TB/s, of 8 tokens x whole lines at
 //     6.2 TB/s.
 //   * Softmax is online in exp2 units against a reference max raised (with 4 units of
-//     headroom) only when a score exceeds it, p = 2^(s - ref + 8) <= 256 split into an
-//     e4m3 hi/lo pair in columns 0-7 / 8-15.  Each lane tests its own scores against the
-//     reference; the cross-lane row maximum is taken only on a raise.  The causal mask
-//     is applied only to a tile pair that reaches past the shortest row window.  With
-//     per-tensor scales the row sums of P come from one more MFMA (a block of e4m3 ones
-//     times P), so the sums are those of the codes the PV MFMA multiplies.  Measured on
-//     MI355X (B=128, Hk=8, L ~ U[4k, 16k], QG=16, fused step): 451 -> 436 us.  PV is a 16x16x32 fp8 MFMA per 8 head dims
-//     with A = V^T: each lane pair loads 16 dims of 4 tokens with 16-byte loads, swaps
-//     halves (DPP) and byte-transposes (v_perm), so V codes go to the MFMA untouched.
+//     headroom) only when a score exceeds it, p = 2^(s - ref + 8) <= 256: an e4m3 hi/lo
+//     pair in columns 0-7 / 8-15 of an e4m3 tile, one f16 in an f16 tile.  Each lane
+//     tests its own scores against the reference; the cross-lane row maximum is taken
+//     only on a raise.  The causal mask is applied only to a tile pair that reaches past
+//     the shortest row window.  With per-tensor scales the row sums of P come from one
+//     more MFMA (a block of ones times P), so the sums are those of the values the PV
+//     MFMA multiplies.  Measured on MI355X (B=128, Hk=8, L ~ U[4k, 16k], QG=16, fused
+//     step, two e4m3 tiles): 451 -> 436 us.
+//   * PV takes A = V^T: each lane pair loads 16 dims of 4 tokens with 16-byte loads, swaps
+//     halves (DPP) and byte-transposes (v_perm).  In an e4m3 tile the V codes go to a
+//     16x16x32 fp8 MFMA per 8 head dims untouched; in an f16 tile they are converted to
+//     f16 once (exactly) and shared by the row tiles.
 //   * Per-token scales (the PR's per_token_kv mode): each lane loads the K and V scale of
 //     one token of its 4-token quad (a 64-byte line per tile and head) and DPP-broadcasts
 //     them.  The K scale multiplies the score.  The V scale rides in P: P's pair holds

@@ -27,12 +27,12 @@ struct DecodeArgs {
   int32_t runs;     // work items per (sequence, kv head)
   int32_t run_len;  // partitions per work item when each partition is one tile-group, else 0
   int32_t head_groups;  // fp8: 1 = a workgroup's waves are consecutive kv heads of one run
-  int32_t row_base;     // fp8: first unit row of this launch (wide groups run in passes of
-                        // 16 rows; set by the launcher)
-  int32_t row_splits;   // fp8 head groups, more than 16 rows: 2 or 4 = one launch in which
-                        // each kv head's rows are split over that many waves of a workgroup
-                        // (16 rows each; 4 / row_splits kv heads per workgroup); 0 or 1 =
-                        // passes of 16 rows
+  int32_t row_base;     // fp8: first unit row of this launch (without head groups, wide
+                        // groups run in passes of 16 rows; set by the launcher)
+  int32_t row_splits;   // fp8 head groups: 2 = one launch in which each kv head's 33-64
+                        // rows are split over two waves of a workgroup (32 rows each, in
+                        // f16 row tiles; 2 kv heads per workgroup); 0 or 1 = one wave per
+                        // kv head (up to 32 rows)
   int32_t balanced_items;  // fp8 head groups: > 0 = the partitions of all sequences are
                            // split on the device into this many equal slices per head group
   float softmax_scale;

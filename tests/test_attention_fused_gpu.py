@@ -1,12 +1,13 @@
 """uq_paged_attention: decode and flash-combine in one call.  With the fp8 formats and head
-groups (num_kv_heads a multiple of 4) one launch does both: every work unit that covers
-only part of its sequence leaves its softmax state in the workspace and counts its
-partitions; the unit that completes the count merges the states and writes the output
-rows.  These cases aim at the shapes of that bookkeeping (balanced slices that split
-sequences, empty slices, sequences wholly inside one slice, zero-length sequences, two
-row tiles, several passes of 16 rows, float32 output) and at the workspace contract
-(counters back at zero after every call, reuse across calls of other sizes, graph
-replay).  Every output is compared with the fp64 oracle."""
+groups (num_kv_heads a multiple of 4, or of 2 for 33-64 rows) one launch does both: every
+work unit that covers only part of its sequence leaves its softmax state in the workspace
+and counts its partitions; the unit that completes the count merges the states and writes
+the output rows.  These cases aim at the shapes of that bookkeeping (balanced slices that
+split sequences, empty slices, sequences wholly inside one slice, zero-length sequences,
+e4m3 and f16 row tiles, row slices, passes of 16 rows without head groups, float32
+output) and at the workspace contract (counters back at zero after every call, reuse
+across calls of other sizes, graph replay).  Every output is compared with the fp64
+oracle."""
 
 import numpy as np
 import pytest

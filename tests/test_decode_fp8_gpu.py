@@ -316,8 +316,10 @@ def test_head_group_large_batch_runs():
 @pytest.mark.parametrize("qg", [12, 16, 24, 32, 64])
 @pytest.mark.parametrize("hk", [2, 4])
 def test_wide_query_groups(qg, hk):
-    """Query groups above 8 rows: two row tiles of 8 share one pass over the cache, and
-    groups above 16 rows run one pass per 16 rows (the pages' wide-GQA case)."""
+    """Query groups above 8 rows (the pages' wide-GQA case).  hk = 4: head groups with f16
+    row tiles of 16 rows, one wave per kv head up to 32 rows and two above.  hk = 2: no head
+    groups up to 32 rows, so two e4m3 row tiles of 8 share one pass over the cache and
+    wider groups run one pass per 16 rows; at 64 rows head groups of 2 kv heads."""
     need_gpu()
     case = small(hk=hk, qg=qg, seed=80 + qg + hk, q_dtype="f32" if qg == 12 else "bf16",
                  lens=(1, 17, 256, 257, 1000, 2500))

@@ -159,7 +159,9 @@ def test_fp4_d256_mtp_full(kind):
 
 @pytest.mark.parametrize("ql,qg,hk", [(2, 8, 2), (3, 5, 4), (4, 8, 4), (2, 16, 2)])
 def test_fp8_query_rows_wide(ql, qg, hk):
-    """Query rows x heads above 8 (two row tiles; 32 rows run two passes)."""
+    """Query rows x heads above 8: with hk = 2 (no head groups) two e4m3 row tiles of 8,
+    and 32 rows in two passes; with hk = 4 f16 row tiles of 16 (15 rows in one, 32 in
+    two)."""
     need_gpu()
     case = fp8(ql, qg, seed=280 + 10 * ql + qg + hk, hk=hk, k_scale=0.05, v_scale=0.02,
                values="uniform_codes", lens=(1, 2, 3, 7, 255, 256, 257, 1000))
