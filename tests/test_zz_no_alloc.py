@@ -35,17 +35,25 @@ def run_both(case):
             ref.float().cpu().numpy().astype(np.float64))
 
 
-@pytest.mark.parametrize("kind", ["fp8_fused", "fp4_split"])
+@pytest.mark.parametrize("kind", ["fp8_fused", "fp8_wide", "fp4_split"])
 def test_noalloc_matches_workspace_entry(kind):
     """Calls in a row on the shared scratch, the second smaller, the third larger: each
-    output equals the workspace entry point's within 1e-3 of max|out| (the merge order may
-    differ) and the oracle within the decode tolerance."""
+    output element equals the workspace entry point's to within one bf16 step at its
+    magnitude plus 1e-5 of max|out| (both compute the same states; only the order in which
+    the last unit of a sequence merges the others' may differ, which changes the f32 sums
+    by rounding and can move an element across a bf16 boundary; the same holds between
+    two calls of either entry point) and the oracle within the decode tolerance."""
     need_gpu()
     rng = np.random.default_rng(500)
     if kind == "fp8_fused":
         big = fp8_case(rng.integers(1, 9000, size=96), hk=8, qg=8, seed=501)
         small = fp8_case((1, 700, 5000, 0, 257), hk=8, qg=8, seed=502)
         grow = fp8_case(rng.integers(0, 3000, size=128), hk=8, qg=8, seed=505)
+    elif kind == "fp8_wide":
+        # f16 row tiles: two per wave (32 rows), one (16 rows), two row slices (48 rows)
+        big = fp8_case(rng.integers(1, 9000, size=40), hk=4, qg=32, seed=507)
+        small = fp8_case((1, 700, 5000, 0, 257), hk=4, qg=16, seed=508)
+        grow = fp8_case(rng.integers(0, 6000, size=64), hk=4, qg=48, seed=509)
     else:
         big = synth.make_fp4_case("noalloc4", 503, seq_lens=[300, 5000, 20000, 64], num_kv_heads=2,
                                   qg=16, head_dim=256, block_size=64, rotate=True, spare_blocks=3)
@@ -59,8 +67,11 @@ def test_noalloc_matches_workspace_entry(kind):
         log(f"case noalloc {kind} call {i} B={case.B}")
         got, ref = run_both(case)
         assert np.isfinite(got).all()
-        scale = np.abs(ref).max()
-        err = float(np.abs(got - ref).max() / (scale if scale > 0 else 1.0))
-        log(f"  noalloc vs workspace entry: {err:.3e}")
-        assert err <= 1e-3
+        mag = np.maximum(np.abs(got), np.abs(ref))
+        # one bf16 step at each element's magnitude: 2^(e - 7) for |x| in [2^e, 2^(e+1))
+        step = np.exp2(np.floor(np.log2(np.maximum(mag, 2.0 ** -126))) - 7)
+        bound = step + 1e-5 * np.abs(ref).max()
+        worst = float((np.abs(got - ref) / bound).max())
+        log(f"  noalloc vs workspace entry: {worst:.2f} of the bound at most")
+        assert worst <= 1.0
         assert_decode_close(got, oracle_decode(case), f"noalloc {kind} call {i}")
