@@ -736,10 +736,19 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, const int lane,
         old = __hip_atomic_fetch_add(cnt, fz.take, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       old = __builtin_amdgcn_readfirstlane(old);
       if (old + fz.take != fz.pm) return;  // wave-uniform: another unit finishes the sequence
-      // the next used slot of the range at or after k, other than this unit's own
+      // The merge starts empty and folds in every used slot of the sequence in slot order,
+      // this unit's own included (read back: its stores have completed), so the output
+      // does not depend on which unit happened to finish last.
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        ref[t] = -INFINITY;
+        lsum[t] = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // the next used slot of the range at or after k
       auto next_used = [&](int64_t k) {
         for (; k <= fz.hi; ++k) {
-          if (k == fz.slot) continue;
           if (fz.Tt > 0) {
             const int64_t sl = k - b;
             if (sl * fz.Tt / fz.N >= (sl + 1) * fz.Tt / fz.N) continue;  // empty slice
