@@ -155,6 +155,27 @@ def test_fused_strided_partitions(P):
     assert_decode_close(got, oracle_decode(case), f"fused strided P={P}")
 
 
+@pytest.mark.parametrize("qg,layout", [(8, "sparse"), (32, "sparse"), (48, "ragged"),
+                                       (16, "ragged")])
+def test_fused_repeat_bit_identical(qg, layout):
+    """Repeated calls give the same output bit for bit: the unit that completes a sequence
+    merges its slots' states in slot order whichever unit finished last.  The sparse batch
+    spreads one 16k sequence over dozens of units; the ragged one splits most sequences
+    once or twice (e4m3 tiles at 8 rows, f16 tiles at 16 and 32, row slices at 48)."""
+    need_gpu()
+    lens = sparse_lens(371 + qg) if layout == "sparse" else np.random.default_rng(
+        372 + qg).integers(0, 9000, size=96)
+    case = fp8(lens, hk=4, qg=qg, seed=373 + qg)
+    log(f"case fused repeat qg={qg} {layout}")
+    dev = device_case(case)
+    q = q_tensor(case)
+    first, _ = run_decode(case, dev=dev, q=q)
+    assert_decode_close(first, oracle_decode(case), f"fused repeat qg={qg}")
+    for i in range(5):
+        got, _ = run_decode(case, dev=dev, q=q)
+        assert np.array_equal(got, first), f"call {i + 1}"
+
+
 def test_fused_graph_replay():
     """uq_paged_attention captured in a HIP graph: every replay, with eager work and
     synchronisations in between, gives the eager result bit for bit (the counters return
