@@ -13,13 +13,16 @@
 //     packed f16 multiply per byte) and the dot products run on v_mfma_f32_16x16x32_f16
 //     with exact products and fp32 accumulation.
 //   * A = K tile (lane = token, 32 consecutive dims per lane), B = the request's query
-//     rows (columns = (j, h), at most 32: two column tiles).  The output layout puts
+//     rows (columns = (j, h), at most 32: two column tiles), kept as raw e4m3 words and
+//     converted to f16 at each use (v_cvt_scalef32_pk_f16_fp8, exact).  The output layout puts
 //     4 tokens of one column in a lane; masked tokens are selected to -inf (never
 //     multiplied, so garbage past the sequence cannot leak), the page max is kept per
 //     lane and reduced across the four lane rows once per page.  A page that every row
 //     sees whole skips the causal selects.
-//   * A whole page (8 tiles: 128 code bytes + 1 scale word per lane, non-temporal, one
-//     buffer resource) is in registers before its first MFMA.
+//   * A page (8 tiles: 128 code bytes + 1 scale word per lane, non-temporal, one buffer
+//     resource) is requested whole before its first MFMA: into registers with one column
+//     tile; with two, half of it, each later tile loaded into the registers of the tile
+//     4 before it once that one is dequantised (5 waves per SIMD either way).
 //   * Up to 64 requests: one wave per LIVE page.  The lengths give each request's live
 //     pages; all requests' live pages form one list, and wave g of the launch takes
 //     entries g, g + NW, ... with NW = the waves the chip holds at once.  A wave's chain
@@ -35,9 +38,9 @@
 //     (graph-timed on MI355X: 11.8 -> 11.45 us at QL 1 x H 1).  The table entries of the
 //     wave's page and of its next one are read before the loop, which the compiler turns
 //     into scalar loads running beside the query loads (11.3 -> 10.6 us); the next page's
-//     chain after the first is then one load.  At QL 8 x H 4 the two column tiles take
-//     4 waves per SIMD: 4096 waves for the 4128 live pages of the workload, so 32 waves
-//     score a second page (12.3 us when they skip it, 14.8 us with it).
+//     chain after the first is then one load.  At QL 8 x H 4 the scorer still takes
+//     ~3.5 us more than at QL 8 x H 2 (one column tile, 10.9 us): twice the MFMAs and
+//     the query conversions per page, on the last pages to arrive.
 //   * More requests: one wave per (request, page slot), the table entry read after the
 //     length says the page is live.
 #include "uq_device.h"
@@ -53,11 +56,14 @@ constexpr int kCodeBytes = 64;    // per token: 128 e2m1 codes
 constexpr int kScaleBytes = 8;    // per token: one e4m3 scale per 16 dims
 constexpr int kScaleRegion = kPageTokens * kCodeBytes;
 constexpr int kWaves = 4;
-// waves per SIMD of the scorer kernels by column tiles (registers: at most 96 and 128).
-// Two column tiles at 5 waves per SIMD spill inside the page loop: measured on MI355X
-// (QL 8 x H 4) 29.7 us against 16.0 us at 4, although at 4 the 4096 waves take the
-// 4128 live pages in two rounds.
-constexpr int kLiveWavesPerSimd[2] = {5, 4};
+// waves per SIMD of the scorer kernels by column tiles (at most 96 registers).  Two
+// column tiles fit by keeping half a page in registers (tile T + 4 streams into the
+// registers of tile T once it is dequantised) and the query as raw e4m3 words, converted
+// at each use: so the QL 8 x H 4 workload's 4128 live pages get a wave each (5120 waves)
+// instead of 32 of the 4096 waves at 4 per SIMD taking a second page (MI355X: 14.7 ->
+// 14.1 us; with the whole page and f16 query operands 5 waves per SIMD spilled in the
+// page loop, 29.7 us).
+constexpr int kLiveWavesPerSimd[2] = {5, 5};
 
 template <int sel>
 __device__ __forceinline__ f16x2 fp4_pair(uint32_t word) {
@@ -68,18 +74,13 @@ __device__ __forceinline__ f16x8 cat4(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// 8 e4m3 bytes (two words, low byte first) -> 8 f16 (exact)
-__device__ __forceinline__ f16x8 e4m3x8_to_f16(int w0, int w1) {
-  return f16x8{(_Float16)e4m3_to_f<0>(w0), (_Float16)e4m3_to_f<1>(w0),
-               (_Float16)e4m3_to_f<2>(w0), (_Float16)e4m3_to_f<3>(w0),
-               (_Float16)e4m3_to_f<0>(w1), (_Float16)e4m3_to_f<1>(w1),
-               (_Float16)e4m3_to_f<2>(w1), (_Float16)e4m3_to_f<3>(w1)};
-}
-
-struct Page {
-  i32x4 kc[8];       // codes [16 q, 16 q + 16) of tokens 16 T + n
-  uint32_t ksw[8];   // the scale word of groups 2q, 2q + 1 of those tokens
+// NS tile slots of a page (8: the whole page; 4: half, refilled as it is scored)
+template <int NS>
+struct PageT {
+  i32x4 kc[NS];       // codes [16 q, 16 q + 16) of tokens 16 T + n
+  uint32_t ksw[NS];   // the scale word of groups 2q, 2q + 1 of those tokens
 };
+using Page = PageT<8>;
 
 // The page through one buffer resource (wave-uniform base): a lane-constant byte offset
 // plus the tile's offset as the scalar offset, so the 16 loads need no per-tile address
@@ -94,10 +95,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* pg, i
 }
 
 // Tile T of a page (codes, then the scale word) at the lane offsets co / so.
+template <int NS>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, uint32_t co, uint32_t so,
-                                          int T, Page& d) {
-  d.kc[T] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 16 * T * kCodeBytes, 2);
-  d.ksw[T] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 16 * T * kScaleBytes, 2);
+                                          int T, PageT<NS>& d) {
+  d.kc[T % NS] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 16 * T * kCodeBytes, 2);
+  d.ksw[T % NS] = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 16 * T * kScaleBytes, 2);
 }
 
 __device__ __forceinline__ uint32_t code_off(int n, int q) {
@@ -107,46 +109,64 @@ __device__ __forceinline__ uint32_t scale_off(int n, int q) {
   return (uint32_t)(kScaleRegion + n * kScaleBytes + 4 * (q >> 1));
 }
 
-__device__ __forceinline__ void load_page(const uint8_t* pg, int n, int q, Page& d) {
+template <int NS>
+__device__ __forceinline__ void load_page(const uint8_t* pg, int n, int q, PageT<NS>& d) {
   const auto rs = page_rsrc(pg, kPageTokens * (kCodeBytes + kScaleBytes));
   // tile by tile: loads return in order, so tile T can be scored as soon as its two loads
   // are back
 #pragma unroll
-  for (int T = 0; T < 8; ++T) {
+  for (int T = 0; T < NS; ++T) {
     load_tile(rs, code_off(n, q), scale_off(n, q), T, d);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Score one page: query operands qb (columns c = j * H + h of request r, causal limits
-// lim0[ct] = last visible token of the column's row), page data d at page index b.
-// full (wave-uniform): every token of the page is visible to every row, so the causal
-// selects drop out of the page max.
-template <int NCT>
-__device__ __forceinline__ void score_page(const IndexArgs& a, const Page& d, const f16x8 (&qb)[2][4],
+// 8 e4m3 bytes (two words, low byte first) -> 8 f16 (exact)
+__device__ __forceinline__ f16x8 e4m3x8_f16_pk(int w0, int w1) {
+  const f16x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return cat4(x0, x1, x2, x3);
+}
+
+// Score one page: raw e4m3 query words qr (columns c = j * H + h of request r, causal
+// limits lim0[ct] = last visible token of the column's row), page data d (NS tile slots;
+// with NS < 8 the page's later tiles stream in through rs) at page index b.  full
+// (wave-uniform): every token of the page is visible to every row, so the causal selects
+// drop out of the page max.
+template <int NCT, int NS>
+__device__ __forceinline__ void score_page(const IndexArgs& a, PageT<NS>& d, const i32x4 (&qr)[2][2],
                                            const int (&lim0)[2], const int r, const int b,
-                                           const int n, const int q, const int R, const bool full) {
+                                           const int n, const int q, const int R, const bool full,
+                                           __amdgpu_buffer_rsrc_t rs) {
   float best[2] = {-INFINITY, -INFINITY};
   const int t_page = b * kPageTokens;
 #pragma unroll
   for (int T = 0; T < 8; ++T) {
-    const uint32_t sw = d.ksw[T] >> (16 * (q & 1));
+    const uint32_t sw = d.ksw[T % NS] >> (16 * (q & 1));
     const _Float16 s0h = (_Float16)e4m3_to_f<0>((int)sw), s1h = (_Float16)e4m3_to_f<1>((int)sw);
     const f16x2 s0 = f16x2{s0h, s0h}, s1 = f16x2{s1h, s1h};
     f16x8 A[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint32_t wd = (uint32_t)d.kc[T][kk];
+      const uint32_t wd = (uint32_t)d.kc[T % NS][kk];
       const f16x2 sc = kk < 2 ? s0 : s1;
       A[kk] = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc, fp4_pair<2>(wd) * sc,
                    fp4_pair<3>(wd) * sc);
+    }
+    // a half page in registers: tile T + NS streams into the slot tile T just freed
+    if constexpr (NS < 8) {
+      if (T + NS < 8) load_tile(rs, code_off(n, q), scale_off(n, q), T + NS, d);
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 c4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[kk], qb[ct][kk], c4, 0, 0, 0);
+        c4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            A[kk], e4m3x8_f16_pk(qr[ct][kk >> 1][2 * (kk & 1)], qr[ct][kk >> 1][2 * (kk & 1) + 1]),
+            c4, 0, 0, 0);
       if (!full) {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -196,17 +216,6 @@ __device__ __forceinline__ void load_q_raw(const IndexArgs& a, int r, int n, int
       raw[ct][0] = *reinterpret_cast<const i32x4*>(src);
       raw[ct][1] = *reinterpret_cast<const i32x4*>(src + 16);
     }
-  }
-}
-
-template <int NCT = 2>
-__device__ __forceinline__ void q_operands(const i32x4 (&raw)[2][2], f16x8 (&qb)[2][4]) {
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    qb[ct][0] = e4m3x8_to_f16(raw[ct][0][0], raw[ct][0][1]);
-    qb[ct][1] = e4m3x8_to_f16(raw[ct][0][2], raw[ct][0][3]);
-    qb[ct][2] = e4m3x8_to_f16(raw[ct][1][0], raw[ct][1][1]);
-    qb[ct][3] = e4m3x8_to_f16(raw[ct][1][2], raw[ct][1][3]);
   }
 }
 
@@ -261,17 +270,18 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
     // page the first tile's MFMAs can start while the rest of the page is in flight
     i32x4 qraw[2][2];
     load_q_raw<NCT>(a, r, n, q, R, qraw);
-    Page cur;
-    load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
-    f16x8 qb[2][4];
-    q_operands<NCT>(qraw, qb);
+    constexpr int NS = NCT == 2 ? 4 : 8;
+    PageT<NS> cur;
+    const uint8_t* pg = a.pages + (int64_t)pid * a.page_stride;
+    load_page(pg, n, q, cur);
     int lim0[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int col = 16 * ct + n;
       lim0[ct] = col < R ? L - a.QL + col / a.H : -1;  // last visible token of the row
     }
-    score_page<NCT>(a, cur, qb, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL);
+    score_page<NCT, NS>(a, cur, qraw, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL,
+                        page_rsrc(pg, kPageTokens * (kCodeBytes + kScaleBytes)));
     if (e2 >= Tp) break;  // wave-uniform
     e = e2;
     r = r2;
@@ -307,16 +317,16 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
   load_q_raw<NCT>(a, r, n, q, R, qraw);
   const int pid = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r * a.bt_stride + b]);
   Page cur;
-  load_page(a.pages + (int64_t)pid * a.page_stride, n, q, cur);
-  f16x8 qb[2][4];
-  q_operands<NCT>(qraw, qb);
+  const uint8_t* pg = a.pages + (int64_t)pid * a.page_stride;
+  load_page(pg, n, q, cur);
   int lim0[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int col = 16 * ct + n;
     lim0[ct] = col < R ? L - a.QL + col / a.H : -1;  // last visible token of the row
   }
-  score_page<NCT>(a, cur, qb, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL);
+  score_page<NCT, 8>(a, cur, qraw, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL,
+                     page_rsrc(pg, 0));
 }
 
 }  // namespace
