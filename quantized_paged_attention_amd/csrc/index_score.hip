@@ -248,7 +248,7 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
   auto locate = [&](int e, int& r, int& b, int& L) {
     // the request holding entry e: the first lane whose inclusive count exceeds e
     r = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
-    b = e - (__builtin_amdgcn_readlane(incl, r) - __builtin_amdgcn_readlane(pl, r));
+    b = e - (r > 0 ? __builtin_amdgcn_readlane(incl, r - 1) : 0);
     L = __builtin_amdgcn_readlane(Ll, r);
   };
   int e = (int)gw;
