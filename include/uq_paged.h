@@ -206,8 +206,10 @@ int uq_paged_reduce_mtp(const void* part_out, const float* part_max, const float
  * 2 for groups of 33-64 rows) one launch; every work unit of a (sequence, kv
  * head) that does not cover the whole sequence leaves its softmax state in the workspace
  * and counts its partitions with a device-scope atomic, and the unit that completes the
- * count merges the states and writes the output rows.  Other formats and head counts run
- * the decode into partials held in the workspace, then the reduce (two launches).  Errors
+ * count merges the states, in a fixed order whichever unit finishes last, and writes the
+ * output rows.  Other formats and head counts run the decode into partials held in the
+ * workspace, then the reduce (two launches).  Either way the output depends only on the
+ * inputs: repeated calls give bit-identical results.  Errors
  * as uq_paged_decode_mtp, plus UQ_ERR_INVALID_ARG for a NULL, misaligned or too small
  * workspace or output. */
 int uq_paged_attention(const void* query, int q_dtype, int64_t q_stride_seq,
