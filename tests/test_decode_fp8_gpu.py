@@ -374,14 +374,17 @@ def test_balanced_slices_wide_group():
     assert_decode_close(got, oracle_decode(case), "balanced wide qg=24")
 
 
-def test_balanced_slices_many_sequences():
-    """1000 sequences (16 lengths per lane of the slice lookup), lengths 0..900 with a few
-    long ones: balanced slices start in the middle of lanes' runs of sequences."""
+@pytest.mark.parametrize("B,qg", [(1000, 2), (1024, 16), (1000, 48), (1100, 8)])
+def test_balanced_slices_many_sequences(B, qg):
+    """Up to 1024 sequences (16 lengths per lane of the slice lookup), lengths 0..900 with
+    a few long ones: balanced slices start in the middle of lanes' runs of sequences, with
+    e4m3 row tiles (2 rows), one f16 tile (16) and row slices (48); 1100 sequences take
+    the runs of head groups instead."""
     need_gpu()
-    rng = np.random.default_rng(97)
-    lens = rng.integers(0, 900, size=1000)
-    lens[rng.choice(1000, 20, replace=False)] = rng.integers(4000, 9000, size=20)
-    case = small(hk=4, qg=2, lens=tuple(int(x) for x in lens), seed=98)
-    log(f"case fp8 balanced B={case.B}")
+    rng = np.random.default_rng(97 + qg)
+    lens = rng.integers(0, 900, size=B)
+    lens[rng.choice(B, 20, replace=False)] = rng.integers(4000, 9000, size=20)
+    case = small(hk=4, qg=qg, lens=tuple(int(x) for x in lens), seed=98 + qg)
+    log(f"case fp8 balanced B={case.B} qg={qg}")
     got, _ = run_decode(case, P=64)
-    assert_decode_close(got, oracle_decode(case), "balanced 1000 sequences")
+    assert_decode_close(got, oracle_decode(case), f"balanced B={B} qg={qg}")
