@@ -46,6 +46,10 @@
 #include "uq_device.h"
 #include "uq_kernels.h"
 
+#ifndef UQ_IDX_XCD_RUNS
+#define UQ_IDX_XCD_RUNS 1
+#endif
+
 namespace uq {
 namespace {
 
@@ -219,20 +223,20 @@ __device__ __forceinline__ void load_q_raw(const IndexArgs& a, int r, int n, int
   }
 }
 
-// One wave per live page, for up to 64 requests.  Lane l holds request l's length and
+// The live-page walk for up to 64 requests.  Lane l holds request l's length and
 // live-page count (b < min(ceil(L / 128), max_blocks)); the live pages of all requests, in
-// request order, form a list of Tp entries, and wave g of the NW launched takes entries g,
-// g + NW, ...  So no wave exists for a page past a sequence, a wave's chain is length ->
-// table entry -> page (the table entry is read only for a live page), and the waves of
-// one launch all fit on the chip at once.
-template <int NCT>
-__global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index_score_live(IndexArgs a) {
+// request order, form a list of Tp entries, and wave gw of the NW launched takes entries
+// e, e + NW, ..., calling page(live, r, b, L, pid) for each (request, page index, length,
+// physical page; live = true).  So no wave exists for a page past a sequence, a wave's
+// chain is length -> table entry -> page (the table entry is read only for a live page),
+// and the waves of one launch all fit on the chip at once.  The waves of a workgroup hold
+// consecutive entries; with kUniform every wave of it makes as many calls as its first
+// wave, a wave whose entry is past the list calling with live = false (and r, b, L, pid
+// meaningless), so that the page function may synchronise the workgroup.
+template <bool kUniform, class PageFn>
+__device__ __forceinline__ void for_live_pages(const IndexArgs& a, int64_t gw, int64_t NW,
+                                               PageFn&& page) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t NW = (int64_t)gridDim.x * kWaves;
-  const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
-  const int n = lane & 15, q = lane >> 4;
-  const int R = a.QL * a.H;
   int Ll = lane < a.num_reqs ? a.seq_lens[lane] : 0;
   Ll = Ll < 0 ? 0 : Ll;
   int pl = (Ll + kPageTokens - 1) / kPageTokens;
@@ -244,28 +248,71 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
     incl += lane >= d ? u : 0;
   }
   const int Tp = __builtin_amdgcn_readlane(incl, 63);
-  // list entry e -> (request r, page b, length L)
+  // list entry e < Tp -> (request r, page b, length L)
   auto locate = [&](int e, int& r, int& b, int& L) {
     // the request holding entry e: the first lane whose inclusive count exceeds e
     r = __builtin_popcountll(__builtin_amdgcn_ballot_w64(incl <= e));
     b = e - (r > 0 ? __builtin_amdgcn_readlane(incl, r - 1) : 0);
     L = __builtin_amdgcn_readlane(Ll, r);
   };
+  // the wave's first entry.  Workgroups are dealt to the 8 XCDs in turn; with UQ_IDX_XCD_RUNS
+  // the entries go to them in runs of 32, so the pages of a run (one 128-byte line of
+  // every score row they write) are scored under one L2.  Entries e + NW, e + 2 NW, ...
+  // follow on the same XCD as long as NW is a multiple of 256.  Either way the kWaves
+  // waves of a workgroup hold consecutive entries.
+  const int w = (int)(gw % kWaves);
   int e = (int)gw;
-  if (e >= Tp) return;  // wave-uniform
-  int r, b, L;
-  locate(e, r, b, L);
+  if (UQ_IDX_XCD_RUNS && NW % 256 == 0) {
+    const int64_t wg = gw / kWaves;
+    const int x = (int)(wg % 8);
+    const int i = (int)((wg / 8) * kWaves + w);  // the wave's index on its XCD
+    e = 32 * (x + 8 * (i / 32)) + i % 32;
+  }
+  // the entry that decides the calls: the wave's own, or its workgroup's first
+  int lead = kUniform ? e - w : e;
+  if (lead >= Tp) return;  // wave-uniform (workgroup-uniform with kUniform)
+  bool live = kUniform ? e < Tp : true;
+  int r = 0, b = 0, L = 0;
+  if (live) locate(e, r, b, L);
   // the table entries of this page and of the wave's next one (when the live pages
   // outnumber the waves) in one round trip, so the next page's chain after this one is
   // a single load
   int e2 = e + (int)NW;
   int r2 = 0, b2 = 0, L2 = 0;
   if (e2 < Tp) locate(e2, r2, b2, L2);
-  const int id1 = a.bt[(int64_t)r * a.bt_stride + b];
+  const int id1 = live ? a.bt[(int64_t)r * a.bt_stride + b] : 0;
   const int id2 = e2 < Tp ? a.bt[(int64_t)r2 * a.bt_stride + b2] : 0;
   int pid = __builtin_amdgcn_readfirstlane(id1);
   int pid2 = __builtin_amdgcn_readfirstlane(id2);
   while (true) {
+    page(live, r, b, L, pid);
+    lead += (int)NW;
+    if (lead >= Tp) break;  // wave-uniform (workgroup-uniform with kUniform)
+    e = e2;
+    live = kUniform ? e < Tp : true;
+    r = r2;
+    b = b2;
+    L = L2;
+    pid = pid2;
+    e2 = e + (int)NW;
+    if (e2 < Tp) {  // a third page (more than twice as many live pages as waves)
+      locate(e2, r2, b2, L2);
+      pid2 = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r2 * a.bt_stride + b2]);
+    }
+  }
+}
+
+// One wave per live page, for up to 64 requests and at most 16 query columns (H * QL):
+// 16 x 16 output tiles.
+template <int NCT>
+__global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index_score_live(IndexArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t NW = (int64_t)gridDim.x * kWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+  const int n = lane & 15, q = lane >> 4;
+  const int R = a.QL * a.H;
+  for_live_pages<false>(a, gw, NW, [&](bool, int r, int b, int L, int pid) {
     // the query bytes first: vector loads return in order, so with them ahead of the
     // page the first tile's MFMAs can start while the rest of the page is in flight
     i32x4 qraw[2][2];
@@ -282,18 +329,203 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
     }
     score_page<NCT, NS>(a, cur, qraw, lim0, r, b, n, q, R, (b + 1) * kPageTokens - 1 <= L - a.QL,
                         page_rsrc(pg, kPageTokens * (kCodeBytes + kScaleBytes)));
-    if (e2 >= Tp) break;  // wave-uniform
-    e = e2;
-    r = r2;
-    b = b2;
-    L = L2;
-    pid = pid2;
-    e2 = e + (int)NW;
-    if (e2 < Tp) {  // a third page (more than twice as many live pages as waves)
-      locate(e2, r2, b2, L2);
-      pid2 = __builtin_amdgcn_readfirstlane(a.bt[(int64_t)r2 * a.bt_stride + b2]);
+  });
+}
+
+// ---- 17-32 query columns: 32 x 32 output tiles ----
+//
+// One v_mfma_f32_32x32x16_f16 takes 32 tokens (A rows) against all 32 query columns (B),
+// so a query operand is converted once per 32 tokens for every column, where two 16 x 16
+// column tiles convert it once per 16 tokens for each half of the columns: half the
+// query conversions per page (or none, with the query held in f16), the same K
+// dequantisation and the same MFMA cycles.  Lane l takes token 32 T + (l % 32) of tile T
+// and dims [64 h, 64 h + 64), h = l / 32: 32 code bytes and the 4 scale bytes of those
+// dims; k-step s of the tile is dims 8 s .. 8 s + 8 of each half, whose scale is byte s / 2
+// of the lane's scale word.  The query operand of a lane is column l % 32, the same dims.
+// Output: lane l holds column l % 32 and tokens 8 (v / 4) + 4 h + v % 4 of register v.
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Tile T of a page: the lane's 32 code bytes (two 16-byte words) and its scale word.
+struct Tile32 {
+  i32x4 kc[2];
+  uint32_t ksw;
+};
+
+__device__ __forceinline__ Tile32 load_tile32(__amdgpu_buffer_rsrc_t rs, uint32_t co, uint32_t so,
+                                              int T) {
+  Tile32 d;
+  d.kc[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, co, 32 * T * kCodeBytes, 2);
+  d.kc[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, co + 16, 32 * T * kCodeBytes, 2);
+  d.ksw = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 32 * T * kScaleBytes, 2);
+  return d;
+}
+
+// The query operand of k-step s from the lane's 64 raw e4m3 bytes.
+__device__ __forceinline__ f16x8 q32_operand(const i32x4 (&qr)[4], int s) {
+  return e4m3x8_f16_pk(qr[s >> 1][2 * (s & 1)], qr[s >> 1][2 * (s & 1) + 1]);
+}
+
+// One tile's 32 x 32 scores: lane l gets column l % 32, rows 8 (v / 4) + 4 h + v % 4 in
+// register v.
+__device__ __forceinline__ f32x16 mfma_tile32(const Tile32& d, const f16x8 (&qf)[8]) {
+  const int sw = (int)d.ksw;
+  f32x16 c = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const _Float16 sh = (_Float16)(s < 2   ? e4m3_to_f<0>(sw)
+                                   : s < 4 ? e4m3_to_f<1>(sw)
+                                   : s < 6 ? e4m3_to_f<2>(sw)
+                                           : e4m3_to_f<3>(sw));
+    const f16x2 sc = f16x2{sh, sh};
+    const uint32_t wd = (uint32_t)d.kc[s >> 2][s & 3];
+    const f16x8 A = cat4(fp4_pair<0>(wd) * sc, fp4_pair<1>(wd) * sc, fp4_pair<2>(wd) * sc,
+                         fp4_pair<3>(wd) * sc);
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, qf[s], c, 0, 0, 0);
+  }
+  return c;
+}
+
+// The tile's scores into the lane's running max.  lt: the last visible row of the tile for
+// the lane's column, relative to row 4 h of the tile.
+__device__ __forceinline__ void max_tile32(const f32x16& c, bool full, int lt, float& best) {
+  if (!full) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) best = fmaxf(best, 8 * (v >> 2) + (v & 3) <= lt ? c[v] : -INFINITY);
+  } else {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) best = fmaxf(best, c[v]);
+  }
+}
+
+// x / d for 0 <= x < 64 and 1 <= d <= 64 with inv_d = 1 / d in float: exact, since
+// (x + 1/2) / d lies at least 1 / (2 d) from every integer, far beyond the float error.
+__device__ __forceinline__ int small_div(int x, float inv_d) {
+  return (int)(((float)x + 0.5f) * inv_d);
+}
+
+// The query rows of request r as 32 rows of 128 bytes in the wave's LDS block, through
+// direct buffer-to-LDS loads.  Load i writes bytes [1024 i, 1024 i + 1024) of the block,
+// lane l the 16 bytes 1024 i + 16 l: row c = 8 i + l / 8, slot l % 8, which receives chunk
+// (l % 8) ^ (c % 8) of query column c's 128 bytes.  So each load reads 8 whole rows (8
+// lines, where a load of the lane's own 16 bytes of 32 columns touches 32 lines), and
+// the reads below are free of bank conflicts.  Columns at or past R are not loaded.
+// Nothing tracks these LDS writes: the reader waits on vmcnt for them.
+__device__ __forceinline__ void stage_query32(const IndexArgs& a, int r, int R, int lane,
+                                              uint8_t* blk) {
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  const uint64_t base = (uint64_t)(a.q + (int64_t)r * a.QL * a.q_st);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  // the request's query bytes (a record count past 2^32 - 1 is clamped: offsets are 32-bit)
+  const int64_t span = (int64_t)(a.QL - 1) * a.q_st + (int64_t)(a.H - 1) * a.q_sh + 128;
+  const int records = (int)(uint32_t)(span < 0xFFFFFFFFll ? span : 0xFFFFFFFFll);
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, records, 0x00020000);
+  const int sl = lane & 7;
+  int c0 = lane >> 3;
+  // opaque, so the offsets are computed here for every page rather than hoisted out of
+  // the page loop and spilled (a scratch reload ahead of the query loads)
+  asm volatile("" : "+v"(c0));
+  const float inv_h = 1.0f / (float)a.H;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = 8 * i + c0;
+    if (c < R) {
+      const int j = small_div(c, inv_h), hh = c - j * a.H;
+      const uint32_t off = (uint32_t)(j * a.q_st + hh * a.q_sh + 16 * (sl ^ c0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(blk + 1024 * i), 16, off, 0, 0, 0);
     }
   }
+}
+
+// The lane's 64 query bytes (column m, dims [64 h, 64 h + 64)) from the staged block.
+__device__ __forceinline__ void read_query32(const uint8_t* blk, int m, int h, i32x4 (&qr)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    qr[i] = *reinterpret_cast<const i32x4*>(blk + 128 * m + 16 * ((4 * h + i) ^ (m & 7)));
+}
+
+// Two of the page's four tiles in registers at a time: tile T + 2 is loaded into the
+// registers of tile T once T's MFMAs have read them (with the f16 query held, the whole page
+// in registers needs more than the 96 registers of 5 waves per SIMD).  The page maxima
+// of a workgroup's four waves (four consecutive list entries: mostly four consecutive
+// pages of one request) meet in LDS and are stored together, each score row receiving 16
+// contiguous bytes from four adjacent lanes where one wave per page would touch 32 lines
+// with 4 bytes each.
+template <int NS>
+__global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[1]) void index_score_live32(IndexArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[kWaves][32 * 128];
+  __shared__ float lds_best[2][kWaves][32];
+  __shared__ int lds_rb[2][kWaves][2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t NW = (int64_t)gridDim.x * kWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+  const int m = lane & 31, h = lane >> 5;
+  const int R = a.QL * a.H;
+  int par = 0;
+  for_live_pages<true>(a, gw, NW, [&](bool live, int r, int b, int L, int pid) {
+    float best = -INFINITY;
+    if (live) {
+      // the query rows first (loads return in order), then the first tiles
+      uint8_t* qblk = &lds_q[wave][0];
+      stage_query32(a, r, R, lane, qblk);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* pg = a.pages + (int64_t)pid * a.page_stride;
+      const auto rs = page_rsrc(pg, kPageTokens * (kCodeBytes + kScaleBytes));
+      const uint32_t co = (uint32_t)(m * kCodeBytes + 32 * h);
+      const uint32_t so = (uint32_t)(kScaleRegion + m * kScaleBytes + 4 * h);
+      Tile32 reg[NS];
+#pragma unroll
+      for (int T = 0; T < NS; ++T) {
+        reg[T] = load_tile32(rs, co, so, T);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      static_assert(NS == 2, "the wait below counts the tile loads issued after the query");
+      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      i32x4 qr[4];
+      read_query32(qblk, m, h, qr);
+      f16x8 qf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[s] = q32_operand(qr, s);
+      // last visible token of the row
+      const int lim = m < R ? L - a.QL + small_div(m, 1.0f / (float)a.H) : -1;
+      const bool full = (b + 1) * kPageTokens - 1 <= L - a.QL;
+      const int lt0 = lim - (b * kPageTokens + 4 * h);
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        const f32x16 c = mfma_tile32(reg[T % NS], qf);
+        if (T + NS < 4) reg[T % NS] = load_tile32(rs, co, so, T + NS);
+        max_tile32(c, full, lt0 - 32 * T, best);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const auto o = __builtin_amdgcn_permlane32_swap(f_bits(best), f_bits(best), false, false);
+      best = fmaxf(bits_f(o[0]), bits_f(o[1]));
+      int mm = m;
+      asm volatile("" : "+v"(mm));  // the slot address built here, not hoisted and spilled
+      if (h == 0) lds_best[par][wave][mm] = best;
+    }
+    if (lane == 0) {
+      lds_rb[par][wave][0] = live ? r : -1;
+      lds_rb[par][wave][1] = b;
+    }
+    // every wave of the workgroup gets here once per call (the walk is uniform); the two
+    // buffers alternate, so a buffer is written again only after the barrier of the next
+    // call, when every wave has read it
+    __syncthreads();
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // the addresses below built here, not hoisted and spilled
+    if (ln < 32) {
+      const int k = ln & 3, col = 8 * wave + (ln >> 2);
+      const int rk = lds_rb[par][k][0], bk = lds_rb[par][k][1];
+      if (rk >= 0 && col < R) {
+        const int j = small_div(col, 1.0f / (float)a.H), hh = col - j * a.H;
+        a.scores[(int64_t)hh * a.s_sh + ((int64_t)rk * a.QL + j) * a.s_st + bk] = lds_best[par][k][col];
+      }
+    }
+    par ^= 1;
+  });
 }
 
 // One wave per (request, page slot) of the grid; waves past their sequence exit after the
@@ -341,7 +573,7 @@ hipError_t launch_index_score(const IndexArgs& a, hipStream_t stream) {
     waves = waves < most ? waves : most;
     const int64_t wgs = (waves + kWaves - 1) / kWaves;
     if (nct == 2)
-      hipLaunchKernelGGL((index_score_live<2>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
+      hipLaunchKernelGGL((index_score_live32<2>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
     else
       hipLaunchKernelGGL((index_score_live<1>), dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, a);
     return hipGetLastError();

@@ -161,6 +161,25 @@ def test_shared_pages_across_windows_and_partial():
     assert_index_match(got, run_oracle(case), case.scores_init(), "irregular sharing")
 
 
+@pytest.mark.parametrize("ql,h", [(17, 1), (10, 2), (5, 4), (6, 4), (7, 4), (16, 2), (32, 1)])
+def test_wide_column_counts(ql, h):
+    """17-32 query columns (H * QL), each a 32 x 32 output tile, at counts other than 8 x 4:
+    columns past H * QL unused, 21 requests whose pages meet inside workgroups, an empty
+    request and page-edge lengths, the query rows taken from a wider buffer."""
+    need_gpu()
+    rng = np.random.default_rng(150 + ql * h + ql)
+    lens = [max(ql, int(x)) for x in rng.integers(1, 3001, size=21)]
+    lens[3], lens[7], lens[11], lens[12] = 0, ql, 128, 129
+    case = synth.make_index_case("idx_wide", 151 + ql * h + ql, seq_lens=lens, query_len=ql,
+                                 heads=h, max_pages=24)
+    R, H, D = case.q.shape
+    wide = torch.zeros(R, H + 1, D + 64, dtype=torch.uint8)
+    wide[:, :H, :D] = torch.from_numpy(case.q)
+    log(f"case index wide columns ql={ql} h={h}")
+    got = run_gpu(case, q=wide.to(DEV)[:, :H, :D])
+    assert_index_match(got, run_oracle(case), case.scores_init(), f"wide ql={ql} h={h}")
+
+
 @pytest.mark.parametrize("R", [60, 300])
 def test_many_requests_with_empty_ones(R):
     """Lengths from 0 to 3000.  60 requests: one wave per live page of the list built from
