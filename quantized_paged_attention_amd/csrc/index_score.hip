@@ -12,17 +12,18 @@
 //     is dequantised exactly (one v_cvt_scalef32_pk_f16_fp4 with unit scale and one
 //     packed f16 multiply per byte) and the dot products run on v_mfma_f32_16x16x32_f16
 //     with exact products and fp32 accumulation.
-//   * A = K tile (lane = token, 32 consecutive dims per lane), B = the request's query
-//     rows (columns = (j, h), at most 32: two column tiles), kept as raw e4m3 words and
-//     converted to f16 at each use (v_cvt_scalef32_pk_f16_fp8, exact).  The output layout puts
-//     4 tokens of one column in a lane; masked tokens are selected to -inf (never
-//     multiplied, so garbage past the sequence cannot leak), the page max is kept per
-//     lane and reduced across the four lane rows once per page.  A page that every row
-//     sees whole skips the causal selects.
-//   * A page (8 tiles: 128 code bytes + 1 scale word per lane, non-temporal, one buffer
-//     resource) is requested whole before its first MFMA: into registers with one column
-//     tile; with two, half of it, each later tile loaded into the registers of the tile
-//     4 before it once that one is dequantised (5 waves per SIMD either way).
+//   * Up to 16 query columns (j, h): A = K tile (lane = token, 32 consecutive dims per
+//     lane), B = the request's query rows, kept as raw e4m3 words and converted to f16 at
+//     each use (v_cvt_scalef32_pk_f16_fp8, exact).  The output layout puts 4 tokens of one
+//     column in a lane; masked tokens are selected to -inf (never multiplied, so garbage
+//     past the sequence cannot leak), the page max is kept per lane and reduced across
+//     the four lane rows once per page.  A page that every row sees whole skips the
+//     causal selects.  A page (8 tiles: 128 code bytes + 1 scale word per lane,
+//     non-temporal, one buffer resource) is requested whole before its first MFMA.
+//   * 17-32 columns: 32 x 32 tiles (v_mfma_f32_32x32x16_f16, all columns per operand),
+//     the f16 query held in registers, half the page in flight at a time; the query rows
+//     reach the wave through LDS and the page maxima of a workgroup's four waves are
+//     stored together (see index_score_live32).
 //   * Up to 64 requests: one wave per LIVE page.  The lengths give each request's live
 //     pages; all requests' live pages form one list, and wave g of the launch takes
 //     entries g, g + NW, ... with NW = the waves the chip holds at once.  A wave's chain
@@ -38,9 +39,7 @@
 //     (graph-timed on MI355X: 11.8 -> 11.45 us at QL 1 x H 1).  The table entries of the
 //     wave's page and of its next one are read before the loop, which the compiler turns
 //     into scalar loads running beside the query loads (11.3 -> 10.6 us); the next page's
-//     chain after the first is then one load.  At QL 8 x H 4 the scorer still takes
-//     ~3.5 us more than at QL 8 x H 2 (one column tile, 10.9 us): twice the MFMAs and
-//     the query conversions per page, on the last pages to arrive.
+//     chain after the first is then one load.
 //   * More requests: one wave per (request, page slot), the table entry read after the
 //     length says the page is live.
 #include "uq_device.h"
@@ -343,6 +342,16 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
 // dims; k-step s of the tile is dims 8 s .. 8 s + 8 of each half, whose scale is byte s / 2
 // of the lane's scale word.  The query operand of a lane is column l % 32, the same dims.
 // Output: lane l holds column l % 32 and tokens 8 (v / 4) + 4 h + v % 4 of register v.
+//
+// Measured on MI355X (QL 8 x H 4, 32 requests, L ~ U[1024, 32768], graph-timed on cold
+// pages, one session each): two 16 x 16 column tiles 13.8 us; 32 x 32 tiles 13.5 us;
+// entries dealt to XCDs in runs of 32, 13.0-13.2 us; query through LDS and grouped score
+// stores, 12.3 us.  Timing copies that skipped work showed where the rest went: no score
+// store 11.8 us, no query load 11.8 us, half the k-steps 12.3-12.6 us; the query and the
+// stores each touched 32 lines per instruction (coalesced in a copy: 12.4 and 12.1 us).
+// Not kept: the whole page in flight with two tiles landing in LDS (13.8 us against
+// 13.5), or in registers with the query converted at each use from LDS (13.0 against
+// 12.4): the extra conversions cost more than the second round trip of half a page.
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
