@@ -346,7 +346,8 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
 // Measured on MI355X (QL 8 x H 4, 32 requests, L ~ U[1024, 32768], graph-timed on cold
 // pages, one session each): two 16 x 16 column tiles 13.8 us; 32 x 32 tiles 13.5 us;
 // entries dealt to XCDs in runs of 32, 13.0-13.2 us; query through LDS and grouped score
-// stores, 12.3 us.  Timing copies that skipped work showed where the rest went: no score
+// stores, 12.3 us (query by direct buffer-to-LDS loads) and 12.1 us (by whole-line
+// register loads written to LDS, as now).  Timing copies that skipped work showed where the rest went: no score
 // store 11.8 us, no query load 11.8 us, half the k-steps 12.3-12.6 us; the query and the
 // stores each touched 32 lines per instruction (coalesced in a copy: 12.4 and 12.1 us).
 // Not kept: the whole page in flight with two tiles landing in LDS (13.8 us against
@@ -413,16 +414,14 @@ __device__ __forceinline__ int small_div(int x, float inv_d) {
   return (int)(((float)x + 0.5f) * inv_d);
 }
 
-// The query rows of request r as 32 rows of 128 bytes in the wave's LDS block, through
-// direct buffer-to-LDS loads.  Load i writes bytes [1024 i, 1024 i + 1024) of the block,
-// lane l the 16 bytes 1024 i + 16 l: row c = 8 i + l / 8, slot l % 8, which receives chunk
-// (l % 8) ^ (c % 8) of query column c's 128 bytes.  So each load reads 8 whole rows (8
-// lines, where a load of the lane's own 16 bytes of 32 columns touches 32 lines), and
-// the reads below are free of bank conflicts.  Columns at or past R are not loaded.
-// Nothing tracks these LDS writes: the reader waits on vmcnt for them.
-__device__ __forceinline__ void stage_query32(const IndexArgs& a, int r, int R, int lane,
-                                              uint8_t* blk) {
-  using lds_ptr = __attribute__((address_space(3))) void*;
+// The query rows of request r, read whole-line: load i gives lane l the 16 bytes of row
+// c = 8 i + l / 8 (columns past R read column R - 1, never used), chunk (l % 8) ^ (c % 8)
+// of its 128 bytes, so each load reads 8 whole rows (8 lines, where a load of the lane's
+// own 16 bytes of 32 columns touches 32 lines).  put_query32 then writes them to the
+// wave's LDS block at 1024 i + 16 l: row c, slot l % 8, so the reads below are free of
+// bank conflicts.
+__device__ __forceinline__ void load_query32(const IndexArgs& a, int r, int R, int lane,
+                                             i32x4 (&raw)[4]) {
   const uint64_t base = (uint64_t)(a.q + (int64_t)r * a.QL * a.q_st);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
@@ -439,13 +438,16 @@ __device__ __forceinline__ void stage_query32(const IndexArgs& a, int r, int R, 
   const float inv_h = 1.0f / (float)a.H;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = 8 * i + c0;
-    if (c < R) {
-      const int j = small_div(c, inv_h), hh = c - j * a.H;
-      const uint32_t off = (uint32_t)(j * a.q_st + hh * a.q_sh + 16 * (sl ^ c0));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(blk + 1024 * i), 16, off, 0, 0, 0);
-    }
+    const int c = 8 * i + c0 < R ? 8 * i + c0 : R - 1;
+    const int j = small_div(c, inv_h), hh = c - j * a.H;
+    const uint32_t off = (uint32_t)(j * a.q_st + hh * a.q_sh + 16 * (sl ^ c0));
+    raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
   }
+}
+
+__device__ __forceinline__ void put_query32(uint8_t* blk, int lane, const i32x4 (&raw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(blk + 1024 * i + 16 * lane) = raw[i];
 }
 
 // The lane's 64 query bytes (column m, dims [64 h, 64 h + 64)) from the staged block.
@@ -479,7 +481,8 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[1]) void index_score
     if (live) {
       // the query rows first (loads return in order), then the first tiles
       uint8_t* qblk = &lds_q[wave][0];
-      stage_query32(a, r, R, lane, qblk);
+      i32x4 qraw[4];
+      load_query32(a, r, R, lane, qraw);
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* pg = a.pages + (int64_t)pid * a.page_stride;
       const auto rs = page_rsrc(pg, kPageTokens * (kCodeBytes + kScaleBytes));
@@ -491,8 +494,8 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[1]) void index_score
         reg[T] = load_tile32(rs, co, so, T);
         __builtin_amdgcn_sched_barrier(0);
       }
-      static_assert(NS == 2, "the wait below counts the tile loads issued after the query");
-      asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+      // the query through the wave's LDS block: its whole-line layout into the operand's
+      put_query32(qblk, lane, qraw);
       i32x4 qr[4];
       read_query32(qblk, m, h, qr);
       f16x8 qf[8];
