@@ -230,7 +230,9 @@ int uq_paged_attention(const void* query, int q_dtype, int64_t q_stride_seq,
  * with k = e2m1(code) * e4m3(scale of its 16-dim group), products exact and fp32
  * accumulation; -inf when page b holds no such token ([P2] frag_max / score_cgs).
  *   q        e4m3 codes [num_reqs*query_len, heads, head_dim], byte strides
- *            q_stride_tok / q_stride_head (> 0; dims contiguous).
+ *            q_stride_tok / q_stride_head (> 0, multiples of 16; dims contiguous).  One
+ *            request's rows, (query_len - 1) * q_stride_tok + (heads - 1) * q_stride_head
+ *            + head_dim bytes, must span less than 2^31 (else UQ_ERR_UNSUPPORTED).
  *   k_pages  [num_pages] pages of page_stride bytes: codes [128 tok][head_dim/2] then
  *            scales [128 tok][head_dim/16] ([P2] load_tile offsets).  page_stride >=
  *            128 * (head_dim/2 + head_dim/16) and a multiple of 16.

@@ -543,6 +543,10 @@ int uq_index_score(const uint8_t* q, int64_t q_stride_tok, int64_t q_stride_head
     return fail(UQ_ERR_UNSUPPORTED, "sentinel init/local blocks are not supported");
   if (q_stride_tok <= 0 || q_stride_head <= 0 || q_stride_tok % 16 || q_stride_head % 16)
     return fail(UQ_ERR_INVALID_ARG, "q strides must be positive multiples of 16 bytes");
+  // one request's query rows are addressed with 32-bit offsets
+  if ((int64_t)(query_len - 1) * q_stride_tok + (int64_t)(heads - 1) * q_stride_head + head_dim >
+      0x7FFFFFFFLL)
+    return fail(UQ_ERR_UNSUPPORTED, "a request's query rows span more than 2^31 - 1 bytes");
   const int64_t content = 128LL * (head_dim / 2 + head_dim / 16);
   if (page_stride < content || page_stride % 16)
     return fail(UQ_ERR_INVALID_ARG, "page_stride %lld must be >= %lld and a multiple of 16",

@@ -165,6 +165,7 @@ def index_args(**over):
     (dict(npages=0), uq.UQ_ERR_INVALID_ARG),
     (dict(s_st=255), uq.UQ_ERR_INVALID_ARG),              # score rows overlap
     (dict(s_sh=63 * 256 + 255), uq.UQ_ERR_INVALID_ARG),   # heads' score planes overlap
+    (dict(QL=32, H=1, q_st=1 << 27), uq.UQ_ERR_UNSUPPORTED),  # query rows past 2^31 bytes
 ])
 def test_index_validation(lib, over, status):
     assert lib.uq_index_score(*index_args(**over)) == status
