@@ -196,11 +196,13 @@ def test_many_requests_with_empty_ones(R):
     assert_index_match(got, run_oracle(case), case.scores_init(), f"{R} requests")
 
 
-@pytest.mark.parametrize("R,ql,h", [(64, 1, 1), (64, 8, 4), (512, 1, 1)])
+@pytest.mark.parametrize("R,ql,h", [(64, 1, 1), (64, 8, 4), (64, 5, 4), (512, 1, 1)])
 def test_long_page_lists(R, ql, h):
     """Requests of ~38k tokens whose tables all point at the same 300 pages.  64 requests:
     19k live pages, more than the waves of one launch, so each wave loops over several
-    entries of the list; 512 requests: 150k page slots, one wave each."""
+    entries of the list (with 17-32 query columns every wave of a workgroup makes the same
+    number of calls, those past the list idle); 512 requests: 150k page slots, one wave
+    each."""
     need_gpu()
     base = synth.make_index_case("idx_long", 140, seq_lens=[300 * 128], query_len=1, heads=1,
                                  spare_pages=2)
