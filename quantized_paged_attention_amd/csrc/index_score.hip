@@ -45,9 +45,6 @@
 #include "uq_device.h"
 #include "uq_kernels.h"
 
-#ifndef UQ_IDX_XCD_RUNS
-#define UQ_IDX_XCD_RUNS 1
-#endif
 
 namespace uq {
 namespace {
@@ -254,14 +251,14 @@ __device__ __forceinline__ void for_live_pages(const IndexArgs& a, int64_t gw, i
     b = e - (r > 0 ? __builtin_amdgcn_readlane(incl, r - 1) : 0);
     L = __builtin_amdgcn_readlane(Ll, r);
   };
-  // the wave's first entry.  Workgroups are dealt to the 8 XCDs in turn; with UQ_IDX_XCD_RUNS
-  // the entries go to them in runs of 32, so the pages of a run (one 128-byte line of
+  // the wave's first entry.  Workgroups are dealt to the 8 XCDs in turn, and the entries
+  // go to them in runs of 32, so the pages of a run (one 128-byte line of
   // every score row they write) are scored under one L2.  Entries e + NW, e + 2 NW, ...
   // follow on the same XCD as long as NW is a multiple of 256.  Either way the kWaves
   // waves of a workgroup hold consecutive entries.
   const int w = (int)(gw % kWaves);
   int e = (int)gw;
-  if (UQ_IDX_XCD_RUNS && NW % 256 == 0) {
+  if (NW % 256 == 0) {
     const int64_t wg = gw / kWaves;
     const int x = (int)(wg % 8);
     const int i = (int)((wg / 8) * kWaves + w);  // the wave's index on its XCD
@@ -347,12 +344,13 @@ __global__ __launch_bounds__(64 * kWaves, kLiveWavesPerSimd[NCT - 1]) void index
 // pages, one session each): two 16 x 16 column tiles 13.8 us; 32 x 32 tiles 13.5 us;
 // entries dealt to XCDs in runs of 32, 13.0-13.2 us; query through LDS and grouped score
 // stores, 12.3 us (query by direct buffer-to-LDS loads) and 12.1 us (by whole-line
-// register loads written to LDS, as now).  Timing copies that skipped work showed where the rest went: no score
-// store 11.8 us, no query load 11.8 us, half the k-steps 12.3-12.6 us; the query and the
-// stores each touched 32 lines per instruction (coalesced in a copy: 12.4 and 12.1 us).
-// Not kept: the whole page in flight with two tiles landing in LDS (13.8 us against
-// 13.5), or in registers with the query converted at each use from LDS (13.0 against
-// 12.4): the extra conversions cost more than the second round trip of half a page.
+// register loads written to LDS, as now).  Timing copies that skipped work showed where
+// the rest went: no score store 11.8 us, no query load 11.8 us, half the k-steps
+// 12.3-12.6 us; the query and the stores each touched 32 lines per instruction
+// (coalesced in a copy: 12.4 and 12.1 us).  Not kept: the whole page in flight with two
+// tiles landing in LDS (13.8 us against 13.5), or in registers with the query converted
+// at each use from LDS (13.0 against 12.4): the extra conversions cost more than the
+// second round trip of half a page.
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
